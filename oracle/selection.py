@@ -1,0 +1,39 @@
+"""Row selection for the next forward pass (test infrastructure only).
+
+EntropyCache (zh) §2.2 and EntropyCache (pt) §2: a full step recomputes every
+position; a partial step recomputes only the tokens that are still masked plus
+the k most recently decoded tokens (kept in a decode history of O(k) memory,
+zh §2.3), and every other position reads its K/V from the cache.
+
+Readings where the pages are silent:
+  * "still masked" means the masked positions of the current block; masked
+    positions of later blocks keep the K/V of the last full step;
+  * the history holds decoded positions only (never prompt positions), in the
+    order they were unmasked; within one step they are appended in ascending
+    position order, so "last k" cuts at that order;
+  * the history persists across blocks and across full steps.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+import numpy as np
+
+
+def candidates(masked, block_start: int, block_len: int) -> np.ndarray:
+    """Masked positions of the current block, ascending (the rows that get logits)."""
+    masked = np.asarray(masked).astype(bool)
+    return np.array([p for p in range(block_start, block_start + block_len) if masked[p]],
+                    dtype=np.int64)
+
+
+def select_rows(full: int, masked, block_start: int, block_len: int,
+                history: Sequence[int], k: int) -> np.ndarray:
+    """Ascending list of the positions whose Q/K/V are recomputed this step."""
+    L = len(masked)
+    if full:
+        return np.arange(L, dtype=np.int64)
+    chosen = set(int(p) for p in candidates(masked, block_start, block_len))
+    if k > 0:
+        chosen |= set(int(p) for p in list(history)[-k:])
+    return np.array(sorted(chosen), dtype=np.int64)

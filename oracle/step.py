@@ -1,0 +1,160 @@
+"""One EntropyCache denoising step and the generation loop (test infrastructure only).
+
+EntropyCache (zh) §2.2 describes each step as three phases:
+  1. forward pass, full or partial according to the previous step's flag; a
+     partial pass recomputes only the current masked tokens and the k most
+     recently decoded tokens and reads every other position from the KV cache;
+  2. decode new tokens from the logits and take E_{t+1}, the largest entropy
+     among the newly decoded tokens;
+  3. decide: E_{t+1} > tau makes the next step full, otherwise partial, with
+     the recompute set drawn from the decode history.
+EntropyCache (pt) §2 gives the same flow.  Readings where the pages are silent
+(each also stated at the function that applies it):
+  * the first step is full (there is no cache yet);
+  * the decision made at step t governs step t+1;
+  * on a partial step every layer recomputes only the selected rows (Q/K/V,
+    attention, output projection, FFN) and attends over its whole cache;
+  * layer input = token embedding + additive position embedding; the MASK token
+    has its own embedding row;
+  * logits are produced only for the masked positions of the current block,
+    optionally times a per-position scale, and stored in the storage dtype;
+  * when the block has no masked position left the host moves to the next
+    block (the schedule is fixed on the host).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from .entropy import choose, decide, max_entropy, row_stats
+from .layers import bidir_attention, kv_refresh, linear, rmsnorm, swiglu
+from .rounding import to_storage
+from .selection import candidates, select_rows
+
+
+@dataclasses.dataclass
+class Model:
+    n_layers: int
+    d: int
+    n_q: int
+    n_kv: int
+    dh: int
+    V: int
+    d_ffn: int
+    eps: float
+    dtype: str
+    tok_emb: np.ndarray                  # [V + 1, d]; row V is MASK
+    pos_emb: np.ndarray                  # [L, d]
+    layers: List[dict]
+    w_lm: np.ndarray                     # [V, d]
+    norm_final: Optional[np.ndarray] = None
+    logit_scale: Optional[np.ndarray] = None   # [L] or None
+
+    @classmethod
+    def from_arrays(cls, shape, dtype: str, w: dict) -> "Model":
+        f = lambda a: None if a is None else np.asarray(a, dtype=np.float64)  # noqa: E731
+        return cls(n_layers=shape.n_layers, d=shape.d, n_q=shape.n_q_heads, n_kv=shape.n_kv_heads,
+                   dh=shape.head_dim, V=shape.vocab, d_ffn=shape.d_ffn, eps=shape.rms_eps,
+                   dtype=dtype, tok_emb=f(w["tok_emb"]), pos_emb=f(w["pos_emb"]),
+                   layers=[{k: f(v) for k, v in lw.items()} for lw in w["layers"]],
+                   w_lm=f(w["w_lm"]), norm_final=f(w.get("norm_final")),
+                   logit_scale=f(w.get("logit_scale")))
+
+
+@dataclasses.dataclass
+class State:
+    tokens: np.ndarray                   # [L] int64
+    masked: np.ndarray                   # [L] bool
+    history: List[int]                   # decoded positions in unmask order
+    flag: int                            # 1: this step recomputes every row
+    K: List[np.ndarray]                  # per layer [Hkv, L, dh]
+    V: List[np.ndarray]
+
+    def copy(self) -> "State":
+        return State(self.tokens.copy(), self.masked.copy(), list(self.history), self.flag,
+                     [k.copy() for k in self.K], [v.copy() for v in self.V])
+
+
+@dataclasses.dataclass
+class StepTrace:
+    flag_used: int
+    rows: np.ndarray
+    cand: np.ndarray
+    logits: Optional[np.ndarray]
+    H: np.ndarray
+    argmax: np.ndarray
+    p1: np.ndarray
+    chosen: np.ndarray
+    E: float
+    flag_next: int
+
+
+def init_state(model: Model, tokens, masked) -> State:
+    """Fresh sequence state: empty history, empty caches, first step full."""
+    L = len(tokens)
+    K = [np.zeros((model.n_kv, L, model.dh)) for _ in range(model.n_layers)]
+    V = [np.zeros((model.n_kv, L, model.dh)) for _ in range(model.n_layers)]
+    return State(np.asarray(tokens, dtype=np.int64).copy(), np.asarray(masked).astype(bool).copy(),
+                 [], 1, K, V)
+
+
+def forward_rows(model: Model, state: State, rows: np.ndarray) -> np.ndarray:
+    """Run every layer over the selected rows, refreshing their K/V in each cache.
+
+    Returns the final activations of those rows (after the final norm, if any).
+    """
+    dt = model.dtype
+    n = len(rows)
+    x = to_storage(model.tok_emb[state.tokens[rows]] + model.pos_emb[rows], dt)
+    scale = 1.0 / math.sqrt(model.dh)
+    for l, lw in enumerate(model.layers):
+        a = to_storage(rmsnorm(x, lw["norm_attn"], model.eps), dt) if model.d_ffn else x
+        q = kv_refresh(a, rows, lw["w_qkv"], state.K[l], state.V[l], model.n_q, model.n_kv,
+                       model.dh, dt)
+        o = to_storage(bidir_attention(q, state.K[l], state.V[l], scale), dt)
+        x = to_storage(x + linear(o.reshape(n, model.n_q * model.dh), lw["w_o"]), dt)
+        if model.d_ffn:
+            a2 = to_storage(rmsnorm(x, lw["norm_ffn"], model.eps), dt)
+            h = to_storage(swiglu(a2, lw["w_gate"], lw["w_up"]), dt)
+            x = to_storage(x + linear(h, lw["w_down"]), dt)
+    if model.d_ffn:
+        x = to_storage(rmsnorm(x, model.norm_final, model.eps), dt)
+    return x
+
+
+def step(model: Model, state: State, tau: float, k: int, block_start: int, block_len: int,
+         n_unmask: int, keep_logits: bool = True) -> StepTrace:
+    """One denoising step; mutates `state` and returns what the step computed."""
+    flag_used = state.flag
+    rows = select_rows(flag_used, state.masked, block_start, block_len, state.history, k)
+    x = forward_rows(model, state, rows)
+    cand = candidates(state.masked, block_start, block_len)
+    ci = np.searchsorted(rows, cand)
+    z = linear(x[ci], model.w_lm)
+    if model.logit_scale is not None:
+        z = z * model.logit_scale[cand][:, None]
+    z = to_storage(z, model.dtype)
+    H, A, P = row_stats(z)
+    chosen = choose(cand, P, n_unmask)
+    pick = np.searchsorted(cand, chosen)
+    state.tokens[chosen] = A[pick]
+    state.masked[chosen] = False
+    state.history.extend(int(c) for c in chosen)
+    E = max_entropy(H, pick)
+    state.flag = decide(E, tau)
+    return StepTrace(flag_used, rows, cand, z if keep_logits else None, H, A, P, chosen, E,
+                     state.flag)
+
+
+def generate(model: Model, state: State, schedule: Sequence[Tuple[int, int, int]], tau: float,
+             k: int, keep_logits: bool = False, n_steps: Optional[int] = None) -> List[StepTrace]:
+    """Run the schedule [(block_start, block_len, n_unmask), ...] from `state`."""
+    out = []
+    for i, (bs, bl, n) in enumerate(schedule):
+        if n_steps is not None and i >= n_steps:
+            break
+        out.append(step(model, state, tau, k, bs, bl, n, keep_logits))
+    return out
