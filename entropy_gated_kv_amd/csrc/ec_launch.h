@@ -1,0 +1,106 @@
+// Host-side launchers of the gfx950 kernels, called by the C-ABI layer after
+// its argument checks.  Internal to libec.so.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ec {
+
+// ---- entropy pass ----------------------------------------------------------
+struct EntropyPartial {   // online softmax statistics of one V segment
+  float m;                // max over the segment (NaN never; +/-inf possible)
+  float z;                // sum 2^u, u = (x - m) log2(e)
+  float s2;               // sum 2^u * u
+  int32_t idx;            // lowest index holding m (INT32_MAX: none)
+};
+// Rows are split into segments of 2048 16-byte vectors (16384 bf16 / 8192 fp32).
+int entropy_segments(int64_t V, int dtype);
+size_t entropy_ws_bytes(int64_t n_rows, int64_t V, int dtype);
+
+// Per-row H / argmax / p1 for rows < min(n_rows, *n_rows_dev) (n_rows_dev may
+// be NULL) and, when e_max != NULL, E = max over D of H and flag = E > tau
+// (NaN -> 1); D NULL means rows [0, n_rows).  ws holds the segment partials.
+int device_cu_count();
+hipError_t launch_entropy(const void* logits, int dtype, int64_t n_rows, const int32_t* n_rows_dev,
+                          int64_t V, int64_t stride, float* H, int32_t* argmax, float* p1,
+                          const int32_t* D, const int32_t* nD, int32_t maxD, float tau,
+                          float* e_max, int32_t* flag, void* ws, hipStream_t s);
+
+}  // namespace ec
+
+namespace ec {
+
+// ---- row selection -----------------------------------------------------------
+int32_t select_max_L();
+hipError_t launch_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
+                              int32_t block_start, int32_t block_len, const int32_t* history,
+                              const int32_t* history_len, int32_t history_cap, int32_t k,
+                              int32_t* rows, int32_t* n_rows, int32_t* cand_pos,
+                              int32_t* cand_idx, int32_t* n_cand, hipStream_t s);
+
+// ---- glue --------------------------------------------------------------------
+hipError_t launch_embed(int dtype, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
+                        const int32_t* rows, const int32_t* n_rows, int max_rows, int d, void* x,
+                        hipStream_t s);
+hipError_t launch_rmsnorm(int dtype, const void* x, const int32_t* n_rows, int max_rows, int d,
+                          const void* gain, float eps, void* out, hipStream_t s);
+int32_t choose_max_candidates();
+hipError_t launch_choose_decide(const int32_t* cand_pos, const int32_t* n_cand, const float* H,
+                                const int32_t* argmax, const float* p1, int32_t n_unmask,
+                                float tau, int32_t* chosen, int32_t* n_chosen, int32_t* tokens,
+                                uint8_t* is_masked, int32_t* history, int32_t* history_len,
+                                int32_t history_cap, float* e_max, int32_t* flag, hipStream_t s);
+
+// ---- row GEMM with fused epilogues ---------------------------------------------
+// C[r, n] = sum_k A[row(r), k] * W[n, k] for r < *n_rows_dev (<= max_rows), n < N,
+// where row(r) = a_idx ? a_idx[r] : r.  W is [N, K] row-major.
+enum class Epi : int {
+  kStore = 0,     // C[r, n] = acc                                    (C [max_rows, ldc])
+  kQKV = 1,       // Q / K cache / V^T cache scatter at rows[r]
+  kResidual = 2,  // C[r, n] = C[r, n] + acc  (in place)
+  kSwiGLU = 3,    // C[r, n] = silu(acc) * acc2, acc2 from W2
+  kLogits = 4,    // C[r, n] = acc * scale[scale_pos[r]]  (scale may be NULL)
+};
+struct GemmArgs {
+  int dtype = 0;
+  Epi epi = Epi::kStore;
+  const void* A = nullptr;
+  int64_t lda = 0;
+  const int32_t* a_idx = nullptr;
+  const int32_t* n_rows_dev = nullptr;
+  int max_rows = 0;
+  const void* W = nullptr;
+  const void* W2 = nullptr;
+  int N = 0, K = 0;
+  void* C = nullptr;
+  int64_t ldc = 0;
+  // kQKV
+  const int32_t* rows = nullptr;
+  void* q_out = nullptr;
+  void* k_cache = nullptr;
+  void* v_cache = nullptr;
+  int Hq = 0, Hkv = 0, dh = 0, L_cap = 0;
+  // kLogits
+  const float* scale = nullptr;
+  const int32_t* scale_pos = nullptr;
+};
+size_t gemm_ws_bytes(const GemmArgs& a);
+hipError_t launch_gemm_rows(const GemmArgs& a, void* ws, hipStream_t s);
+
+// ---- bidirectional attention -----------------------------------------------------
+struct AttnArgs {
+  int dtype = 0;
+  const void* q = nullptr;            // [max_rows, Hq, dh]
+  const int32_t* n_rows_dev = nullptr;
+  int max_rows = 0;
+  const void* k_cache = nullptr;      // [Hkv, L_cap, dh]
+  const void* v_cache = nullptr;      // [Hkv, dh, L_cap]
+  int L = 0, L_cap = 0, Hq = 0, Hkv = 0, dh = 0;
+  float scale = 1.f;
+  void* out = nullptr;                // [max_rows, Hq, dh]
+};
+size_t attn_ws_bytes(int max_rows, int L, int Hq, int Hkv, int dh);
+hipError_t launch_attention(const AttnArgs& a, void* ws, hipStream_t s);
+
+}  // namespace ec

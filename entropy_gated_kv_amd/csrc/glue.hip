@@ -1,0 +1,189 @@
+// Step glue around the three graded phases: embedding gather of the selected
+// rows, RMSNorm, and the decode/decide kernel that unmasks tokens, appends to
+// the decode history and takes the threshold decision.
+//
+// EntropyCache, Chinese summary page §2.2: after the forward pass new tokens are
+// decoded from the logits and E_{t+1} is the maximum entropy over the newly
+// decoded tokens; E_{t+1} > tau makes the next step a full recompute.  The
+// Portuguese page §2 adds that a decode history is kept to pick the k most
+// recent tokens.  The pages do not fix the decode rule; this library decodes
+// each candidate to its argmax and unmasks the n candidates with the largest
+// top-1 probability (ties to the lower position, NaN last), appending them to
+// the history in ascending position order.
+#include <math.h>
+
+#include "ec_device.h"
+#include "ec_launch.h"
+
+namespace ec {
+
+namespace {
+
+// x[r, :] = tok_emb[tokens[rows[r]], :] + pos_emb[rows[r], :]  (fp32 add, one rounding)
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ tok_emb,
+                                                   const T* __restrict__ pos_emb,
+                                                   const int32_t* __restrict__ tokens,
+                                                   const int32_t* __restrict__ rows,
+                                                   const int32_t* __restrict__ n_rows, int d,
+                                                   T* __restrict__ x) {
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const int p = rows[r];
+  const int t = tokens[p];
+  const T* te = tok_emb + int64_t(t) * d;
+  const T* pe = pos_emb + int64_t(p) * d;
+  T* xr = x + int64_t(r) * d;
+  for (int c = threadIdx.x; c < d; c += 256)
+    Elem<T>::store(xr, c, Elem<T>::load(te, c) + Elem<T>::load(pe, c));
+}
+
+// out[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * gain   (one workgroup per row)
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x,
+                                                     const int32_t* __restrict__ n_rows, int d,
+                                                     const T* __restrict__ gain, float eps,
+                                                     T* __restrict__ out) {
+  const int r = blockIdx.x;
+  if (r >= *n_rows) return;
+  const T* xr = x + int64_t(r) * d;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    const float v = Elem<T>::load(xr, c);
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  __shared__ float sw[4];
+  if ((threadIdx.x & 63) == 0) sw[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (sw[0] + sw[1]) + (sw[2] + sw[3]);
+  const float inv = 1.0f / sqrtf(tot / float(d) + eps);
+  T* orow = out + int64_t(r) * d;
+  for (int c = threadIdx.x; c < d; c += 256)
+    Elem<T>::store(orow, c, Elem<T>::load(xr, c) * inv * Elem<T>::load(gain, c));
+}
+
+constexpr int kChooseThreads = 1024;
+
+__device__ __forceinline__ bool better(float pj, int posj, float pi, int posi) {
+  const bool nj = (pj != pj), ni = (pi != pi);
+  if (nj != ni) return ni;                 // a number beats NaN
+  if (!nj && pj != pi) return pj > pi;
+  return posj < posi;                      // equal (or both NaN): lower position first
+}
+
+__global__ __launch_bounds__(kChooseThreads) void choose_decide_kernel(
+    const int32_t* __restrict__ cand_pos, const int32_t* __restrict__ n_cand,
+    const float* __restrict__ H, const int32_t* __restrict__ argmax,
+    const float* __restrict__ p1, int32_t n_unmask, float tau, int32_t* __restrict__ chosen,
+    int32_t* __restrict__ n_chosen, int32_t* __restrict__ tokens, uint8_t* __restrict__ is_masked,
+    int32_t* __restrict__ history, int32_t* __restrict__ history_len, int32_t history_cap,
+    float* __restrict__ e_max, int32_t* __restrict__ flag) {
+  __shared__ float s_p1[kChooseThreads];
+  __shared__ int s_pos[kChooseThreads];
+  __shared__ int s_cnt[kChooseThreads / kWave + 1];
+  __shared__ float s_max[kChooseThreads / kWave];
+  __shared__ int s_nan[kChooseThreads / kWave];
+  const int tid = threadIdx.x;
+  const int nc = min(*n_cand, kChooseThreads);
+  const int ns = min(n_unmask, nc);
+  const int hl = *history_len;
+  if (tid < nc) { s_p1[tid] = p1[tid]; s_pos[tid] = cand_pos[tid]; }
+  __syncthreads();
+  bool pick = false;
+  if (tid < nc) {
+    const float pi = s_p1[tid];
+    const int posi = s_pos[tid];
+    int rank = 0;
+    for (int j = 0; j < nc; ++j) rank += better(s_p1[j], s_pos[j], pi, posi) ? 1 : 0;
+    pick = rank < ns;
+  }
+  // ascending-position slot of each chosen candidate (candidates are ascending)
+  const int lane = tid & (kWave - 1), w = tid / kWave;
+  const int v = pick ? 1 : 0;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) s_cnt[w] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int k = 0; k < kChooseThreads / kWave; ++k) { const int t = s_cnt[k]; s_cnt[k] = acc; acc += t; }
+    s_cnt[kChooseThreads / kWave] = acc;
+  }
+  __syncthreads();
+  float hmax = -INFINITY;
+  int hnan = 0;
+  if (pick) {
+    const int slot = s_cnt[w] + incl - v;
+    const int pos = s_pos[tid];
+    chosen[slot] = pos;
+    tokens[pos] = argmax[tid];
+    is_masked[pos] = 0;
+    history[(hl + slot) % history_cap] = pos;
+    const float h = H[tid];
+    if (h != h) hnan = 1; else hmax = h;
+  }
+  hmax = wave_max(hmax);
+  hnan = wave_sum_i(hnan);
+  if (lane == 0) { s_max[w] = hmax; s_nan[w] = hnan; }
+  __syncthreads();
+  if (tid == 0) {
+    float b = -INFINITY;
+    int n = 0;
+    for (int k = 0; k < kChooseThreads / kWave; ++k) { b = fmaxf(b, s_max[k]); n += s_nan[k]; }
+    const int total = s_cnt[kChooseThreads / kWave];
+    const float E = n ? NAN : b;
+    *n_chosen = total;
+    *history_len = hl + total;
+    *e_max = E;
+    *flag = (n || E > tau) ? 1 : 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_embed(int dtype, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
+                        const int32_t* rows, const int32_t* n_rows, int max_rows, int d, void* x,
+                        hipStream_t s) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(max_rows), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(tok_emb), static_cast<const bf16_t*>(pos_emb),
+                       tokens, rows, n_rows, d, static_cast<bf16_t*>(x));
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(max_rows), dim3(256), 0, s,
+                       static_cast<const float*>(tok_emb), static_cast<const float*>(pos_emb),
+                       tokens, rows, n_rows, d, static_cast<float*>(x));
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int dtype, const void* x, const int32_t* n_rows, int max_rows, int d,
+                          const void* gain, float eps, void* out, hipStream_t s) {
+  if (dtype == 1)
+    hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(max_rows), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(x), n_rows, d, static_cast<const bf16_t*>(gain),
+                       eps, static_cast<bf16_t*>(out));
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(max_rows), dim3(256), 0, s,
+                       static_cast<const float*>(x), n_rows, d, static_cast<const float*>(gain), eps,
+                       static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+int32_t choose_max_candidates() { return kChooseThreads; }
+
+hipError_t launch_choose_decide(const int32_t* cand_pos, const int32_t* n_cand, const float* H,
+                                const int32_t* argmax, const float* p1, int32_t n_unmask,
+                                float tau, int32_t* chosen, int32_t* n_chosen, int32_t* tokens,
+                                uint8_t* is_masked, int32_t* history, int32_t* history_len,
+                                int32_t history_cap, float* e_max, int32_t* flag, hipStream_t s) {
+  hipLaunchKernelGGL(choose_decide_kernel, dim3(1), dim3(kChooseThreads), 0, s, cand_pos, n_cand, H,
+                     argmax, p1, n_unmask, tau, chosen, n_chosen, tokens, is_masked, history,
+                     history_len, history_cap, e_max, flag);
+  return hipGetLastError();
+}
+
+}  // namespace ec

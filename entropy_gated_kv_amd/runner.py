@@ -1,0 +1,150 @@
+"""Device buffers for one model and one sequence, and a step loop over ec_step.
+
+Argument marshalling only: this module allocates torch tensors, fills the
+ec_model / ec_state structs with their addresses and calls the C entry point.
+Every step of the computation runs inside libec.so.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+from . import lib as L
+
+
+def _torch_dtype(dtype: str):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+
+def to_device(a: np.ndarray, dtype: str):
+    """Upload a float32 array (holding values exact in `dtype`) as a device tensor."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(_torch_dtype(dtype)).cuda()
+
+
+class DeviceModel:
+    """Weights in HBM plus the ec_model struct that points at them."""
+
+    def __init__(self, shape, dtype: str, L_cap: int, weights: Dict[str, object]):
+        import torch
+        self.shape, self.dtype, self.L_cap = shape, dtype, L_cap
+        self.code = L.EC_BF16 if dtype == "bf16" else L.EC_F32
+        up = lambda a: None if a is None else to_device(a, dtype)  # noqa: E731
+        self.tok_emb = up(weights["tok_emb"])
+        pos = np.zeros((L_cap, shape.d), dtype=np.float32)
+        pos[: weights["pos_emb"].shape[0]] = weights["pos_emb"]
+        self.pos_emb = up(pos)
+        self.w_lm = up(weights["w_lm"])
+        self.norm_final = up(weights.get("norm_final"))
+        ls = weights.get("logit_scale")
+        self.logit_scale = None
+        if ls is not None:
+            buf = np.ones(L_cap, dtype=np.float32)
+            buf[: len(ls)] = ls
+            self.logit_scale = torch.from_numpy(buf).cuda()
+        self.layers = []
+        for lw in weights["layers"]:
+            self.layers.append({k: up(v) for k, v in lw.items()})
+        self._layer_arr = (L.ec_layer * len(self.layers))()
+        for i, lw in enumerate(self.layers):
+            ptr = lambda k: None if lw.get(k) is None else lw[k].data_ptr()  # noqa: E731
+            self._layer_arr[i] = L.ec_layer(ptr("w_qkv"), ptr("w_o"), ptr("norm_attn"),
+                                            ptr("norm_ffn"), ptr("w_gate"), ptr("w_up"),
+                                            ptr("w_down"))
+        m = L.ec_model()
+        m.n_layers, m.d, m.Hq, m.Hkv = len(self.layers), shape.d, shape.n_q_heads, shape.n_kv_heads
+        m.dh, m.d_ffn, m.V, m.L_cap, m.dtype = shape.head_dim, shape.d_ffn, shape.vocab, L_cap, self.code
+        m.rms_eps = shape.rms_eps
+        m.tok_emb, m.pos_emb = self.tok_emb.data_ptr(), self.pos_emb.data_ptr()
+        m.layers = C.cast(self._layer_arr, C.POINTER(L.ec_layer))
+        m.norm_final = None if self.norm_final is None else self.norm_final.data_ptr()
+        m.w_lm = self.w_lm.data_ptr()
+        m.logit_scale = None if self.logit_scale is None else self.logit_scale.data_ptr()
+        self.struct = m
+
+
+class DeviceSequence:
+    """Per-sequence device state (tokens, mask, history, flag, KV caches, step outputs)."""
+
+    def __init__(self, model: DeviceModel, tokens: np.ndarray, masked: np.ndarray,
+                 history_cap: int, max_block: int):
+        import torch
+        sh = model.shape
+        self.model, self.L, self.max_block = model, len(tokens), max_block
+        dev = "cuda"
+        i32 = torch.int32
+        self.tokens = torch.tensor(np.asarray(tokens, dtype=np.int32), device=dev)
+        self.is_masked = torch.tensor(np.asarray(masked, dtype=np.uint8), device=dev)
+        self.history = torch.full((history_cap,), -1, dtype=i32, device=dev)
+        self.history_len = torch.zeros(1, dtype=i32, device=dev)
+        self.full_flag = torch.ones(1, dtype=i32, device=dev)
+        td = _torch_dtype(model.dtype)
+        self.k_cache = [torch.zeros((sh.n_kv_heads, model.L_cap, sh.head_dim), dtype=td, device=dev)
+                        for _ in range(sh.n_layers)]
+        self.v_cache = [torch.zeros((sh.n_kv_heads, sh.head_dim, model.L_cap), dtype=td, device=dev)
+                        for _ in range(sh.n_layers)]
+        self.rows = torch.zeros(model.L_cap, dtype=i32, device=dev)
+        self.n_rows = torch.zeros(1, dtype=i32, device=dev)
+        self.logits = torch.zeros((max_block, sh.vocab), dtype=td, device=dev)
+        self.row_entropy = torch.zeros(max_block, dtype=torch.float32, device=dev)
+        self.row_argmax = torch.zeros(max_block, dtype=i32, device=dev)
+        self.row_top1 = torch.zeros(max_block, dtype=torch.float32, device=dev)
+        self.chosen = torch.zeros(max_block, dtype=i32, device=dev)
+        self.n_chosen = torch.zeros(1, dtype=i32, device=dev)
+        self.e_max = torch.zeros(1, dtype=torch.float32, device=dev)
+        nbytes = L.ec_step_workspace_bytes(model.struct, max_block)
+        if nbytes == 0:
+            raise RuntimeError("ec_step_workspace_bytes rejected the model shape")
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self._k_arr = (C.c_void_p * sh.n_layers)(*[t.data_ptr() for t in self.k_cache])
+        self._v_arr = (C.c_void_p * sh.n_layers)(*[t.data_ptr() for t in self.v_cache])
+        s = L.ec_state()
+        s.L, s.tokens, s.is_masked = self.L, self.tokens.data_ptr(), self.is_masked.data_ptr()
+        s.history, s.history_len, s.history_cap = (self.history.data_ptr(),
+                                                   self.history_len.data_ptr(), history_cap)
+        s.full_flag = self.full_flag.data_ptr()
+        s.k_cache = C.cast(self._k_arr, C.POINTER(C.c_void_p))
+        s.v_cache = C.cast(self._v_arr, C.POINTER(C.c_void_p))
+        s.rows, s.n_rows, s.logits = self.rows.data_ptr(), self.n_rows.data_ptr(), self.logits.data_ptr()
+        s.row_entropy, s.row_argmax = self.row_entropy.data_ptr(), self.row_argmax.data_ptr()
+        s.row_top1, s.chosen = self.row_top1.data_ptr(), self.chosen.data_ptr()
+        s.n_chosen, s.e_max = self.n_chosen.data_ptr(), self.e_max.data_ptr()
+        self.struct = s
+
+    def step(self, tau: float, k: int, block_start: int, block_len: int, n_unmask: int,
+             phase_events=None) -> None:
+        cfg = L.ec_step_cfg(float(tau), int(k), int(n_unmask), int(block_start), int(block_len))
+        L.ec_step(self.model.struct, self.struct, cfg, self.ws, phase_events)
+
+    # -- state transfer (tests: teacher forcing and read-back) -------------------
+    def load_state(self, tokens, masked, history: Sequence[int], flag: int,
+                   K: Optional[List[np.ndarray]] = None, V: Optional[List[np.ndarray]] = None):
+        """Overwrite the device state; K/V given as [Hkv, L, dh] float arrays."""
+        import torch
+        cap = self.history.numel()
+        ring = np.full(cap, -1, dtype=np.int32)
+        for i, p in enumerate(history):
+            ring[i % cap] = p
+        self.tokens.copy_(torch.from_numpy(np.asarray(tokens, dtype=np.int32)))
+        self.is_masked.copy_(torch.from_numpy(np.asarray(masked, dtype=np.uint8)))
+        self.history.copy_(torch.from_numpy(ring))
+        self.history_len.fill_(len(history))
+        self.full_flag.fill_(int(flag))
+        if K is not None:
+            for l in range(len(self.k_cache)):
+                Lq = K[l].shape[1]
+                self.k_cache[l][:, :Lq].copy_(to_device(K[l].astype(np.float32), self.model.dtype))
+                vt = np.ascontiguousarray(V[l].transpose(0, 2, 1)).astype(np.float32)
+                self.v_cache[l][:, :, :Lq].copy_(to_device(vt, self.model.dtype))
+
+    def caches(self, layer: int):
+        """(K [Hkv, L, dh], V [Hkv, L, dh]) of one layer as float64 numpy arrays."""
+        Lq = self.L
+        k = self.k_cache[layer][:, :Lq].float().cpu().numpy().astype(np.float64)
+        v = self.v_cache[layer][:, :, :Lq].float().cpu().numpy().astype(np.float64).transpose(0, 2, 1)
+        return k, v
+

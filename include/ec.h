@@ -1,0 +1,284 @@
+/*
+ * ec.h -- C ABI of the EntropyCache denoising-step library (libec.so, gfx950).
+ *
+ * One EntropyCache denoising step (paper "EntropyCache: Decoded Token Entropy
+ * Guided KV Caching for Diffusion Language Models"; Chinese summary page
+ * gist.science/zh/paper/2603.18489, technical summary §2.2, algorithm
+ * workflow) has three phases: a forward pass that is full or partial according
+ * to the previous step's flag, decoding plus the maximum entropy of the newly
+ * decoded tokens, and the threshold decision that sets the next step's flag.
+ * The entry points below are those phases and the kernels inside them.
+ *
+ * Conventions shared by every entry point
+ *  - Tensor arguments are DEVICE pointers, allocated and owned by the caller.
+ *    The library never allocates or frees device memory; scratch space is a
+ *    caller-provided workspace sized by the matching *_workspace_bytes().
+ *  - Work is enqueued on the caller's stream and the call returns at once; no
+ *    call synchronises the device or reads device memory on the host.  Row
+ *    counts and decision flags that live in device memory stay there.
+ *  - Every call returns an ec_status.  All argument checks run on the host
+ *    before anything is enqueued, and nothing is enqueued on an error.
+ *  - Tensor pointers must be 16-byte aligned and row strides multiples of 16
+ *    bytes (EC_E_ALIGN otherwise).
+ *  - dtype is EC_F32 or EC_BF16 for activations, weights, caches and logits of
+ *    one call.  Entropies, maxima and probabilities are always float32.
+ *  - The library keeps no global mutable state; calls on different streams
+ *    with disjoint buffers may run concurrently.
+ */
+#ifndef EC_H_
+#define EC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ec_status {
+  EC_OK = 0,
+  EC_E_NULL = -1,        /* a required pointer is NULL                        */
+  EC_E_SHAPE = -2,       /* a size is out of range or inconsistent             */
+  EC_E_DTYPE = -3,       /* unknown dtype                                      */
+  EC_E_WORKSPACE = -4,   /* workspace smaller than *_workspace_bytes()         */
+  EC_E_ALIGN = -5,       /* pointer or stride not 16-byte aligned              */
+  EC_E_LAUNCH = -6,      /* the HIP runtime refused a launch                   */
+  EC_E_UNSUPPORTED = -7  /* a valid but unsupported combination (e.g. head dim) */
+} ec_status;
+
+enum { EC_F32 = 0, EC_BF16 = 1 };
+
+/* Static description of a status code (never NULL). */
+const char* ec_status_string(int32_t status);
+
+/* ABI revision of this header; bumped on any signature or struct change. */
+int32_t ec_abi_version(void);
+#define EC_ABI_VERSION 1
+
+/* --------------------------------------------------------------------------
+ * Entropy pass (a1) and decision (a2).
+ *
+ * Source: EntropyCache Chinese summary page, §2.2: E_{t+1} is the largest
+ * softmax entropy -sum_j p_ij ln p_ij over the newly decoded tokens i, and
+ * E_{t+1} > tau sends the next step to a full forward, E_{t+1} <= tau to a
+ * partial one; §2.3: the decision costs O(V) compute.  The Portuguese page
+ * (gist.science/pt/paper/2603.18489, §2) states the same strict ">" rule.
+ *
+ * For each row r < n_rows of logits [n_rows, row_stride] (dtype elements,
+ * first V of each row used):
+ *   row_entropy[r] = H = -sum_j p_j ln p_j with p = softmax(row) (nats)
+ *   row_argmax[r]  = lowest j with row[j] = max (NaN ignored; all-NaN -> 0)
+ *   row_top1[r]    = max_j p_j
+ * then over the decoded rows D:
+ *   *e_max     = max_{r in D} H_r   (-inf if D is empty, NaN if any H_r is NaN)
+ *   *full_flag = (*e_max > tau) || isnan(*e_max)
+ * -inf logits contribute p = 0.  A row containing NaN or +inf has H = NaN and
+ * p1 = NaN; an all -inf row has H = p1 = NaN.
+ *
+ * D is decoded_rows[0 .. *n_decoded) (device int32 indices into the rows,
+ * each < n_rows; *n_decoded <= max_decoded), or every row when decoded_rows
+ * is NULL (then n_decoded is ignored).
+ *
+ * Determinism: the per-row results depend only on that row's V logits (the
+ * split of V into segments depends on V alone), so they are bitwise identical
+ * whatever n_rows, D or the other rows are.
+ *
+ * row_argmax and row_top1 may be NULL.  ws must hold
+ * ec_entropy_workspace_bytes(n_rows, V) bytes (16-byte aligned); it holds
+ * per-segment partial statistics.  Two calls that overlap in time must not
+ * share a workspace.
+ * Errors: EC_E_NULL (logits, row_entropy, e_max, full_flag or ws NULL),
+ * EC_E_SHAPE (n_rows < 1, V < 1, row_stride < V, max_decoded < 0),
+ * EC_E_DTYPE, EC_E_ALIGN, EC_E_WORKSPACE, EC_E_LAUNCH.
+ * ------------------------------------------------------------------------ */
+size_t ec_entropy_workspace_bytes(int64_t n_rows, int64_t V);
+
+int32_t ec_entropy_max(const void* logits, int32_t dtype, int64_t n_rows, int64_t V,
+                       int64_t row_stride,
+                       const int32_t* decoded_rows, const int32_t* n_decoded, int32_t max_decoded,
+                       float tau,
+                       float* row_entropy, int32_t* row_argmax, float* row_top1,
+                       float* e_max, int32_t* full_flag,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * Row selection (a3).
+ *
+ * Source: EntropyCache Chinese page §2.2 and Portuguese page §2: a full step
+ * recomputes every position; a partial step recomputes only the still-masked
+ * tokens and the k most recently decoded tokens, kept in a decode history
+ * (O(k) memory, Chinese page §2.3); all other positions read the KV cache.
+ *
+ *   *full_flag != 0:  rows = 0, 1, ..., L-1
+ *   *full_flag == 0:  rows = ascending union of
+ *                       { p in [block_start, block_start+block_len) : is_masked[p] }
+ *                     and the last min(k, *history_len) entries of the history
+ *
+ * history is a ring of history_cap device int32 positions: entry i (the i-th
+ * position ever decoded, 0-based) is at history[i % history_cap]; *history_len
+ * is the total count appended.  Requires k <= history_cap.  Positions must be
+ * < L; duplicates in the union are written once.
+ * Outputs: rows [L] (device, first *n_rows valid) and *n_rows (device).
+ * Errors: EC_E_NULL, EC_E_SHAPE (L < 1, block outside [0, L), k < 0,
+ * k > history_cap, history_cap < 1), EC_E_LAUNCH.
+ * ------------------------------------------------------------------------ */
+int32_t ec_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
+                       int32_t block_start, int32_t block_len,
+                       const int32_t* history, const int32_t* history_len, int32_t history_cap,
+                       int32_t k, int32_t* rows, int32_t* n_rows, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * Selective KV refresh (a4).
+ *
+ * Source: EntropyCache Chinese page §2.2 (a partial pass recomputes K/V only
+ * for the selected rows, the rest is read from the cache) and Portuguese page
+ * §2 (the full pass refreshes the whole KV cache).
+ *
+ * For r < *n_rows (device count, <= max_rows):
+ *   y_r = x[r, :] . W^T        (W = w_qkv [(Hq + 2 Hkv) * dh, d], row-major,
+ *                               output features ordered Q heads, K heads, V heads)
+ *   q_out[r, h, :]               = y_r[h*dh : (h+1)*dh]                 h < Hq
+ *   k_cache[g, rows[r], :]       = y_r[(Hq+g)*dh : ...]                 g < Hkv
+ *   v_cache[g, :, rows[r]]       = y_r[(Hq+Hkv+g)*dh : ...]             g < Hkv
+ * Layouts: x [max_rows, x_stride] (x_stride >= d), q_out [max_rows, Hq, dh],
+ * k_cache [Hkv, L_cap, dh], v_cache [Hkv, dh, L_cap] (V is stored transposed
+ * so that the attention's P.V contraction reads contiguous positions).
+ * Cache rows not listed in rows[] are left untouched.  Accumulation is fp32;
+ * outputs are rounded to dtype (nearest even).  rows[r] < L_cap, distinct.
+ * ws holds split-K partial sums: ec_kv_refresh_workspace_bytes(...) bytes
+ * (may be 0, then ws may be NULL).
+ * Supported: d % 64 == 0, dh in {32, 64, 128}, Hq % Hkv == 0.
+ * Errors: EC_E_NULL, EC_E_SHAPE, EC_E_DTYPE, EC_E_ALIGN, EC_E_WORKSPACE,
+ * EC_E_UNSUPPORTED, EC_E_LAUNCH.
+ * ------------------------------------------------------------------------ */
+size_t ec_kv_refresh_workspace_bytes(int32_t max_rows, int32_t d, int32_t Hq, int32_t Hkv,
+                                     int32_t dh, int32_t dtype);
+
+int32_t ec_kv_refresh(const void* x, int64_t x_stride, const int32_t* rows, const int32_t* n_rows,
+                      int32_t max_rows, const void* w_qkv, int32_t d, int32_t Hq, int32_t Hkv,
+                      int32_t dh, int32_t dtype, void* q_out, void* k_cache, void* v_cache,
+                      int32_t L_cap, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * Bidirectional attention of the selected rows against the whole cache (a5).
+ *
+ * Source: EntropyCache Portuguese page §1 and Chinese page §1: diffusion LMs
+ * use bidirectional attention, so every position attends to every position
+ * (no causal mask); the selected rows' queries read all L cache rows, fresh or
+ * stale.  The split of the cache into partitions merged by log-sum-exp follows
+ * the split-KV kernel described on the Prefilling-dLLM page
+ * (gist.science/pt/paper/2606.10537, attention-kernel section).
+ *
+ * For r < *n_rows, h < Hq, g = h / (Hq / Hkv):
+ *   out[r, h, :] = softmax_j( scale * q[r, h, :] . K[g, j, :] ) . V[g, j, :],  j < L
+ * with K = k_cache [Hkv, L_cap, dh] and V stored transposed, v_cache
+ * [Hkv, dh, L_cap].  fp32 accumulation, output rounded to dtype.
+ * q [max_rows, Hq, dh], out [max_rows, Hq, dh].  1 <= L <= L_cap.
+ * ws must hold ec_attention_workspace_bytes(max_rows, L, Hq, Hkv, dh).
+ * Supported: dh in {32, 64, 128}, Hq % Hkv == 0, Hq / Hkv <= 16.
+ * Errors: EC_E_NULL, EC_E_SHAPE, EC_E_DTYPE, EC_E_ALIGN, EC_E_WORKSPACE,
+ * EC_E_UNSUPPORTED, EC_E_LAUNCH.
+ * ------------------------------------------------------------------------ */
+size_t ec_attention_workspace_bytes(int32_t max_rows, int32_t L, int32_t Hq, int32_t Hkv,
+                                    int32_t dh);
+
+int32_t ec_bidir_attention(const void* q, const int32_t* n_rows, int32_t max_rows,
+                           const void* k_cache, const void* v_cache, int32_t L, int32_t L_cap,
+                           int32_t Hq, int32_t Hkv, int32_t dh, float scale, int32_t dtype,
+                           void* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
+ * One full denoising step (all of the above plus the glue around them).
+ *
+ * Source: EntropyCache Chinese page §2.2 (the three phases of a step) and
+ * Portuguese page §2 (decode, skip-or-recompute decision, decode history).
+ *
+ * Sequence per call, all on `stream`, no host synchronisation:
+ *   rows   = select(*full_flag, is_masked, current block, history, k)
+ *   x      = tok_emb[tokens[rows]] + pos_emb[rows]
+ *   per layer: [a = rmsnorm(x) * norm_attn] ; refresh Q/K/V of rows ;
+ *              o = attention(Q, whole cache) ; x += o . W_o^T ;
+ *              [a2 = rmsnorm(x) * norm_ffn ; x += (silu(a2 W_gate^T) * a2 W_up^T) . W_down^T]
+ *   [x = rmsnorm(x) * norm_final]
+ *   cand   = masked positions of the current block (ascending)
+ *   logits[i, :] = (x[cand_i] . W_lm^T) * logit_scale[cand_i]
+ *   per candidate: H, argmax, p1 (as ec_entropy_max)
+ *   chosen = the min(n_unmask, |cand|) candidates of largest p1 (ties -> lower position)
+ *   tokens[c] = argmax_c, is_masked[c] = 0 for c in chosen;
+ *   chosen positions appended to the history ring in ascending order
+ *   *e_max = max H over chosen (-inf if none); *full_flag = (*e_max > tau) || isnan
+ * The first step of a sequence must run with *full_flag = 1 (no cache yet).
+ * ws (ec_step_workspace_bytes(model, max_block) bytes) must be zero-filled
+ * before its first use; steps leave its counters zeroed.
+ * Norms and FFN are present iff d_ffn > 0.  The block (block_start,
+ * block_len) and n_unmask are host values: the schedule is fixed on the host.
+ * ------------------------------------------------------------------------ */
+typedef struct ec_layer {
+  const void* w_qkv;      /* [(Hq + 2 Hkv) * dh, d]                      */
+  const void* w_o;        /* [d, Hq * dh]                                */
+  const void* norm_attn;  /* [d] (d_ffn > 0 only, else NULL)             */
+  const void* norm_ffn;   /* [d] (d_ffn > 0 only)                        */
+  const void* w_gate;     /* [d_ffn, d] (d_ffn > 0 only)                 */
+  const void* w_up;       /* [d_ffn, d] (d_ffn > 0 only)                 */
+  const void* w_down;     /* [d, d_ffn] (d_ffn > 0 only)                 */
+} ec_layer;
+
+typedef struct ec_model {
+  int32_t n_layers, d, Hq, Hkv, dh, d_ffn, V, L_cap, dtype;
+  float rms_eps;
+  const void* tok_emb;        /* [V + 1, d]; row V is the MASK embedding   */
+  const void* pos_emb;        /* [L_cap, d]                                */
+  const ec_layer* layers;     /* host array [n_layers]                     */
+  const void* norm_final;     /* [d] (d_ffn > 0 only)                      */
+  const void* w_lm;           /* [V, d]                                    */
+  const float* logit_scale;   /* [L_cap] device float32, or NULL (= 1)     */
+} ec_model;
+
+typedef struct ec_state {
+  int32_t L;                  /* sequence length, <= L_cap                 */
+  int32_t* tokens;            /* [L] device                                */
+  uint8_t* is_masked;         /* [L] device                                */
+  int32_t* history;           /* [history_cap] device ring                 */
+  int32_t* history_len;       /* [1] device                                */
+  int32_t history_cap;
+  int32_t* full_flag;         /* [1] device: read as this step's mode, then
+                                 overwritten with the next step's decision */
+  void* const* k_cache;       /* host array [n_layers] of [Hkv, L_cap, dh] */
+  void* const* v_cache;       /* host array [n_layers] of [Hkv, dh, L_cap] */
+  /* per-step outputs (device, caller-owned) */
+  int32_t* rows;              /* [L_cap]                                   */
+  int32_t* n_rows;            /* [1]                                       */
+  void* logits;               /* [max_block, V] dtype                      */
+  float* row_entropy;         /* [max_block]                               */
+  int32_t* row_argmax;        /* [max_block]                               */
+  float* row_top1;            /* [max_block]                               */
+  int32_t* chosen;            /* [max_block] positions, ascending          */
+  int32_t* n_chosen;          /* [1]                                       */
+  float* e_max;               /* [1]                                       */
+} ec_state;
+
+typedef struct ec_step_cfg {
+  float tau;
+  int32_t k;
+  int32_t n_unmask;
+  int32_t block_start;
+  int32_t block_len;          /* <= max_block of the workspace             */
+} ec_step_cfg;
+
+/* Optional per-phase timing: when non-NULL, ec_step records events[2*i] and
+ * events[2*i+1] around phase i on the stream (phases: see EC_PHASE_*). */
+enum {
+  EC_PHASE_SELECT = 0, EC_PHASE_EMBED, EC_PHASE_QKV, EC_PHASE_ATTN, EC_PHASE_OPROJ,
+  EC_PHASE_FFN, EC_PHASE_LMHEAD, EC_PHASE_ENTROPY, EC_PHASE_DECIDE, EC_PHASE_COUNT
+};
+
+size_t ec_step_workspace_bytes(const ec_model* model, int32_t max_block);
+
+int32_t ec_step(const ec_model* model, const ec_state* state, const ec_step_cfg* cfg,
+                void* ws, size_t ws_bytes, hipEvent_t* phase_events, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EC_H_ */

@@ -90,6 +90,7 @@ class StepTrace:
     chosen: np.ndarray
     E: float
     flag_next: int
+    x_cand: Optional[np.ndarray] = None   # final activations of the candidate rows
 
 
 def init_state(model: Model, tokens, masked) -> State:
@@ -146,7 +147,7 @@ def step(model: Model, state: State, tau: float, k: int, block_start: int, block
     E = max_entropy(H, pick)
     state.flag = decide(E, tau)
     return StepTrace(flag_used, rows, cand, z if keep_logits else None, H, A, P, chosen, E,
-                     state.flag)
+                     state.flag, x[ci] if keep_logits else None)
 
 
 def generate(model: Model, state: State, schedule: Sequence[Tuple[int, int, int]], tau: float,

@@ -1,0 +1,97 @@
+"""The C-ABI library loads on a CPU-only host, exports every function include/ec.h
+declares, and rejects bad arguments on the host with the documented status
+codes (no call here reaches a kernel launch)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from entropy_gated_kv_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ec.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(ec_[a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTED)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ec_abi_version() == 1
+    for s in range(-7, 1):
+        assert lib.ec_status_string(s)
+    assert lib.ec_status_string(99) == b"unknown status"
+
+
+def test_workspace_queries(lib):
+    assert lib.ec_entropy_workspace_bytes(4096, 126464) >= 4096 * 8 * 16
+    assert lib.ec_entropy_workspace_bytes(0, 10) == 0
+    assert lib.ec_attention_workspace_bytes(0, 1, 1, 1, 32) == 0
+
+
+FAKE = 1 << 20       # an aligned, never dereferenced address
+ODD = FAKE + 4       # misaligned
+
+
+def test_entropy_argument_checks(lib):
+    f = lib.ec_entropy_max
+    ws = lib.ec_entropy_workspace_bytes(4, 100)
+    args = [FAKE, 1, 4, 100, 104, None, None, 0, 1.0, FAKE, None, None, FAKE, FAKE, FAKE, ws, None]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=None) == -1
+    assert call(a1=7) == -3
+    assert call(a2=0) == -2
+    assert call(a4=99) == -2                 # stride < V
+    assert call(a0=ODD) == -5
+    assert call(a4=101) == -5                # stride not a multiple of 16 bytes
+    assert call(a15=ws - 1) == -4
+    assert call(a5=FAKE, a6=None) == -1      # decoded rows without a count
+
+
+def test_select_and_refresh_and_attention_checks(lib):
+    assert lib.ec_select_rows(FAKE, FAKE, 10, 8, 4, FAKE, FAKE, 16, 4, FAKE, FAKE, None) == -2
+    assert lib.ec_select_rows(FAKE, FAKE, 10, 0, 4, FAKE, FAKE, 2, 4, FAKE, FAKE, None) == -2
+    assert lib.ec_select_rows(None, FAKE, 10, 0, 4, FAKE, FAKE, 16, 4, FAKE, FAKE, None) == -1
+    assert lib.ec_kv_refresh(FAKE, 128, FAKE, FAKE, 4, FAKE, 128, 4, 4, 48, 1, FAKE, FAKE, FAKE,
+                             16, None, 0, None) == -7              # head dim 48
+    assert lib.ec_kv_refresh(FAKE, 128, FAKE, FAKE, 4, FAKE, 128, 4, 3, 32, 1, FAKE, FAKE, FAKE,
+                             16, None, 0, None) == -2              # Hq % Hkv
+    assert lib.ec_kv_refresh(FAKE, 128, FAKE, FAKE, 4, FAKE, 128, 4, 4, 32, 2, FAKE, FAKE, FAKE,
+                             16, None, 0, None) == -3
+    need = lib.ec_kv_refresh_workspace_bytes(96, 4096, 32, 32, 128, 1)
+    assert need > 0
+    assert lib.ec_kv_refresh(FAKE, 4096, FAKE, FAKE, 96, FAKE, 4096, 32, 32, 128, 1, FAKE, FAKE,
+                             FAKE, 1024, FAKE, need - 1, None) == -4
+    assert lib.ec_bidir_attention(FAKE, FAKE, 4, FAKE, FAKE, 17, 16, 4, 4, 32, 0.17, 1, FAKE, FAKE,
+                                  1 << 20, None) == -2             # L > L_cap
+    assert lib.ec_bidir_attention(FAKE, FAKE, 4, FAKE, FAKE, 8, 16, 4, 4, 32, -1.0, 1, FAKE, FAKE,
+                                  1 << 20, None) == -2             # bad scale
+
+
+def test_step_argument_checks(lib):
+    m = L.ec_model()
+    assert lib.ec_step_workspace_bytes(C.byref(m), 32) == 0        # n_layers = 0
+    st, cfg = L.ec_state(), L.ec_step_cfg()
+    assert lib.ec_step(C.byref(m), C.byref(st), C.byref(cfg), FAKE, 0, None, None) == -2
+    assert lib.ec_step(None, C.byref(st), C.byref(cfg), FAKE, 0, None, None) == -1

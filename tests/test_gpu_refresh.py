@@ -1,0 +1,66 @@
+"""GPU parity of the selective KV refresh (ec_kv_refresh) against the oracle.
+
+Q and the refreshed cache rows within 2e-3 (fp32) / 2e-2 (bf16) abs and rel;
+cache rows not selected must be bitwise unchanged (sentinel-filled caches).
+Row counts cover 1..4 row blocks of the skinny kernel, the 128-row boundary,
+the tiled kernel with a ragged last tile, and the LLaDA-shaped full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from entropy_gated_kv_amd import lib as L
+from synth import generators as G
+from tests.gpu_helpers import assert_close, dev, host, i32
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(dtype, d, Hq, Hkv, dh, Lc, rows, seed, sample=None):
+    n = len(rows)
+    x = G.random_matrix(seed, (1, n, d), (n, d), 1.0, dtype)
+    W = G.random_matrix(seed, (2, d), ((Hq + 2 * Hkv) * dh, d), 0.02, dtype)
+    xd, Wd = dev(x, dtype), dev(W, dtype)
+    sentinel = 7.0
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    K = torch.full((Hkv, Lc, dh), sentinel, dtype=td, device="cuda")
+    Vt = torch.full((Hkv, dh, Lc), -sentinel, dtype=td, device="cuda")
+    q = torch.zeros((n, Hq, dh), dtype=td, device="cuda")
+    ws_n = L.ec_kv_refresh_workspace_bytes(n, d, Hq, Hkv, dh, L.EC_BF16 if dtype == "bf16" else L.EC_F32)
+    ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+    L.ec_kv_refresh(xd, i32(rows), i32([n]), Wd, Hq, Hkv, dh, q, K, Vt, ws)
+    torch.cuda.synchronize()
+    pick = np.arange(n) if sample is None else np.asarray(sample)
+    Ko = np.zeros((Hkv, Lc, dh))
+    Vo = np.zeros((Hkv, Lc, dh))
+    qo = O.kv_refresh(x[pick].astype(np.float64), np.asarray(rows)[pick], W.astype(np.float64),
+                      Ko, Vo, Hq, Hkv, dh, dtype)
+    Kg, Vg = host(K), host(Vt).transpose(0, 2, 1)
+    sel = np.asarray(rows)[pick]
+    assert_close(host(q)[pick], qo, dtype, "Q")
+    assert_close(Kg[:, sel], Ko[:, sel], dtype, "K cache")
+    assert_close(Vg[:, sel], Vo[:, sel], dtype, "V cache")
+    keep = np.setdiff1d(np.arange(Lc), rows)
+    assert np.all(Kg[:, keep] == sentinel) and np.all(Vg[:, keep] == -sentinel), "unselected rows changed"
+
+
+@pytest.mark.parametrize("n", [1, 20, 64, 256])
+def test_tiny_fp32_shapes(n):
+    rows = np.sort(np.random.default_rng(n).choice(256, n, replace=False))
+    run_case("f32", 128, 4, 4, 32, 256, rows, seed=n)
+
+
+@pytest.mark.parametrize("n", [1, 7, 33, 96, 128, 129, 300])
+@pytest.mark.parametrize("dh", [64, 128])
+def test_bf16_gqa_shapes(n, dh):
+    Lc = 520
+    rows = np.sort(np.random.default_rng(n + dh).choice(Lc, n, replace=False))
+    run_case("bf16", 512, 8, 2, dh, Lc, rows, seed=n + dh)
+
+
+@pytest.mark.parametrize("n", [96, 1024])
+def test_llada_full_size_sampled(n):
+    Lc = 1024
+    rows = np.arange(Lc) if n == Lc else np.sort(np.random.default_rng(3).choice(Lc, n, replace=False))
+    run_case("bf16", 4096, 32, 32, 128, Lc, rows, seed=5, sample=[0, 1, n // 2, n - 1])
