@@ -139,7 +139,10 @@ def step(model: Model, state: State, tau: float, k: int, block_start: int, block
         z = z * model.logit_scale[cand][:, None]
     z = to_storage(z, model.dtype)
     H, A, P = row_stats(z)
-    chosen = choose(cand, P, n_unmask)
+    # The unmask choice ranks candidates by top-1 probability in float32, the
+    # precision of the kernel that produces it: peaked rows round to exactly
+    # 1.0 there, and such ties go to the lower position.
+    chosen = choose(cand, P.astype(np.float32).astype(np.float64), n_unmask)
     pick = np.searchsorted(cand, chosen)
     state.tokens[chosen] = A[pick]
     state.masked[chosen] = False
