@@ -8,8 +8,13 @@ Prints ONE JSON line (see the repository's design notes for the contract):
   cpu_baseline               the float64 oracle on a bounded sample of the same
                              workload, on this host's cores
 Workloads:
-  entropy   4096 x 126464 bf16 logits, one fused entropy pass per step (GB/s)
-  step      LLaDA-8B-shaped layer, L = 1024, EntropyCache loop (steps/s)
+  step      LLaDA-8B-shaped layer (d 4096, 32 x 128 heads, V 126464), L = 1024 =
+            512 prompt + 512 generated in blocks of 32, EntropyCache loop at
+            tau = 1.0 (k = 64): one step = select, embed, QKV refresh,
+            attention, O-projection, LM head, entropy pass, unmask + decision.
+            value = denoise steps/s.  Also: tau sweep, vanilla (tau = -inf).
+  entropy   4096 x 126464 bf16 logits, one entropy pass (GB/s); reported as
+            the "entropy_pass" object next to the step line.
 """
 from __future__ import annotations
 
@@ -137,14 +142,164 @@ def entropy_cpu_baseline(z, V: int) -> dict:
             "sample": f"{rows} of 4096 rows, one row at a time (NumPy float64, single thread), {dt:.1f} s"}
 
 
+# --------------------------------------------------------------------------- step
+PHASES = ("select", "embed", "qkv", "attn", "oproj", "ffn", "lmhead", "entropy", "decide")
+
+
+def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
+    import numpy as np
+    import torch
+
+    from entropy_gated_kv_amd.runner import DeviceModel, DeviceSequence
+    from synth import configs as C
+    from synth import generators as G
+
+    cfg = C.LLADA_LAYER
+    tau = 1.0
+    _log(f"generating weights of {cfg.name}")
+    w = G.model_weights(cfg)
+    toks, masked = G.initial_sequence(cfg)
+    dm = DeviceModel(cfg.model, cfg.dtype, cfg.L, w)
+    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len)
+    sched = C.unmask_schedule(cfg)
+    init = (ds.tokens.clone(), ds.is_masked.clone())
+    stream = torch.cuda.current_stream()
+
+    def reset():   # device-side copies only (no host synchronisation)
+        ds.tokens.copy_(init[0])
+        ds.is_masked.copy_(init[1])
+        ds.history_len.zero_()
+        ds.full_flag.fill_(1)
+
+    def run(n_steps, tau_, events=None, flags=None):
+        i = 0
+        while i < n_steps:
+            for j, (bs, bl, n) in enumerate(sched):
+                if i >= n_steps:
+                    break
+                if flags is not None:
+                    flags[i].copy_(ds.full_flag[0])
+                ev = None if events is None else events[i]
+                ds.step(tau_, cfg.k, bs, bl, n, phase_events=ev)
+                i += 1
+            else:
+                reset()
+
+    # warm-up, then the timed steps from a fresh sequence.  Inside the timed
+    # region only the dominant kernel (the LM head) is bracketed by events.
+    LM = PHASES.index("lmhead")
+    n_ev = 2 * len(PHASES)
+
+    def event_set(only_lm):
+        evs = []
+        for k in range(n_ev):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()                      # materialise the event handle
+            evs.append(e)
+        if only_lm:                         # other phases share one scratch pair
+            scratch = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            for e in scratch:
+                e.record()
+            for k in range(n_ev):
+                if k // 2 != LM:
+                    evs[k] = scratch[k % 2]
+        return evs
+
+    reset()
+    run(warmup, tau)
+    reset()
+    torch.cuda.synchronize()
+    timed_events = [event_set(True) for _ in range(steps)]
+    flags = torch.zeros(steps, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps, tau, timed_events, flags)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fl = flags.cpu().numpy()
+    lm_ms = float(np.mean([ev[2 * LM].elapsed_time(ev[2 * LM + 1]) for ev in timed_events]))
+
+    # untimed pass with every phase bracketed, for the breakdown
+    reset()
+    torch.cuda.synchronize()
+    n_bd = min(steps, len(sched))
+    bd_events = [event_set(False) for _ in range(n_bd)]
+    run(n_bd, tau, bd_events)
+    torch.cuda.synchronize()
+    phase_ms = {}
+    for k, name in enumerate(PHASES):
+        if name == "ffn":
+            continue
+        phase_ms[name] = float(np.mean([ev[2 * k].elapsed_time(ev[2 * k + 1]) for ev in bd_events]))
+    d, V, m = cfg.model.d, cfg.model.vocab, cfg.block_len
+    lm_bytes = V * d * 2 + m * d * 2 + m * V * 2
+    lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
+    decide_ms = phase_ms["select"] + phase_ms["entropy"] + phase_ms["decide"]
+    out = {
+        "value": steps / wall,
+        "ms_per_step": wall * 1e3 / steps,
+        "partial_fraction": float(1.0 - fl.mean()),
+        "phases_us": {k: round(v * 1e3, 2) for k, v in phase_ms.items()},
+        "decision_overhead_frac": decide_ms / sum(phase_ms.values()),
+        "roofline": {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic("gemm_skinny_kernel<bf16,lmhead>", "gemm.hip", 1),
+                     "kernel": "LM-head skinny GEMM (gemm_skinny_kernel<bf16,1,1,false,4>)",
+                     "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)},
+    }
+    _log(f"step: {out['value']:.1f} steps/s, {out['ms_per_step'] * 1e3:.1f} us/step, "
+         f"partial fraction {out['partial_fraction']:.2f}; LM head {lm_ms * 1e3:.1f} us = {lm_gbs:.0f} GB/s")
+    _log("phases (us, separate pass): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in phase_ms.items()))
+
+    # tau sweep and vanilla: one whole generation each
+    sweep = {}
+    for t in (0.5, 1.0, 2.0, float("-inf")):
+        reset()
+        torch.cuda.synchronize()
+        fl2 = torch.zeros(len(sched), dtype=torch.int32, device="cuda")
+        t1 = time.perf_counter()
+        run(len(sched), t, None, fl2)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t1
+        sweep[str(t)] = {"steps_per_s": round(len(sched) / dt, 2),
+                         "partial_fraction": round(float(1.0 - fl2.float().mean().item()), 3)}
+    out["tau_sweep"] = sweep
+    out["speedup_vs_vanilla_at_tau_1"] = round(sweep["1.0"]["steps_per_s"] / sweep["-inf"]["steps_per_s"], 3)
+    _log(f"tau sweep: {sweep}")
+    if cpu_baseline:
+        out["cpu_baseline"] = step_cpu_baseline(cfg, w, toks, masked, sched, tau)
+    return out
+
+
+def step_cpu_baseline(cfg, w, toks, masked, sched, tau) -> dict:
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    model = O.Model.from_arrays(cfg.model, cfg.dtype, w)
+    st = O.init_state(model, toks, masked)
+    n, n_full, t0 = 0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < 20.0 and n < len(sched):
+        bs, bl, nn = sched[n]
+        n_full += st.flag
+        O.step(model, st, tau, cfg.k, bs, bl, nn, keep_logits=False)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} steps of the tau=1.0 trajectory ({n_full} full, {n - n_full} partial), "
+                      f"NumPy float64, {dt:.1f} s"}
+
+
 # --------------------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="entropy", choices=["entropy"])
+    ap.add_argument("--steps", type=int, default=352)
+    ap.add_argument("--warmup", type=int, default=22)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-entropy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -154,11 +309,11 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
-    res = entropy_leg(args.steps, args.warmup, not args.no_cpu_baseline)
+    res = step_leg(args.steps, args.warmup, not args.no_cpu_baseline)
     line = {
         "metric": METRIC,
-        "value": round(res["GB_per_s"], 2),
-        "unit": "GB/s",
+        "value": round(res["value"], 2),
+        "unit": "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -168,12 +323,23 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "entropy_4096x126464_bf16", "rows": 4096, "vocab": 126464,
-                   "tau": 2.0},
+        "config": {"workload": "llada8b_layer_L1024_tau1.0", "L": 1024, "prompt": 512, "gen": 512,
+                   "block": 32, "d_model": 4096, "heads": "32x128", "vocab": 126464, "k": 64,
+                   "tau": 1.0, "layers": 1},
         "roofline": res["roofline"],
+        "partial_fraction": round(res["partial_fraction"], 3),
+        "phases_us": res["phases_us"],
+        "decision_overhead_frac": round(res["decision_overhead_frac"], 4),
+        "tau_sweep": res["tau_sweep"],
+        "speedup_vs_vanilla_at_tau_1": res["speedup_vs_vanilla_at_tau_1"],
     }
     if "cpu_baseline" in res:
         line["cpu_baseline"] = res["cpu_baseline"]
+    if not args.skip_entropy:
+        ent = entropy_leg(50, 5, not args.no_cpu_baseline)
+        line["entropy_pass"] = {"GB_per_s": round(ent["GB_per_s"], 1), "us_per_pass": round(ent["kernel_ms"] * 1e3, 2),
+                                "roofline": ent["roofline"], "workload": "entropy_4096x126464_bf16",
+                                "cpu_baseline": ent.get("cpu_baseline")}
     print(json.dumps(line), flush=True)
     return 0
 

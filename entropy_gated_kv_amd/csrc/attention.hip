@@ -343,8 +343,10 @@ SplitPlan plan_split(int L, int Hkv, int G) {
   sp.mcap = kPartialMaxRows * G;
   const int qtiles = (sp.mcap + kQT - 1) / kQT;
   const int tiles = (L + kKV - 1) / kKV;
+  // enough splits to give the chip two workgroups per CU, but at least 4 kv
+  // tiles (256 rows) per split so the partial outputs stay small
   int S = (2 * device_cu_count() + Hkv * qtiles - 1) / (Hkv * qtiles);
-  S = max(1, min(S, tiles));
+  S = max(1, min(S, (tiles + 3) / 4));
   const int per = (tiles + S - 1) / S;                    // kv tiles per split
   sp.kvps = per * kKV;
   sp.S = (tiles + per - 1) / per;

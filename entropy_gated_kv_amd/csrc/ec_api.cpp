@@ -127,7 +127,7 @@ int32_t ec_kv_refresh(const void* x, int64_t x_stride, const int32_t* rows, cons
   if (max_rows < 1 || d < 1 || Hq < 1 || Hkv < 1 || dh < 1 || L_cap < 1 || x_stride < d ||
       Hq % Hkv != 0)
     return EC_E_SHAPE;
-  if (d % 64 != 0 || !head_dim_ok(dh)) return EC_E_UNSUPPORTED;
+  if (d % ec::gemm_k_multiple(dtype) != 0 || !head_dim_ok(dh)) return EC_E_UNSUPPORTED;
   if (!al16(x) || !al16(w_qkv) || !al16(q_out) || !al16(k_cache) || !al16(v_cache) ||
       (ws && !al16(ws)) || (x_stride * int64_t(esize(dtype))) % 16 != 0)
     return EC_E_ALIGN;
@@ -235,8 +235,8 @@ StepLayout step_layout(const ec_model* m, int32_t max_block, void* ws) {
 struct PhaseTimer {
   hipEvent_t* ev;
   hipStream_t s;
-  void begin(int p) const { if (ev) (void)hipEventRecord(ev[2 * p], s); }
-  void end(int p) const { if (ev) (void)hipEventRecord(ev[2 * p + 1], s); }
+  hipError_t begin(int p) const { return ev ? hipEventRecord(ev[2 * p], s) : hipSuccess; }
+  hipError_t end(int p) const { return ev ? hipEventRecord(ev[2 * p + 1], s) : hipSuccess; }
 };
 
 }  // namespace
@@ -272,13 +272,18 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
       c->block_start + c->block_len > st->L || c->k < 0 || c->k > st->history_cap ||
       c->n_unmask < 0 || st->history_cap < 1)
     return EC_E_SHAPE;
-  if (m->d % 64 != 0 || !head_dim_ok(m->dh) || m->Hq / m->Hkv > 16 ||
+  const int km = ec::gemm_k_multiple(m->dtype);
+  if (m->d % km != 0 || (m->Hq * m->dh) % km != 0 || m->d_ffn % km != 0 || m->d_ffn % 32 != 0 ||
+      !head_dim_ok(m->dh) || m->Hq / m->Hkv > 16 ||
       c->block_len > ec::choose_max_candidates() || st->L > ec::select_max_L())
     return EC_E_UNSUPPORTED;
   if (!al16(ws) || !al16(m->tok_emb) || !al16(m->pos_emb) || !al16(m->w_lm) || !al16(st->logits) ||
       (int64_t(m->V) * int64_t(esize(m->dtype))) % 16 != 0 ||
       (int64_t(m->L_cap) * int64_t(esize(m->dtype))) % 16 != 0)
     return EC_E_ALIGN;
+  if (phase_events)
+    for (int i = 0; i < 2 * EC_PHASE_COUNT; ++i)
+      if (!phase_events[i]) return EC_E_NULL;
   const int32_t max_block = c->block_len;
   const StepLayout s = step_layout(m, max_block, ws);
   if (ws_bytes < s.total) return EC_E_WORKSPACE;
@@ -288,21 +293,21 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   const int hd = m->Hq * m->dh;
   const PhaseTimer tm{phase_events, stream};
 
-  tm.begin(EC_PHASE_SELECT);
+  EC_TRY(tm.begin(EC_PHASE_SELECT));
   EC_TRY(ec::launch_select_rows(st->full_flag, st->is_masked, L, c->block_start, c->block_len,
                                 st->history, st->history_len, st->history_cap, c->k, st->rows,
                                 st->n_rows, s.cand_pos, s.cand_idx, s.n_cand, stream));
-  tm.end(EC_PHASE_SELECT);
-  tm.begin(EC_PHASE_EMBED);
+  EC_TRY(tm.end(EC_PHASE_SELECT));
+  EC_TRY(tm.begin(EC_PHASE_EMBED));
   EC_TRY(ec::launch_embed(dt, m->tok_emb, m->pos_emb, st->tokens, st->rows, st->n_rows, L, m->d,
                           s.x, stream));
-  tm.end(EC_PHASE_EMBED);
+  EC_TRY(tm.end(EC_PHASE_EMBED));
 
   for (int l = 0; l < m->n_layers; ++l) {
     const ec_layer& ly = m->layers[l];
     const bool first = (l == 0);
     const void* a_in = s.x;
-    if (first) tm.begin(EC_PHASE_QKV);
+    if (first) EC_TRY(tm.begin(EC_PHASE_QKV));
     if (m->d_ffn) {
       EC_TRY(ec::launch_rmsnorm(dt, s.x, st->n_rows, L, m->d, ly.norm_attn, m->rms_eps, s.a, stream));
       a_in = s.a;
@@ -313,23 +318,23 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
     g.rows = st->rows; g.q_out = s.q; g.k_cache = st->k_cache[l]; g.v_cache = st->v_cache[l];
     g.Hq = m->Hq; g.Hkv = m->Hkv; g.dh = m->dh; g.L_cap = m->L_cap;
     EC_TRY(ec::launch_gemm_rows(g, s.gemm_ws, stream));
-    if (first) { tm.end(EC_PHASE_QKV); tm.begin(EC_PHASE_ATTN); }
+    if (first) { EC_TRY(tm.end(EC_PHASE_QKV)); EC_TRY(tm.begin(EC_PHASE_ATTN)); }
 
     ec::AttnArgs a;
     a.dtype = dt; a.q = s.q; a.n_rows_dev = st->n_rows; a.max_rows = L; a.k_cache = st->k_cache[l];
     a.v_cache = st->v_cache[l]; a.L = L; a.L_cap = m->L_cap; a.Hq = m->Hq; a.Hkv = m->Hkv;
     a.dh = m->dh; a.scale = 1.0f / sqrtf(float(m->dh)); a.out = s.o;
     EC_TRY(ec::launch_attention(a, s.attn_ws, stream));
-    if (first) { tm.end(EC_PHASE_ATTN); tm.begin(EC_PHASE_OPROJ); }
+    if (first) { EC_TRY(tm.end(EC_PHASE_ATTN)); EC_TRY(tm.begin(EC_PHASE_OPROJ)); }
 
     ec::GemmArgs go;
     go.dtype = dt; go.epi = ec::Epi::kResidual; go.A = s.o; go.lda = hd; go.n_rows_dev = st->n_rows;
     go.max_rows = L; go.W = ly.w_o; go.N = m->d; go.K = hd; go.C = s.x; go.ldc = m->d;
     EC_TRY(ec::launch_gemm_rows(go, s.gemm_ws, stream));
-    if (first) tm.end(EC_PHASE_OPROJ);
+    if (first) EC_TRY(tm.end(EC_PHASE_OPROJ));
 
     if (m->d_ffn) {
-      if (first) tm.begin(EC_PHASE_FFN);
+      if (first) EC_TRY(tm.begin(EC_PHASE_FFN));
       EC_TRY(ec::launch_rmsnorm(dt, s.x, st->n_rows, L, m->d, ly.norm_ffn, m->rms_eps, s.a, stream));
       ec::GemmArgs gu;
       gu.dtype = dt; gu.epi = ec::Epi::kSwiGLU; gu.A = s.a; gu.lda = m->d;
@@ -341,11 +346,11 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
       gd.n_rows_dev = st->n_rows; gd.max_rows = L; gd.W = ly.w_down; gd.N = m->d; gd.K = m->d_ffn;
       gd.C = s.x; gd.ldc = m->d;
       EC_TRY(ec::launch_gemm_rows(gd, s.gemm_ws, stream));
-      if (first) tm.end(EC_PHASE_FFN);
+      if (first) EC_TRY(tm.end(EC_PHASE_FFN));
     }
   }
 
-  tm.begin(EC_PHASE_LMHEAD);
+  EC_TRY(tm.begin(EC_PHASE_LMHEAD));
   const void* xf = s.x;
   if (m->d_ffn) {
     EC_TRY(ec::launch_rmsnorm(dt, s.x, st->n_rows, L, m->d, m->norm_final, m->rms_eps, s.a, stream));
@@ -356,19 +361,19 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   gl.n_rows_dev = s.n_cand; gl.max_rows = max_block; gl.W = m->w_lm; gl.N = m->V; gl.K = m->d;
   gl.C = st->logits; gl.ldc = m->V; gl.scale = m->logit_scale; gl.scale_pos = s.cand_pos;
   EC_TRY(ec::launch_gemm_rows(gl, s.gemm_ws, stream));
-  tm.end(EC_PHASE_LMHEAD);
+  EC_TRY(tm.end(EC_PHASE_LMHEAD));
 
-  tm.begin(EC_PHASE_ENTROPY);
+  EC_TRY(tm.begin(EC_PHASE_ENTROPY));
   EC_TRY(ec::launch_entropy(st->logits, dt, max_block, s.n_cand, m->V, m->V, st->row_entropy,
                             st->row_argmax, st->row_top1, nullptr, nullptr, 0, 0.f, nullptr,
                             nullptr, s.ent_ws, stream));
-  tm.end(EC_PHASE_ENTROPY);
-  tm.begin(EC_PHASE_DECIDE);
+  EC_TRY(tm.end(EC_PHASE_ENTROPY));
+  EC_TRY(tm.begin(EC_PHASE_DECIDE));
   EC_TRY(ec::launch_choose_decide(s.cand_pos, s.n_cand, st->row_entropy, st->row_argmax,
                                   st->row_top1, c->n_unmask, c->tau, st->chosen, st->n_chosen,
                                   st->tokens, st->is_masked, st->history, st->history_len,
                                   st->history_cap, st->e_max, st->full_flag, stream));
-  tm.end(EC_PHASE_DECIDE);
+  EC_TRY(tm.end(EC_PHASE_DECIDE));
   return EC_OK;
 }
 

@@ -55,6 +55,7 @@ template <> struct Mma<float> {
 
 // Per-lane vectors per lane-half per iteration: 4 x 16 B = 64 consecutive bytes of k.
 constexpr int kVecs = 4;
+
 template <typename T> constexpr int kit() { return 2 * kVecs * (16 / int(sizeof(T))); }  // k per iteration
 
 struct GP {
@@ -114,198 +115,200 @@ __device__ __forceinline__ void epilogue(const GP& p, int r, int n, float v, flo
 __device__ __forceinline__ int acc_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
 
 // ============================================================================ skinny
-// Floats of one split's partial tile, laid out [element][thread] and sized for
-// four row blocks: element (rb, cb, j) of thread t at ((rb*CB + cb)*16 + j)*256 + t,
-// the second accumulator (DUAL) after 4*CB*16 elements.
-template <int CB, bool DUAL>
-__host__ __device__ constexpr int split_chunk() { return 4 * CB * 16 * (DUAL ? 2 : 1) * kThreads; }
+// MFMA 16x16x32 bf16 / 16x16x4 fp32.  A wave owns 16 weight rows (output
+// columns).  Lane (n = l%16, g = l/16) loads, per iteration, NV vectors of
+// 16 B at k-offset (v*4 + g)*VPL, v = 0..NV-1: the four lanes of a row read
+// 64 contiguous bytes per instruction and the wave walks 512 B of each of its
+// 16 rows per iteration -- the access pattern that keeps HBM streaming at
+// ~5.5 TB/s on this part, where 32 rows x 32 B per instruction reach ~3 TB/s.
+// For bf16 that is exactly the MFMA's own operand layout (k = 32v + 8g + i);
+// for fp32 each 16-B vector feeds four 16x16x4 MFMAs.  W fragments sit in a
+// ring of kRing register buffers (loads run two iterations ahead); the
+// selected rows' activations are staged in LDS per iteration and shared by
+// the four waves.
+template <typename T> struct Mma16;
+template <> struct Mma16<bf16_t> {
+  __device__ static void run(f32x4& acc, const u32x4& a, const u32x4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+};
+template <> struct Mma16<float> {
+  __device__ static void run(f32x4& acc, const u32x4& a, const u32x4& b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[i]), __uint_as_float(b[i]), acc,
+                                                 0, 0, 0);
+  }
+};
 
-template <typename T, int MB, int CB, bool DUAL, int EPI>
+constexpr int kNV = 8;                       // 16-B vectors per lane per iteration
+constexpr int kRing = 3;                     // W register ring depth
+constexpr int kSkinnyNT = 64;                // output columns per workgroup
+template <typename T> constexpr int skit() { return kNV * 4 * (16 / int(sizeof(T))); }  // k per iteration
+
+template <typename T, int MB, bool DUAL, int EPI>
 __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem) {
   constexpr int VPL = 16 / int(sizeof(T));
-  constexpr int KIT = kit<T>();
+  constexpr int KIT = skit<T>();
   constexpr int ROWB = KIT * int(sizeof(T)) + 16;           // LDS row pitch (bytes), padded
-  constexpr int NT = 4 * CB * 32;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
   const int b = blockIdx.x;
   const int split = b % p.S, tile = b / p.S;
   const int k0 = split * p.KS;
-  const int k1 = min(p.K, k0 + p.KS);
-  const int nit = (k1 - k0) / KIT;
-  const int col0 = tile * NT + wave * CB * 32;
-
+  const int nit = p.KS / KIT;                               // K splits evenly (host plan)
+  const int col = tile * kSkinnyNT + wave * 16 + (lane & 15);
   const T* A = static_cast<const T*>(p.A);
-  const T* W = static_cast<const T*>(p.W);
-  const T* W2 = static_cast<const T*>(p.W2);
+  const T* Wp = static_cast<const T*>(p.W) + int64_t(min(col, p.N - 1)) * p.K + k0 + g * VPL;
+  const T* W2p = DUAL ? static_cast<const T*>(p.W2) + int64_t(min(col, p.N - 1)) * p.K + k0 + g * VPL
+                      : nullptr;
 
-  // A staging: MB*32 rows x KIT k per stage; 16 B per thread-load.
-  constexpr int AV = MB * 32 * (KIT / VPL);                  // 16-B vectors per stage
-  constexpr int APT = (AV + kThreads - 1) / kThreads;        // per thread
+  // A staging: MB*16 rows x KIT k per iteration, 16 B per thread-load.  The
+  // rows a thread stages are the same every iteration, so the (possibly
+  // gathered) row pointers are resolved once; rows past n_rows read row 0
+  // (finite data whose products land only in outputs that are never stored).
+  // Every load in the loop is unconditional, so the compiler can keep the W
+  // ring in flight with precise vmcnt waits.
+  constexpr int AV = MB * 16 * (KIT / VPL);
+  constexpr int APT = AV / kThreads;
+  static_assert(AV % kThreads == 0, "A stage must split evenly over the workgroup");
+  const T* arow[APT];
+#pragma unroll
+  for (int i = 0; i < APT; ++i) {
+    const int v = tid + i * kThreads;
+    const int r = v / (KIT / VPL), c = v % (KIT / VPL);
+    const int ar = (r < n_rows) ? ((p.a_idx != nullptr) ? p.a_idx[r] : r) : 0;
+    arow[i] = A + int64_t(ar) * p.lda + k0 + c * VPL;
+  }
   u32x4 areg[APT];
   auto a_load = [&](int it) {
+#pragma unroll
+    for (int i = 0; i < APT; ++i) areg[i] = *reinterpret_cast<const u32x4*>(arow[i] + it * KIT);
+  };
+  auto a_store = [&]() {
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       const int v = tid + i * kThreads;
       const int r = v / (KIT / VPL), c = v % (KIT / VPL);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (v < AV && r < n_rows) {
-        const int ar = (p.a_idx != nullptr) ? p.a_idx[r] : r;
-        x = *reinterpret_cast<const u32x4*>(A + int64_t(ar) * p.lda + k0 + it * KIT + c * VPL);
-      }
-      areg[i] = x;
+      *reinterpret_cast<u32x4*>(smem + r * ROWB + c * 16) = areg[i];
     }
   };
-  auto a_store = [&](int buf) {
-    char* base = smem + buf * (MB * 32 * ROWB);
+  typedef u32x4 WBuf[kNV];
+  auto w_load = [&](WBuf& dst, const T* src, int it) {
 #pragma unroll
-    for (int i = 0; i < APT; ++i) {
-      const int v = tid + i * kThreads;
-      if (v < AV) {
-        const int r = v / (KIT / VPL), c = v % (KIT / VPL);
-        *reinterpret_cast<u32x4*>(base + r * ROWB + c * 16) = areg[i];
-      }
-    }
+    for (int v = 0; v < kNV; ++v)
+      dst[v] = *reinterpret_cast<const u32x4*>(src + it * KIT + v * 4 * VPL);
   };
 
-  // W fragments: per column block, kVecs consecutive 16-B vectors of row n.
-  u32x4 wcur[CB][kVecs], wnext[CB][kVecs];
-  u32x4 w2cur[DUAL ? CB : 1][kVecs], w2next[DUAL ? CB : 1][kVecs];
-  auto w_load = [&](u32x4 (&dst)[CB][kVecs], const T* Wm, int it) {
+  f32x4 acc[MB], acc2[DUAL ? MB : 1];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int n = col0 + cb * 32 + (lane & 31);
-      const T* src = Wm + int64_t(min(n, p.N - 1)) * p.K + k0 + it * KIT + h * kVecs * VPL;
-#pragma unroll
-      for (int v = 0; v < kVecs; ++v) dst[cb][v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + v);
-    }
-  };
-
-  f32x16 acc[MB][CB], acc2[DUAL ? MB : 1][DUAL ? CB : 1];
-#pragma unroll
-  for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      acc[rb][cb] = f32x16{};
-      if constexpr (DUAL) acc2[rb][cb] = f32x16{};
-    }
-
-  if (nit > 0) {
-    a_load(0);
-    w_load(wcur, W, 0);
-    if constexpr (DUAL) w_load(w2cur, W2, 0);
-    a_store(0);
+  for (int rb = 0; rb < MB; ++rb) {
+    acc[rb] = f32x4{};
+    if constexpr (DUAL) acc2[rb] = f32x4{};
   }
-  __syncthreads();
-  for (int it = 0; it < nit; ++it) {
-    const bool more = (it + 1 < nit);
-    if (more) {
-      a_load(it + 1);
-      w_load(wnext, W, it + 1);
-      if constexpr (DUAL) w_load(w2next, W2, it + 1);
-    }
-    const char* base = smem + (it & 1) * (MB * 32 * ROWB);
+  WBuf r0, r1, r2, q0, q1, q2;   // W ring (q: second matrix of a SwiGLU)
+
+  // one iteration: stage A(it+1), prefetch W(it+2) into `nxt`, multiply with `cur`
+  auto step = [&](WBuf& cur, WBuf& nxt, WBuf& cur2, WBuf& nxt2, int it) {
+    const int last = nit - 1;
+    a_load(min(it + 1, last));                  // before the W prefetch (vmcnt is in order)
+    w_load(nxt, Wp, min(it + 2, last));
+    if constexpr (DUAL) w_load(nxt2, W2p, min(it + 2, last));
 #pragma unroll
-    for (int v = 0; v < kVecs; ++v) {
+    for (int v = 0; v < kNV; ++v) {
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(base + (rb * 32 + (lane & 31)) * ROWB +
-                                                        (h * kVecs + v) * 16);
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          Mma<T>::run(acc[rb][cb], a, wcur[cb][v]);
-          if constexpr (DUAL) Mma<T>::run(acc2[rb][cb], a, w2cur[cb][v]);
-        }
+        const u32x4 a = *reinterpret_cast<const u32x4*>(smem + (rb * 16 + (lane & 15)) * ROWB +
+                                                        (v * 4 + g) * 16);
+        Mma16<T>::run(acc[rb], a, cur[v]);
+        if constexpr (DUAL) Mma16<T>::run(acc2[rb], a, cur2[v]);
       }
     }
-    if (more) {
-      a_store((it + 1) & 1);
+    __syncthreads();                            // every wave is done with this stage
+    a_store();
+    __syncthreads();
+  };
+
+  w_load(r0, Wp, 0);
+  if constexpr (DUAL) w_load(q0, W2p, 0);
+  w_load(r1, Wp, min(1, nit - 1));
+  if constexpr (DUAL) w_load(q1, W2p, min(1, nit - 1));
+  a_load(0);
+  a_store();
+  __syncthreads();
+  int it = 0;
+  for (; it + 3 <= nit; it += 3) {
+    step(r0, r2, q0, q2, it);
+    step(r1, r0, q1, q0, it + 1);
+    step(r2, r1, q2, q1, it + 2);
+  }
+  if (it < nit) step(r0, r2, q0, q2, it);
+  if (it + 1 < nit) step(r1, r0, q1, q0, it + 1);
+
+  // 16x16 accumulator element j of lane l: row 4*(l/16) + j, column l%16.
+  if (p.S > 1) {
+    // split-K: this split's partial sums go to part[split][row][col] (fp32; the
+    // up-projection of a SwiGLU in a second plane); gemm_splitk_epilogue sums
+    // the splits in order and runs the epilogue (no cross-workgroup fence).
+    const int64_t plane = int64_t(kSkinnyMaxRows) * p.N;
+    if (col < p.N) {
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+      for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-        for (int v = 0; v < kVecs; ++v) {
-          wcur[cb][v] = wnext[cb][v];
-          if constexpr (DUAL) w2cur[cb][v] = w2next[cb][v];
+        for (int j = 0; j < 4; ++j) {
+          const int r = rb * 16 + 4 * g + j;
+          if (r >= n_rows) continue;
+          float* dst = p.part + int64_t(split) * plane * (DUAL ? 2 : 1) + int64_t(r) * p.N + col;
+          dst[0] = acc[rb][j];
+          if constexpr (DUAL) dst[plane] = acc2[rb][j];
         }
     }
-    __syncthreads();
+    return;
   }
-
-  // ---- split-K: publish this split's partial tile; gemm_splitk_epilogue sums
-  // the splits in order and runs the epilogue (no cross-workgroup fence).
-  if (p.S > 1) {
-    float* mine = p.part + (int64_t(tile) * p.S + split) * split_chunk<CB, DUAL>();
+  if (col < p.N) {
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          mine[((rb * CB + cb) * 16 + j) * kThreads + tid] = acc[rb][cb][j];
-          if constexpr (DUAL)
-            mine[((4 * CB) * 16 + (rb * CB + cb) * 16 + j) * kThreads + tid] = acc2[rb][cb][j];
-        }
-    return;
-  }
-
-  // ---- epilogue
-#pragma unroll
-  for (int rb = 0; rb < MB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int n = col0 + cb * 32 + (lane & 31);
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int r = rb * 32 + acc_row(j, lane);
-        if (r < n_rows) epilogue<T, EPI>(p, r, n, acc[rb][cb][j], DUAL ? acc2[DUAL ? rb : 0][DUAL ? cb : 0][j] : 0.f);
+      for (int j = 0; j < 4; ++j) {
+        const int r = rb * 16 + 4 * g + j;
+        if (r < n_rows) epilogue<T, EPI>(p, r, col, acc[rb][j], DUAL ? acc2[DUAL ? rb : 0][j] : 0.f);
       }
-    }
+  }
 }
 
-// MBX: largest row-block count this launch can see (from max_rows on the host);
-// the kernel picks the body for the device row count.
-template <typename T, int MBX, int CB, bool DUAL, int EPI>
+// MBX: largest count of 16-row blocks this launch can see (2 when max_rows <= 32,
+// else 8); the kernel picks the body for the device row count.
+template <typename T, int MBX, bool DUAL, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(GP p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int n_rows = min(*p.n_rows, p.max_rows);
   if (n_rows <= 0 || n_rows > kSkinnyMaxRows) return;
-  const int mb = (n_rows + 31) / 32;
-  if (mb == 1 || MBX == 1) skinny_body<T, 1, CB, DUAL, EPI>(p, n_rows, smem);
-  else if constexpr (MBX >= 2) {
-    if (mb == 2 || MBX == 2) skinny_body<T, 2, CB, DUAL, EPI>(p, n_rows, smem);
-    else if constexpr (MBX >= 3) {
-      if (mb == 3 || MBX == 3) skinny_body<T, 3, CB, DUAL, EPI>(p, n_rows, smem);
-      else if constexpr (MBX >= 4) skinny_body<T, 4, CB, DUAL, EPI>(p, n_rows, smem);
-    }
+  const int mb = (n_rows + 15) / 16;
+  if (MBX == 2 || mb <= 2) skinny_body<T, 2, DUAL, EPI>(p, n_rows, smem);
+  else if constexpr (MBX == 8) {
+    if (mb <= 4) skinny_body<T, 4, DUAL, EPI>(p, n_rows, smem);
+    else if (mb <= 6) skinny_body<T, 6, DUAL, EPI>(p, n_rows, smem);
+    else skinny_body<T, 8, DUAL, EPI>(p, n_rows, smem);
   }
 }
 
-// Sum the S partial tiles of each column tile in split order, then epilogue.
-template <typename T, int CB, bool DUAL, int EPI>
+// Sum the S partial planes in split order, then the epilogue: one thread per
+// output element (r, n), reads coalesced along n.
+template <typename T, bool DUAL, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_splitk_epilogue(GP p) {
   const int n_rows = min(*p.n_rows, p.max_rows);
   if (n_rows <= 0 || n_rows > kSkinnyMaxRows) return;
-  const int mb = (n_rows + 31) / 32;
-  const int tile = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NT = 4 * CB * 32;
-  const float* base = p.part + int64_t(tile) * p.S * split_chunk<CB, DUAL>();
-  for (int rb = 0; rb < mb; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int n = tile * NT + wave * CB * 32 + cb * 32 + (lane & 31);
-#pragma unroll 4
-      for (int j = 0; j < 16; ++j) {
-        const int r = rb * 32 + acc_row(j, lane);
-        const int e = ((rb * CB + cb) * 16 + j) * kThreads + tid;
-        float v = 0.f, v2 = 0.f;
-        for (int s = 0; s < p.S; ++s) {
-          v += base[int64_t(s) * split_chunk<CB, DUAL>() + e];
-          if constexpr (DUAL) v2 += base[int64_t(s) * split_chunk<CB, DUAL>() + (4 * CB) * 16 * kThreads + e];
-        }
-        if (r < n_rows && n < p.N) epilogue<T, EPI>(p, r, n, v, v2);
-      }
-    }
+  const int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int r = int(idx / p.N), n = int(idx - int64_t(r) * p.N);
+  if (r >= n_rows) return;
+  const int64_t plane = int64_t(kSkinnyMaxRows) * p.N;
+  const float* src = p.part + int64_t(r) * p.N + n;
+  float v = 0.f, v2 = 0.f;
+  for (int s = 0; s < p.S; ++s) {
+    v += src[int64_t(s) * plane * (DUAL ? 2 : 1)];
+    if constexpr (DUAL) v2 += src[int64_t(s) * plane * 2 + plane];
+  }
+  epilogue<T, EPI>(p, r, n, v, v2);
 }
 
 // ============================================================================ tiled
@@ -342,18 +345,23 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(GP p) {
   constexpr int STAGE = TILEB * (1 + NB);
   constexpr int VPT = kBM * (KIT / VPL) / kThreads;      // 16-B vectors per thread per tile (4)
   u32x4 ra[VPT], rw[NB][VPT];
+  const T* arow[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int v = tid + i * kThreads;
+    const int r = v / (KIT / VPL), c = v % (KIT / VPL);
+    const int gr = row0 + r;
+    arow[i] = nullptr;
+    if (gr < n_rows) arow[i] = A + int64_t((p.a_idx != nullptr) ? p.a_idx[gr] : gr) * p.lda + c * VPL;
+  }
   auto g_load = [&](int it) {
     const int kb = it * KIT;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int v = tid + i * kThreads;
       const int r = v / (KIT / VPL), c = v % (KIT / VPL);
-      const int gr = row0 + r;
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (gr < n_rows) {
-        const int ar = (p.a_idx != nullptr) ? p.a_idx[gr] : gr;
-        x = *reinterpret_cast<const u32x4*>(A + int64_t(ar) * p.lda + kb + c * VPL);
-      }
+      if (arow[i] != nullptr) x = *reinterpret_cast<const u32x4*>(arow[i] + kb);
       ra[i] = x;
 #pragma unroll
       for (int w = 0; w < NB; ++w) {
@@ -429,10 +437,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(GP p) {
 }
 
 // ---------------------------------------------------------------------------- planning
-int mbx_of(int max_rows) { return max_rows >= kSkinnyMaxRows ? 4 : (max_rows + 31) / 32; }
+int mbx_of(int max_rows) { return max_rows <= 32 ? 2 : 8; }
 
 struct Plan {
-  int MBX, CB, S, KS, tiles;
+  int MBX, S, KS, tiles;
   size_t part_floats;
 };
 
@@ -441,42 +449,30 @@ Plan plan_skinny(const GemmArgs& a) {
   Plan pl;
   const bool dual = (a.epi == Epi::kSwiGLU);
   pl.MBX = mbx_of(a.max_rows);
-  pl.CB = (dual || a.N <= 1024 || pl.MBX > 2) ? 1 : 2;
-  const int NT = 4 * pl.CB * 32;
-  pl.tiles = (a.N + NT - 1) / NT;
-  const int KIT = kit<T>();
-  const int iters = a.K / KIT;
+  pl.tiles = (a.N + kSkinnyNT - 1) / kSkinnyNT;
+  const int KIT = skit<T>();
+  const int iters = (a.K + KIT - 1) / KIT;
   int S = 1;
-  // split K only when the column tiles alone leave most CUs idle, and never for
-  // the QKV scatter called without a workspace
-  while (pl.tiles * S < 256 && S * 2 <= 16 && iters % (S * 2) == 0 && iters / (S * 2) >= 2) S *= 2;
+  // split K (into equal whole iterations) only when the column tiles alone
+  // leave most CUs idle
+  while (pl.tiles * S < 2 * 256 && S * 2 <= 16 && iters % (S * 2) == 0 && iters / (S * 2) >= 2) S *= 2;
   pl.S = S;
   pl.KS = (iters / S) * KIT;
-  const int CHUNK = 4 * pl.CB * 16 * (dual ? 2 : 1) * kThreads;
-  pl.part_floats = (S > 1) ? size_t(pl.tiles) * S * CHUNK : 0;
+  pl.part_floats = (S > 1) ? size_t(S) * kSkinnyMaxRows * a.N * (dual ? 2 : 1) : 0;
   return pl;
 }
 
 size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
 
-template <typename T, int MBX, int CB, bool DUAL, int EPI>
+template <typename T, int MBX, bool DUAL, int EPI>
 void go_skinny(dim3 g, size_t lds, hipStream_t s, const GP& p) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, MBX, CB, DUAL, EPI>), g, dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, MBX, DUAL, EPI>), g, dim3(kThreads), lds, s, p);
 }
 
-template <typename T, int EPI>
+template <typename T, int EPI, bool DUAL = false>
 void skinny_by_shape(const Plan& pl, dim3 g, size_t lds, hipStream_t s, const GP& p) {
-  if (pl.CB == 2) {                       // CB = 2 only with MBX <= 2
-    if (pl.MBX == 1) go_skinny<T, 1, 2, false, EPI>(g, lds, s, p);
-    else go_skinny<T, 2, 2, false, EPI>(g, lds, s, p);
-  } else {
-    switch (pl.MBX) {
-      case 1: go_skinny<T, 1, 1, false, EPI>(g, lds, s, p); break;
-      case 2: go_skinny<T, 2, 1, false, EPI>(g, lds, s, p); break;
-      case 3: go_skinny<T, 3, 1, false, EPI>(g, lds, s, p); break;
-      default: go_skinny<T, 4, 1, false, EPI>(g, lds, s, p); break;
-    }
-  }
+  if (pl.MBX == 2) go_skinny<T, 2, DUAL, EPI>(g, lds, s, p);
+  else go_skinny<T, 8, DUAL, EPI>(g, lds, s, p);
 }
 
 template <typename T>
@@ -485,42 +481,20 @@ hipError_t dispatch_skinny(Epi epi, const Plan& pl, dim3 g, size_t lds, hipStrea
     case Epi::kStore: skinny_by_shape<T, 0>(pl, g, lds, s, p); break;
     case Epi::kQKV: skinny_by_shape<T, 1>(pl, g, lds, s, p); break;
     case Epi::kResidual: skinny_by_shape<T, 2>(pl, g, lds, s, p); break;
+    case Epi::kSwiGLU: skinny_by_shape<T, 3, true>(pl, g, lds, s, p); break;
     case Epi::kLogits: skinny_by_shape<T, 4>(pl, g, lds, s, p); break;
-    case Epi::kSwiGLU:
-      switch (pl.MBX) {
-        case 1: go_skinny<T, 1, 1, true, 3>(g, lds, s, p); break;
-        case 2: go_skinny<T, 2, 1, true, 3>(g, lds, s, p); break;
-        case 3: go_skinny<T, 3, 1, true, 3>(g, lds, s, p); break;
-        default: go_skinny<T, 4, 1, true, 3>(g, lds, s, p); break;
-      }
-      break;
   }
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch_split_epi(Epi epi, const Plan& pl, dim3 g, hipStream_t s, const GP& p) {
-  const bool cb2 = (pl.CB == 2);
+hipError_t dispatch_split_epi(Epi epi, dim3 g, hipStream_t s, const GP& p) {
   switch (epi) {
-    case Epi::kStore:
-      if (cb2) hipLaunchKernelGGL((gemm_splitk_epilogue<T, 2, false, 0>), g, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((gemm_splitk_epilogue<T, 1, false, 0>), g, dim3(kThreads), 0, s, p);
-      break;
-    case Epi::kQKV:
-      if (cb2) hipLaunchKernelGGL((gemm_splitk_epilogue<T, 2, false, 1>), g, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((gemm_splitk_epilogue<T, 1, false, 1>), g, dim3(kThreads), 0, s, p);
-      break;
-    case Epi::kResidual:
-      if (cb2) hipLaunchKernelGGL((gemm_splitk_epilogue<T, 2, false, 2>), g, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((gemm_splitk_epilogue<T, 1, false, 2>), g, dim3(kThreads), 0, s, p);
-      break;
-    case Epi::kSwiGLU:
-      hipLaunchKernelGGL((gemm_splitk_epilogue<T, 1, true, 3>), g, dim3(kThreads), 0, s, p);
-      break;
-    case Epi::kLogits:
-      if (cb2) hipLaunchKernelGGL((gemm_splitk_epilogue<T, 2, false, 4>), g, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((gemm_splitk_epilogue<T, 1, false, 4>), g, dim3(kThreads), 0, s, p);
-      break;
+    case Epi::kStore: hipLaunchKernelGGL((gemm_splitk_epilogue<T, false, 0>), g, dim3(kThreads), 0, s, p); break;
+    case Epi::kQKV: hipLaunchKernelGGL((gemm_splitk_epilogue<T, false, 1>), g, dim3(kThreads), 0, s, p); break;
+    case Epi::kResidual: hipLaunchKernelGGL((gemm_splitk_epilogue<T, false, 2>), g, dim3(kThreads), 0, s, p); break;
+    case Epi::kSwiGLU: hipLaunchKernelGGL((gemm_splitk_epilogue<T, true, 3>), g, dim3(kThreads), 0, s, p); break;
+    case Epi::kLogits: hipLaunchKernelGGL((gemm_splitk_epilogue<T, false, 4>), g, dim3(kThreads), 0, s, p); break;
   }
   return hipGetLastError();
 }
@@ -540,12 +514,13 @@ hipError_t launch_typed(const GemmArgs& a, void* ws, hipStream_t s, bool allow_s
   if (!allow_split || ws == nullptr) { pl.S = 1; pl.KS = a.K; }
   p.S = pl.S; p.KS = pl.KS;
   p.part = static_cast<float*>(ws);
-  const size_t lds_sk = size_t(2) * pl.MBX * 32 * ROWB;
+  const size_t lds_sk = size_t(pl.MBX) * 16 * (skit<T>() * sizeof(T) + 16);
   const dim3 g_sk(unsigned(pl.tiles * pl.S));
   hipError_t e = dispatch_skinny<T>(a.epi, pl, g_sk, lds_sk, s, p);
   if (e != hipSuccess) return e;
   if (pl.S > 1) {
-    e = dispatch_split_epi<T>(a.epi, pl, dim3(unsigned(pl.tiles)), s, p);
+    const int64_t outs = int64_t(min(a.max_rows, kSkinnyMaxRows)) * a.N;
+    e = dispatch_split_epi<T>(a.epi, dim3(unsigned((outs + kThreads - 1) / kThreads)), s, p);
     if (e != hipSuccess) return e;
   }
   if (a.max_rows <= kSkinnyMaxRows) return hipSuccess;
@@ -565,6 +540,8 @@ hipError_t launch_typed(const GemmArgs& a, void* ws, hipStream_t s, bool allow_s
 
 }  // namespace
 
+int gemm_k_multiple(int dtype) { return dtype == 1 ? skit<bf16_t>() : skit<float>(); }
+
 size_t gemm_ws_bytes(const GemmArgs& a) {
   if (a.epi == Epi::kQKV && a.N == 0) return 0;
   Plan pl = (a.dtype == 1) ? plan_skinny<bf16_t>(a) : plan_skinny<float>(a);
@@ -573,8 +550,7 @@ size_t gemm_ws_bytes(const GemmArgs& a) {
 }
 
 hipError_t launch_gemm_rows(const GemmArgs& a, void* ws, hipStream_t s) {
-  if (a.N % 32 != 0 || a.K % kit<float>() != 0 || (a.dtype == 1 && a.K % kit<bf16_t>() != 0))
-    return hipErrorNotSupported;
+  if (a.N % 32 != 0 || a.K % gemm_k_multiple(a.dtype) != 0) return hipErrorNotSupported;
   return (a.dtype == 1) ? launch_typed<bf16_t>(a, ws, s, true) : launch_typed<float>(a, ws, s, true);
 }
 

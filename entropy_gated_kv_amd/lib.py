@@ -187,7 +187,12 @@ def ec_step(model: ec_model, state: ec_state, cfg: ec_step_cfg, ws, phase_events
             stream=None) -> None:
     ev = None
     if phase_events is not None:
-        arr = (C.c_void_p * len(phase_events))(*[e.cuda_event for e in phase_events])
+        handles = []
+        for e in phase_events:
+            if not e.cuda_event:          # torch creates events on first record
+                e.record()
+            handles.append(e.cuda_event)
+        arr = (C.c_void_p * len(handles))(*handles)
         ev = C.cast(arr, C.c_void_p)
     _check("ec_step", load().ec_step(C.byref(model), C.byref(state), C.byref(cfg), _ptr(ws),
                                      ws.numel() * ws.element_size(), ev, _stream(stream)))

@@ -148,7 +148,8 @@ int32_t ec_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32
  * outputs are rounded to dtype (nearest even).  rows[r] < L_cap, distinct.
  * ws holds split-K partial sums: ec_kv_refresh_workspace_bytes(...) bytes
  * (may be 0, then ws may be NULL).
- * Supported: d % 64 == 0, dh in {32, 64, 128}, Hq % Hkv == 0.
+ * Supported: d a multiple of 256 (bf16) or 128 (fp32), dh in {32, 64, 128},
+ * Hq % Hkv == 0.
  * Errors: EC_E_NULL, EC_E_SHAPE, EC_E_DTYPE, EC_E_ALIGN, EC_E_WORKSPACE,
  * EC_E_UNSUPPORTED, EC_E_LAUNCH.
  * ------------------------------------------------------------------------ */
@@ -211,7 +212,9 @@ int32_t ec_bidir_attention(const void* q, const int32_t* n_rows, int32_t max_row
  * The first step of a sequence must run with *full_flag = 1 (no cache yet).
  * ws (ec_step_workspace_bytes(model, max_block) bytes) must be zero-filled
  * before its first use; steps leave its counters zeroed.
- * Norms and FFN are present iff d_ffn > 0.  The block (block_start,
+ * Norms and FFN are present iff d_ffn > 0.  d, Hq*dh and d_ffn must be
+ * multiples of 256 (bf16) or 128 (fp32) (EC_E_UNSUPPORTED otherwise); block_len
+ * is at most 1024.  The block (block_start,
  * block_len) and n_unmask are host values: the schedule is fixed on the host.
  * ------------------------------------------------------------------------ */
 typedef struct ec_layer {
@@ -266,8 +269,10 @@ typedef struct ec_step_cfg {
   int32_t block_len;          /* <= max_block of the workspace             */
 } ec_step_cfg;
 
-/* Optional per-phase timing: when non-NULL, ec_step records events[2*i] and
- * events[2*i+1] around phase i on the stream (phases: see EC_PHASE_*). */
+/* Optional per-phase timing: when non-NULL, phase_events holds 2*EC_PHASE_COUNT
+ * created events and ec_step records events[2*i] and events[2*i+1] around
+ * phase i on the stream.  Per-layer phases (QKV, attention, O-projection, FFN)
+ * are bracketed in the first layer only.  A NULL handle is EC_E_NULL. */
 enum {
   EC_PHASE_SELECT = 0, EC_PHASE_EMBED, EC_PHASE_QKV, EC_PHASE_ATTN, EC_PHASE_OPROJ,
   EC_PHASE_FFN, EC_PHASE_LMHEAD, EC_PHASE_ENTROPY, EC_PHASE_DECIDE, EC_PHASE_COUNT

@@ -48,7 +48,7 @@ def gpu_single_cfg():
 def gpu_stack_cfg():
     return C.scaled(C.LLADA_STACK, name="stack_gpu", model_n_layers=2, model_d=256,
                     model_n_q_heads=4, model_n_kv_heads=2, model_head_dim=64, model_vocab=2048,
-                    model_d_ffn=384, prompt_len=96, gen_len=64, block_len=32, k=16)
+                    model_d_ffn=512, prompt_len=96, gen_len=64, block_len=32, k=16)
 
 
 def setup(cfg, dtype=None):
