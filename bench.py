@@ -231,8 +231,19 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         if name == "ffn":
             continue
         phase_ms[name] = float(np.mean([ev[2 * k].elapsed_time(ev[2 * k + 1]) for ev in bd_events]))
-    d, V, m = cfg.model.d, cfg.model.vocab, cfg.block_len
-    lm_bytes = V * d * 2 + m * d * 2 + m * V * 2
+    # LM-head algorithmic bytes per launch: W_lm read once, the candidates'
+    # activations read and their logits written (mean candidate count over the
+    # timed steps: the block's still-masked positions at each step)
+    d, V = cfg.model.d, cfg.model.vocab
+    cand = []
+    left, cur = cfg.block_len, None
+    for bs, bl, nn in sched:
+        if bs != cur:
+            cur, left = bs, bl
+        cand.append(left)
+        left -= nn
+    m = float(np.mean([cand[i % len(sched)] for i in range(steps)]))
+    lm_bytes = int(V * d * 2 + m * d * 2 + m * V * 2)
     lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
     decide_ms = phase_ms["select"] + phase_ms["entropy"] + phase_ms["decide"]
     out = {
@@ -292,6 +303,52 @@ def step_cpu_baseline(cfg, w, toks, masked, sched, tau) -> dict:
                       f"NumPy float64, {dt:.1f} s"}
 
 
+# --------------------------------------------------------------------------- profiling
+def profile_mode() -> int:
+    """A short, fixed sequence for hardware-counter runs (rocprofv3 --pmc):
+    a 1 GiB device copy (the calibration of FETCH_SIZE / WRITE_SIZE), five
+    entropy passes over the 4096 x 126464 logits, and one block (22 steps) of
+    the LLaDA-shaped EntropyCache loop."""
+    import torch
+
+    from entropy_gated_kv_amd import lib as L
+    from entropy_gated_kv_amd.runner import DeviceModel, DeviceSequence
+    from synth import configs as C
+    from synth import generators as G
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    _log("calibration copies done (1 GiB each)")
+    cfg = C.ENTROPY_ONLY
+    x = torch.from_numpy(G.entropy_logits(cfg)).to(torch.bfloat16).cuda()
+    n, V = x.shape
+    H = torch.empty(n, device="cuda")
+    E = torch.empty(1, device="cuda")
+    F = torch.empty(1, device="cuda", dtype=torch.int32)
+    ws = torch.zeros(L.ec_entropy_workspace_bytes(n, V), device="cuda", dtype=torch.uint8)
+    for _ in range(5):
+        L.ec_entropy_max(x, cfg.tau, H, E, F, ws)
+    torch.cuda.synchronize()
+    del x
+    _log("entropy passes done")
+    sc = C.LLADA_LAYER
+    w = G.model_weights(sc)
+    toks, masked = G.initial_sequence(sc)
+    dm = DeviceModel(sc.model, sc.dtype, sc.L, w)
+    ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len)
+    for bs, bl, nn in C.unmask_schedule(sc)[:22]:
+        ds.step(1.0, sc.k, bs, bl, nn)
+    torch.cuda.synchronize()
+    _log("22 steps done")
+    return 0
+
+
 # --------------------------------------------------------------------------- main
 def main() -> int:
     ap = argparse.ArgumentParser()
@@ -300,6 +357,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=22)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-entropy", action="store_true")
+    ap.add_argument("--profile-mode", action="store_true",
+                    help="run the fixed short sequence used for hardware-counter runs")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -309,6 +368,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.profile_mode:
+        return profile_mode()
     res = step_leg(args.steps, args.warmup, not args.no_cpu_baseline)
     line = {
         "metric": METRIC,
