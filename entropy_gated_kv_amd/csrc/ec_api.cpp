@@ -41,6 +41,16 @@ bool head_dim_ok(int32_t dh) { return dh == 32 || dh == 64 || dh == 128; }
 
 }  // namespace
 
+namespace {
+ec::GemmArgs qkv_args(int32_t max_rows, int32_t d, int32_t Hq, int32_t Hkv, int32_t dh,
+                      int32_t dtype) {
+  ec::GemmArgs g;
+  g.dtype = dtype; g.epi = ec::Epi::kQKV; g.max_rows = max_rows; g.N = (Hq + 2 * Hkv) * dh;
+  g.K = d; g.Hq = Hq; g.Hkv = Hkv; g.dh = dh;
+  return g;
+}
+}  // namespace
+
 extern "C" {
 
 const char* ec_status_string(int32_t s) {
@@ -102,15 +112,6 @@ int32_t ec_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32
 }
 
 // ------------------------------------------------------------------ KV refresh
-namespace {
-ec::GemmArgs qkv_args(int32_t max_rows, int32_t d, int32_t Hq, int32_t Hkv, int32_t dh,
-                      int32_t dtype) {
-  ec::GemmArgs g;
-  g.dtype = dtype; g.epi = ec::Epi::kQKV; g.max_rows = max_rows; g.N = (Hq + 2 * Hkv) * dh;
-  g.K = d; g.Hq = Hq; g.Hkv = Hkv; g.dh = dh;
-  return g;
-}
-}  // namespace
 
 size_t ec_kv_refresh_workspace_bytes(int32_t max_rows, int32_t d, int32_t Hq, int32_t Hkv,
                                      int32_t dh, int32_t dtype) {

@@ -71,14 +71,15 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   v += __int_as_float(dpp_i<0x143, 0xc>(0, x)); x = __float_as_int(v);  // row_bcast:31
   return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
+// NaN-propagating maximum (v_maximum_f32: no input canonicalisation).
 __device__ __forceinline__ float wave_max_dpp(float v) {
   int x = __float_as_int(v);
-  v = fmaxf(v, __int_as_float(dpp_i<0xB1, 0xf>(x, x))); x = __float_as_int(v);
-  v = fmaxf(v, __int_as_float(dpp_i<0x4E, 0xf>(x, x))); x = __float_as_int(v);
-  v = fmaxf(v, __int_as_float(dpp_i<0x141, 0xf>(x, x))); x = __float_as_int(v);
-  v = fmaxf(v, __int_as_float(dpp_i<0x140, 0xf>(x, x))); x = __float_as_int(v);
-  v = fmaxf(v, __int_as_float(dpp_i<0x142, 0xa>(x, x))); x = __float_as_int(v);
-  v = fmaxf(v, __int_as_float(dpp_i<0x143, 0xc>(x, x))); x = __float_as_int(v);
+  v = __builtin_elementwise_maximum(v, __int_as_float(dpp_i<0xB1, 0xf>(x, x))); x = __float_as_int(v);
+  v = __builtin_elementwise_maximum(v, __int_as_float(dpp_i<0x4E, 0xf>(x, x))); x = __float_as_int(v);
+  v = __builtin_elementwise_maximum(v, __int_as_float(dpp_i<0x141, 0xf>(x, x))); x = __float_as_int(v);
+  v = __builtin_elementwise_maximum(v, __int_as_float(dpp_i<0x140, 0xf>(x, x))); x = __float_as_int(v);
+  v = __builtin_elementwise_maximum(v, __int_as_float(dpp_i<0x142, 0xa>(x, x))); x = __float_as_int(v);
+  v = __builtin_elementwise_maximum(v, __int_as_float(dpp_i<0x143, 0xc>(x, x))); x = __float_as_int(v);
   return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 __device__ __forceinline__ int wave_min_i_dpp(int v) {

@@ -14,18 +14,19 @@
 //
 // Work decomposition (a function of V only, so every per-row result is a
 // fixed function of that row's logits, whatever the batch):
-//   * a row is cut into segments of 2048 16-byte vectors (16384 bf16 or 8192
-//     fp32 elements);
-//   * within a segment, thread t of 256 owns the 16-byte vectors t, t+256, ...
-//     (8 per thread in a full segment);
-//   * the segment maximum M is reduced first (DPP within each wave, then the
-//     four waves), so every thread accumulates against the exact M with no
-//     rescaling: one fma, one v_exp_f32, one add and one fma per element;
-//   * z and s2 are summed in a fixed DPP tree, then over the waves in order;
-//   * segments of a row are folded left to right by the combine kernel.
-// Kernel 1 is persistent: each workgroup walks (row, segment) units with a
-// stride of the grid size and prefetches the next unit's vectors into
-// registers while it reduces the current one, so HBM reads stay in flight.
+//   * a row is cut into segments of 512 16-byte vectors (4096 bf16 or 2048
+//     fp32 elements), one wave per segment, four independent waves per
+//     workgroup;
+//   * lane l owns the vectors l, l+64, ..., (8 in a full segment), all loaded
+//     before any arithmetic, so a wave keeps 8 KB in flight and the many
+//     resident waves hide HBM latency (no software prefetch, no LDS, no
+//     barrier);
+//   * the segment maximum M is reduced first (DPP), so every lane accumulates
+//     against the exact M with no rescaling: one fma, one v_exp_f32, one add
+//     and one fma per element;
+//   * z and s2 are summed in a fixed DPP tree;
+//   * the combine kernel folds the segments of a row, one wave per row, in a
+//     fixed order.
 // No device-scope fence is used anywhere (on this multi-XCD part a
 // device-scope release writes back the XCD's L2); the combine runs as a
 // second, small kernel.
@@ -44,9 +45,8 @@ namespace ec {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 constexpr int32_t kNoIdx = 0x7fffffff;
+constexpr int32_t kRedo = -1;     // partial marker: the combine recomputes this segment exactly
 
 __device__ __forceinline__ EntropyPartial merge(const EntropyPartial& a, const EntropyPartial& b) {
   EntropyPartial r;
@@ -100,67 +100,43 @@ template <typename T> struct VecOf;
 template <> struct VecOf<float> { typedef f32x4 type; };
 template <> struct VecOf<bf16_t> { typedef u32x4 type; };
 
-constexpr int kVPT = 8;   // vectors per thread in a full segment
+constexpr int kVPT = 8;   // 16-byte vectors per lane in a full segment
 
-constexpr int64_t seg_elems(int per_vec) { return int64_t(kVPT) * kThreads * per_vec; }
+constexpr int64_t seg_elems(int per_vec) { return int64_t(kVPT) * kWave * per_vec; }
 
-template <typename T>
-struct Unit {
-  typename VecOf<T>::type v[kVPT];
-};
-
-struct UnitGeom {
-  int64_t row, e0, e1, nvec;   // nvec: full 16-byte vectors in [e0, e1)
-};
-
-template <typename T>
-__device__ __forceinline__ UnitGeom geom(int64_t u, int P, int64_t V) {
-  constexpr int E = Elem<T>::kPerVec;
-  UnitGeom g;
-  g.row = u / P;
-  const int seg = int(u - g.row * P);
-  g.e0 = int64_t(seg) * seg_elems(E);
-  g.e1 = min(V, g.e0 + seg_elems(E));
-  g.nvec = (g.e1 - g.e0) / E;
-  return g;
+// Maximum of the elements of one vector, NaN-propagating (IEEE 754-2019
+// maximum, v_maximum3_f32: no input canonicalisation, two elements per
+// instruction).  For bf16 the upper element of each 32-bit word is compared as
+// the raw word read as fp32: the low 16 bits only move it within the gap to the
+// next bf16 value, which keeps the order, and masking them off afterwards
+// restores the exact element.  A raw word is NaN only when its upper element
+// is infinite or NaN; the NaN maximum then sends the segment to the exact path.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vec_max(const u32x4& v) {
+  const float h = max2(max2(__uint_as_float(v.x), __uint_as_float(v.y)),
+                       max2(__uint_as_float(v.z), __uint_as_float(v.w)));
+  const float hm = __uint_as_float(__float_as_uint(h) & 0xffff0000u);
+  return max2(max2(max2(hm, bf16_lo(v.x)), max2(bf16_lo(v.y), bf16_lo(v.z))), bf16_lo(v.w));
+}
+__device__ __forceinline__ float vec_max(const f32x4& v) {
+  return max2(max2(v.x, v.y), max2(v.z, v.w));
 }
 
-template <typename T>
-__device__ __forceinline__ void load_unit(const T* __restrict__ logits, int64_t stride,
-                                          const UnitGeom& g, int tid, Unit<T>& d) {
-  using Vec = typename VecOf<T>::type;
-  const Vec* vp = reinterpret_cast<const Vec*>(logits + g.row * stride + g.e0);
-#pragma unroll
-  for (int j = 0; j < kVPT; ++j) {
-    const int64_t i = tid + j * kThreads;
-    if (i < g.nvec) d.v[j] = __builtin_nontemporal_load(vp + i);
-    else d.v[j] = Vec{};
-  }
+__device__ __forceinline__ EntropyPartial empty_partial() {
+  EntropyPartial p;
+  p.m = -INFINITY; p.z = 0.f; p.s2 = 0.f; p.idx = kNoIdx;
+  return p;
 }
 
-struct Shared {
-  float m[kWaves];
-  float z[kWaves];
-  float s[kWaves];
-  int idx[kWaves];
-  EntropyPartial part[kWaves];
-};
+__device__ __forceinline__ EntropyPartial redo_partial() {
+  EntropyPartial p;
+  p.m = NAN; p.z = NAN; p.s2 = NAN; p.idx = kRedo;
+  return p;
+}
 
-template <typename T>
-__device__ __forceinline__ EntropyPartial exact_unit(const T* __restrict__ logits, int64_t stride,
-                                                  const UnitGeom& g, int tid, Shared& sh) {
-  constexpr int E = Elem<T>::kPerVec;
-  const T* rp = logits + g.row * stride;
-  SafeAcc acc;
-  for (int64_t k = tid; k < g.nvec; k += kThreads) {
-    const int64_t base = g.e0 + k * E;
-#pragma unroll
-    for (int j = 0; j < E; ++j) acc.add(Elem<T>::load(rp, base + j), int32_t(base + j));
-  }
-  if (tid == 0)
-    for (int64_t j = g.e0 + g.nvec * E; j < g.e1; ++j) acc.add(Elem<T>::load(rp, j), int32_t(j));
-  EntropyPartial mine = acc.result();
-  const int lane = tid & (kWave - 1);
+// Butterfly merge over the 64 lanes; the lower lane's run always goes first,
+// so every lane ends with the same, order-fixed result.
+__device__ __forceinline__ EntropyPartial wave_merge(EntropyPartial mine, int lane) {
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     EntropyPartial other;
@@ -168,154 +144,167 @@ __device__ __forceinline__ EntropyPartial exact_unit(const T* __restrict__ logit
     other.z = __shfl_xor(mine.z, o, kWave);
     other.s2 = __shfl_xor(mine.s2, o, kWave);
     other.idx = __shfl_xor(mine.idx, o, kWave);
-    mine = (lane & o) ? merge(other, mine) : merge(mine, other);   // lower lane first
+    mine = (lane & o) ? merge(other, mine) : merge(mine, other);
   }
-  if (lane == 0) sh.part[tid / kWave] = mine;
-  __syncthreads();
-  EntropyPartial r = sh.part[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) r = merge(r, sh.part[w]);
-  __syncthreads();
-  return r;
+  return mine;
 }
 
-// Fast path for one unit whose vectors are already in registers.
+// Exact element-by-element statistics of one segment, any values.
 template <typename T>
-__device__ __forceinline__ void process_unit(const T* __restrict__ logits, int64_t stride,
-                                             const UnitGeom& g, const Unit<T>& d, int tid,
-                                             Shared& sh, EntropyPartial* __restrict__ out,
-                                             int64_t u) {
+__device__ EntropyPartial exact_segment(const T* __restrict__ rp, int64_t e0, int64_t e1,
+                                        int64_t nvec, int lane) {
   constexpr int E = Elem<T>::kPerVec;
-  const int lane = tid & (kWave - 1), w = tid / kWave;
-  const bool full = (g.nvec == int64_t(kVPT) * kThreads);
-  const int64_t tail0 = g.e0 + g.nvec * E;           // scalar tail [tail0, e1): thread 0
-  const T* rp = logits + g.row * stride;
+  SafeAcc acc;
+  for (int64_t k = lane; k < nvec; k += kWave) {
+    const int64_t base = e0 + k * E;
+#pragma unroll
+    for (int j = 0; j < E; ++j) acc.add(Elem<T>::load(rp, base + j), int32_t(base + j));
+  }
+  if (lane == 0)
+    for (int64_t j = e0 + nvec * E; j < e1; ++j) acc.add(Elem<T>::load(rp, j), int32_t(j));
+  return wave_merge(acc.result(), lane);
+}
 
-  // ---- phase 1: segment maximum
-  float tm = -INFINITY;
+// One wave per (row, segment) unit; segments are kVPT * 64 vectors long.  All
+// loads of the unit are issued first (indices clamped into the segment, so the
+// loads are unconditional), then the wave reduces the segment maximum with
+// DPP, sums 2^u and 2^u u against it, and lane 0 writes the partial.  No LDS
+// and no barrier: HBM latency is hidden by the other resident waves.  A
+// segment whose fast statistics are not finite (or that holds only a few
+// trailing elements) is marked kRedo and recomputed exactly by the combine
+// kernel, which keeps that rare code out of this kernel's register budget.
+template <typename T>
+__global__ __launch_bounds__(256) void entropy_partials_kernel(
+    const T* __restrict__ logits, int64_t stride, int64_t V, int64_t n_rows,
+    const int32_t* __restrict__ n_rows_dev, int P, EntropyPartial* __restrict__ part) {
+  using Vec = typename VecOf<T>::type;
+  constexpr int E = Elem<T>::kPerVec;
+  const int lane = threadIdx.x & (kWave - 1);
+  // readfirstlane: the wave index is uniform, so the segment geometry and the
+  // base address live in scalar registers and the loads take 32-bit offsets
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t u = int64_t(blockIdx.x) * (256 / kWave) + wave;
+  int64_t nr = n_rows;
+  if (n_rows_dev != nullptr) nr = min(nr, int64_t(max(0, *n_rows_dev)));
+  if (u >= nr * P) return;                                   // wave-uniform
+  const int64_t row = u / P;
+  const int64_t e0 = (u - row * P) * seg_elems(E);
+  const int64_t e1 = min(V, e0 + seg_elems(E));
+  const int nvec = int((e1 - e0) / E);
+  const T* rp = logits + row * stride;
+  if (nvec == 0) {                                           // fewer than E elements
+    if (lane == 0) part[u] = redo_partial();
+    return;
+  }
+  // uniform base + 32-bit unsigned per-lane byte offset: scalar-base loads
+  const char* base = reinterpret_cast<const char*>(rp + e0);
+  Vec d[kVPT];
 #pragma unroll
   for (int j = 0; j < kVPT; ++j) {
-    if (!full && tid + j * kThreads >= g.nvec) continue;
-    float x[E];
-    unpack16(d.v[j], x);
-#pragma unroll
-    for (int k = 0; k < E; ++k) tm = fmaxf(tm, x[k]);
+    const uint32_t off = uint32_t(min(lane + j * kWave, nvec - 1)) * uint32_t(sizeof(Vec));
+    d[j] = *reinterpret_cast<const Vec*>(base + off);
   }
-  const bool has_tail = (tid == 0) && (tail0 < g.e1);  // < E elements past the last vector
-  if (has_tail)
-    for (int64_t j = tail0; j < g.e1; ++j) tm = fmaxf(tm, Elem<T>::load(rp, j));
-  const float wm = wave_max_dpp(tm);
-  if (lane == 0) sh.m[w] = wm;
-  __syncthreads();
-  float M = sh.m[0];
-#pragma unroll
-  for (int k = 1; k < kWaves; ++k) M = fmaxf(M, sh.m[k]);
+  const bool full = (nvec == kVPT * kWave);
+  const int64_t tail0 = e0 + int64_t(nvec) * E;              // < E trailing elements: lane 0
+  const bool has_tail = (lane == 0) && (tail0 < e1);
 
-  // ---- phase 2: sums against the exact segment maximum
+  // ---- segment maximum (per vector kept for the argmax)
+  float vm[kVPT];
+#pragma unroll
+  for (int j = 0; j < kVPT; ++j) {
+    vm[j] = vec_max(d[j]);
+    if (!full && lane + j * kWave >= nvec) vm[j] = -INFINITY;
+  }
+  float tm = vm[0];
+#pragma unroll
+  for (int j = 1; j < kVPT; ++j) tm = max2(tm, vm[j]);
+  if (has_tail)
+    for (int64_t j = tail0; j < e1; ++j) tm = max2(tm, Elem<T>::load(rp, j));
+  const float M = wave_max_dpp(tm);
+
+  // ---- sums against the exact segment maximum
   const float mL = M * kLog2e;
   float z0 = 0.f, z1 = 0.f, s0 = 0.f, s1 = 0.f;
+  if (full) {
 #pragma unroll
-  for (int j = 0; j < kVPT; ++j) {
-    if (!full && tid + j * kThreads >= g.nvec) continue;
-    float x[E];
-    unpack16(d.v[j], x);
+    for (int j = 0; j < kVPT; ++j) {
+      float x[E];
+      unpack16(d[j], x);
 #pragma unroll
-    for (int k = 0; k < E; k += 2) {
-      const float u0 = fmaf(x[k], kLog2e, -mL);
-      const float u1 = fmaf(x[k + 1], kLog2e, -mL);
-      const float e0 = fast_exp2(u0);
-      const float e1 = fast_exp2(u1);
-      z0 += e0;
-      z1 += e1;
-      s0 = fmaf(e0, u0, s0);
-      s1 = fmaf(e1, u1, s1);
+      for (int k = 0; k < E; k += 2) {
+        const float u0 = fmaf(x[k], kLog2e, -mL);
+        const float u1 = fmaf(x[k + 1], kLog2e, -mL);
+        const float q0 = fast_exp2(u0);
+        const float q1 = fast_exp2(u1);
+        z0 += q0;
+        z1 += q1;
+        s0 = fmaf(q0, u0, s0);
+        s1 = fmaf(q1, u1, s1);
+      }
+    }
+  } else {                                                   // last segment of a row
+#pragma unroll
+    for (int j = 0; j < kVPT; ++j) {
+      const bool ok = lane + j * kWave < nvec;
+      float x[E];
+      unpack16(d[j], x);
+#pragma unroll
+      for (int k = 0; k < E; k += 2) {
+        const float u0 = ok ? fmaf(x[k], kLog2e, -mL) : 0.f;
+        const float u1 = ok ? fmaf(x[k + 1], kLog2e, -mL) : 0.f;
+        const float q0 = ok ? fast_exp2(u0) : 0.f;
+        const float q1 = ok ? fast_exp2(u1) : 0.f;
+        z0 += q0;
+        z1 += q1;
+        s0 = fmaf(q0, u0, s0);
+        s1 = fmaf(q1, u1, s1);
+      }
     }
   }
   if (has_tail)
-    for (int64_t j = tail0; j < g.e1; ++j) {
+    for (int64_t j = tail0; j < e1; ++j) {
       const float u0 = fmaf(Elem<T>::load(rp, j), kLog2e, -mL);
-      const float e0 = fast_exp2(u0);
-      z0 += e0;
-      s0 = fmaf(e0, u0, s0);
+      const float q0 = fast_exp2(u0);
+      z0 += q0;
+      s0 = fmaf(q0, u0, s0);
     }
-  // argmax: the lowest index holding M, searched only by threads whose max is M
+
+  // ---- argmax: the lowest index holding M; only the lane(s) whose vectors
+  // reach M scan, and only the first such vector
   int idx = kNoIdx;
   if (tm == M) {
 #pragma unroll
     for (int j = 0; j < kVPT; ++j) {
-      if (tid + j * kThreads < g.nvec) {
+      if (idx == kNoIdx && vm[j] == M) {
         float x[E];
-        unpack16(d.v[j], x);
+        unpack16(d[j], x);
+        int k0 = E;
 #pragma unroll
-        for (int k = E - 1; k >= 0; --k)      // scanning down leaves the lowest match
-          if (x[k] == M) idx = min(idx, int32_t(g.e0 + (int64_t(tid) + j * kThreads) * E + k));
+        for (int k = E - 1; k >= 0; --k) k0 = (x[k] == M) ? k : k0;
+        idx = int32_t(e0 + int64_t(lane + j * kWave) * E + k0);
       }
     }
     if (idx == kNoIdx && has_tail)
-      for (int64_t j = tail0; j < g.e1; ++j)
+      for (int64_t j = tail0; j < e1; ++j)
         if (Elem<T>::load(rp, j) == M) { idx = int32_t(j); break; }
   }
-  const float wz = wave_sum_dpp(z0 + z1);
-  const float ws = wave_sum_dpp(s0 + s1);
-  const int wi = wave_min_i_dpp(idx);
-  if (lane == 0) { sh.z[w] = wz; sh.s[w] = ws; sh.idx[w] = wi; }
-  __syncthreads();
-  float Z = sh.z[0], S = sh.s[0];
-  int I = sh.idx[0];
-#pragma unroll
-  for (int k = 1; k < kWaves; ++k) { Z += sh.z[k]; S += sh.s[k]; I = min(I, sh.idx[k]); }
+  const float Z = wave_sum_dpp(z0 + z1);
+  const float S = wave_sum_dpp(s0 + s1);
+  const int I = wave_min_i_dpp(idx);
   const bool ok = (Z > 0.f) && (Z < INFINITY) && (fabsf(S) < INFINITY) && (fabsf(M) < INFINITY);
-  if (ok) {
-    if (tid == 0) {
-      EntropyPartial p;
-      p.m = M; p.z = Z; p.s2 = S; p.idx = I;
-      out[u] = p;
-    }
-  } else {                                       // uniform across the workgroup
-    const EntropyPartial p = exact_unit<T>(logits, stride, g, tid, sh);
-    if (tid == 0) out[u] = p;
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void entropy_partials_kernel(
-    const T* __restrict__ logits, int64_t stride, int64_t V, int64_t n_rows,
-    const int32_t* __restrict__ n_rows_dev, int P, EntropyPartial* __restrict__ part) {
-  __shared__ Shared sh;
-  const int tid = threadIdx.x;
-  int64_t nr = n_rows;
-  if (n_rows_dev != nullptr) nr = min(nr, int64_t(max(0, *n_rows_dev)));
-  const int64_t total = nr * P;
-  const int64_t G = gridDim.x;
-  int64_t u = blockIdx.x;
-  if (u >= total) return;
-  Unit<T> a, b;
-  UnitGeom ga = geom<T>(u, P, V), gb = ga;
-  load_unit<T>(logits, stride, ga, tid, a);
-  while (true) {
-    int64_t un = u + G;
-    if (un < total) { gb = geom<T>(un, P, V); load_unit<T>(logits, stride, gb, tid, b); }
-    process_unit<T>(logits, stride, ga, a, tid, sh, part, u);
-    u = un;
-    if (u >= total) break;
-    un = u + G;
-    if (un < total) { ga = geom<T>(un, P, V); load_unit<T>(logits, stride, ga, tid, a); }
-    process_unit<T>(logits, stride, gb, b, tid, sh, part, u);
-    u = un;
-    if (u >= total) break;
-  }
+  EntropyPartial p = redo_partial();
+  if (ok) { p.m = M; p.z = Z; p.s2 = S; p.idx = I; }
+  if (lane == 0) part[u] = p;
 }
 
 // Fold the segments of each row in order, then (optionally) take E over D and
 // decide.
 constexpr int kCombineThreads = 1024;
 
-__device__ __forceinline__ void finish_row(const EntropyPartial* __restrict__ part, int64_t row,
-                                           int P, float* __restrict__ H, int32_t* __restrict__ A,
+// Row statistics from the merged partial.
+__device__ __forceinline__ void finish_row(const EntropyPartial& acc, int64_t row,
+                                           float* __restrict__ H, int32_t* __restrict__ A,
                                            float* __restrict__ p1) {
-  EntropyPartial acc = part[row * P];
-  for (int s = 1; s < P; ++s) acc = merge(acc, part[row * P + s]);
   const float z = acc.z;
   const bool ok = (z > 0.f) && (z < INFINITY);            // false for NaN
   H[row] = ok ? kLn2 * (log2f(z) - acc.s2 / z) : NAN;
@@ -323,24 +312,45 @@ __device__ __forceinline__ void finish_row(const EntropyPartial* __restrict__ pa
   if (A != nullptr) A[row] = (acc.idx == kNoIdx) ? 0 : acc.idx;
 }
 
+// One wave per row: lane l folds segments l, l + 64, ... in order, then the
+// lanes merge in a fixed butterfly.  Segments marked kRedo are first replaced
+// by their exact statistics, computed by the whole wave.
+template <typename T>
 __global__ __launch_bounds__(256) void entropy_combine_kernel(
+    const T* __restrict__ logits, int64_t stride, int64_t V,
     const EntropyPartial* __restrict__ part, int64_t n_rows, const int32_t* __restrict__ n_rows_dev,
     int P, float* __restrict__ H, int32_t* __restrict__ A, float* __restrict__ p1) {
-  const int64_t row = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  constexpr int E = Elem<T>::kPerVec;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = int64_t(blockIdx.x) * (256 / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t nr = n_rows;
   if (n_rows_dev != nullptr) nr = min(nr, int64_t(max(0, *n_rows_dev)));
-  if (row < nr) finish_row(part, row, P, H, A, p1);
+  if (row >= nr) return;                                  // wave-uniform
+  const T* rp = logits + row * stride;
+  EntropyPartial acc = empty_partial();
+  for (int b = 0; b < P; b += kWave) {                    // wave-uniform loop
+    const int s = b + lane;
+    EntropyPartial p = (s < P) ? part[row * P + s] : empty_partial();
+    uint64_t redo = __ballot(s < P && p.idx == kRedo);
+    while (redo != 0) {
+      const int l = __ffsll(static_cast<unsigned long long>(redo)) - 1;
+      redo &= redo - 1;
+      const int64_t e0 = int64_t(b + l) * seg_elems(E);
+      const int64_t e1 = min(V, e0 + seg_elems(E));
+      const EntropyPartial q = exact_segment<T>(rp, e0, e1, (e1 - e0) / E, lane);
+      if (lane == l) p = q;
+    }
+    acc = merge(acc, p);
+  }
+  acc = wave_merge(acc, lane);
+  if (lane == 0) finish_row(acc, row, H, A, p1);
 }
 
 __global__ __launch_bounds__(kCombineThreads) void entropy_decide_kernel(
-    const EntropyPartial* __restrict__ part, int64_t n_rows, int P, int do_rows,
-    float* __restrict__ H, int32_t* __restrict__ A, float* __restrict__ p1,
-    const int32_t* __restrict__ D, const int32_t* __restrict__ nD, int32_t maxD, float tau,
-    float* __restrict__ e_max, int32_t* __restrict__ flag) {
+    int64_t n_rows, const float* __restrict__ H, const int32_t* __restrict__ D,
+    const int32_t* __restrict__ nD, int32_t maxD, float tau, float* __restrict__ e_max,
+    int32_t* __restrict__ flag) {
   const int tid = threadIdx.x;
-  if (do_rows)
-    for (int64_t row = tid; row < n_rows; row += kCombineThreads) finish_row(part, row, P, H, A, p1);
-  __syncthreads();                                        // H of every row visible to the workgroup
   int64_t count = n_rows;
   if (D != nullptr) count = min(int64_t(max(0, *nD)), int64_t(maxD));
   float best = -INFINITY;
@@ -395,27 +405,30 @@ hipError_t launch_entropy(const void* logits, int dtype, int64_t n_rows, const i
                           float* e_max, int32_t* flag, void* ws, hipStream_t s) {
   const int P = entropy_segments(V, dtype);
   EntropyPartial* part = static_cast<EntropyPartial*>(ws);
+  constexpr int kUnitsPerWG = 256 / kWave;
   const int64_t units = n_rows * P;
-  const int64_t cap = int64_t(device_cu_count()) * 4;
-  const int64_t grid = units < cap ? units : cap;
+  const unsigned grid = unsigned((units + kUnitsPerWG - 1) / kUnitsPerWG);
   if (dtype == 1)
-    hipLaunchKernelGGL(entropy_partials_kernel<bf16_t>, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(entropy_partials_kernel<bf16_t>, dim3(grid), dim3(256), 0, s,
                        static_cast<const bf16_t*>(logits), stride, V, n_rows, n_rows_dev, P, part);
   else
-    hipLaunchKernelGGL(entropy_partials_kernel<float>, dim3(unsigned(grid)), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(entropy_partials_kernel<float>, dim3(grid), dim3(256), 0, s,
                        static_cast<const float*>(logits), stride, V, n_rows, n_rows_dev, P, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Small standalone batches: one workgroup folds the rows and decides.
-  const bool one_wg = (e_max != nullptr) && n_rows <= 16384 && n_rows_dev == nullptr;
-  if (!one_wg) {
-    hipLaunchKernelGGL(entropy_combine_kernel, dim3(unsigned((n_rows + 255) / 256)), dim3(256), 0, s,
-                       part, n_rows, n_rows_dev, P, H, argmax, p1);
-    e = hipGetLastError();
-    if (e != hipSuccess || e_max == nullptr) return e;
-  }
-  hipLaunchKernelGGL(entropy_decide_kernel, dim3(1), dim3(kCombineThreads), 0, s, part, n_rows, P,
-                     one_wg ? 1 : 0, H, argmax, p1, D, nD, maxD, tau, e_max, flag);
+  const dim3 cgrid(unsigned((n_rows + kUnitsPerWG - 1) / kUnitsPerWG));
+  if (dtype == 1)
+    hipLaunchKernelGGL(entropy_combine_kernel<bf16_t>, cgrid, dim3(256), 0, s,
+                       static_cast<const bf16_t*>(logits), stride, V, part, n_rows, n_rows_dev, P,
+                       H, argmax, p1);
+  else
+    hipLaunchKernelGGL(entropy_combine_kernel<float>, cgrid, dim3(256), 0, s,
+                       static_cast<const float*>(logits), stride, V, part, n_rows, n_rows_dev, P,
+                       H, argmax, p1);
+  e = hipGetLastError();
+  if (e != hipSuccess || e_max == nullptr) return e;
+  hipLaunchKernelGGL(entropy_decide_kernel, dim3(1), dim3(kCombineThreads), 0, s, n_rows, H, D,
+                     nD, maxD, tau, e_max, flag);
   return hipGetLastError();
 }
 

@@ -123,7 +123,7 @@ __device__ __forceinline__ int acc_row(int j, int lane) { return 8 * (j >> 2) + 
 // ~5.5 TB/s on this part, where 32 rows x 32 B per instruction reach ~3 TB/s.
 // For bf16 that is exactly the MFMA's own operand layout (k = 32v + 8g + i);
 // for fp32 each 16-B vector feeds four 16x16x4 MFMAs.  W fragments sit in a
-// ring of kRing register buffers (loads run two iterations ahead); the
+// ring of three register buffers (loads run two iterations ahead); the
 // selected rows' activations are staged in LDS per iteration and shared by
 // the four waves.
 template <typename T> struct Mma16;
@@ -143,7 +143,6 @@ template <> struct Mma16<float> {
 };
 
 constexpr int kNV = 8;                       // 16-B vectors per lane per iteration
-constexpr int kRing = 3;                     // W register ring depth
 constexpr int kSkinnyNT = 64;                // output columns per workgroup
 template <typename T> constexpr int skit() { return kNV * 4 * (16 / int(sizeof(T))); }  // k per iteration
 
