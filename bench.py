@@ -119,7 +119,7 @@ def entropy_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("entropy_kernel<bf16>", "entropy.hip", 1),
-                     "kernel": "entropy_kernel<bf16> (one fused launch per pass)"},
+                     "kernel": "entropy pass: entropy_partials_kernel<bf16> + combine + decide"},
     }
     _log(f"entropy pass: {kern_ms * 1e3:.1f} us/launch, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
     if cpu_baseline:
@@ -303,6 +303,152 @@ def step_cpu_baseline(cfg, w, toks, masked, sched, tau) -> dict:
                       f"NumPy float64, {dt:.1f} s"}
 
 
+# --------------------------------------------------------------------------- long context
+def long_context_leg(cfg, tok_table, steps: int = 64, warmup: int = 8, cpu_baseline: bool = True) -> dict:
+    """Steady-state long-context step (Dream-shaped layer, no LM head): a
+    prefill (full step), `warmup` untimed steps, then `steps` timed steps.
+    Step t decides from two synthetic decoded rows, flat when t % 8 == 7, so
+    every step after such a step is full (all L rows) and the others recompute
+    the fixed 96 rows.  Per-step kernel time comes from events around each
+    step; attention, QKV and O-projection times from a separate pass with the
+    phase events of ec_step."""
+    import numpy as np
+    import torch
+
+    from entropy_gated_kv_amd.runner import DeviceModel, DeviceSequence, to_device
+    from synth import generators as G
+
+    m = cfg.model
+    _log(f"{cfg.name}: generating weights")
+    w = G.model_weights(cfg, tok_table=tok_table)
+    toks, masked = G.initial_sequence(cfg)
+    hist = [int(p) for p in G.long_context_history(cfg)]
+    dm = DeviceModel(m, cfg.dtype, cfg.L, w)
+    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.k, max_block=cfg.block_len)
+    ds.load_state(toks, masked, hist, 1)
+    n_total = 1 + warmup + steps + 2 * cfg.full_every
+    dec = torch.stack([to_device(G.decision_logits(cfg, t), cfg.dtype) for t in range(n_total)])
+    stream = torch.cuda.current_stream()
+
+    def one(t, ev=None):
+        ds.step_external(cfg.tau, cfg.k, cfg.prefix_len, cfg.block_len, dec[t], phase_events=ev)
+
+    def is_full(t):
+        return t == 0 or (t - 1) % cfg.full_every == cfg.full_every - 1
+
+    for t in range(0, 1 + warmup):
+        one(t)
+    torch.cuda.synchronize()
+    t_lo = 1 + warmup
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    flags = torch.zeros(steps, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flags[i].copy_(ds.full_flag[0])
+        ev[i][0].record(stream)
+        one(t_lo + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fl = flags.cpu().numpy()
+    want = np.array([int(is_full(t_lo + i)) for i in range(steps)])
+    if not np.array_equal(fl, want):
+        raise RuntimeError(f"{cfg.name}: unexpected step modes {fl.tolist()}")
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    part_ms, full_ms = float(ms[fl == 0].mean()), float(ms[fl == 1].mean())
+
+    # phase breakdown: one partial and one full step, each repeated
+    n_ev = 2 * len(PHASES)
+
+    def phase_pass(t_first, count):
+        sets = []
+        for i in range(count):
+            evs = []
+            for _ in range(n_ev):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                evs.append(e)
+            sets.append(evs)
+        torch.cuda.synchronize()
+        out = {}
+        for i in range(count):
+            one(t_first + i, sets[i])
+        torch.cuda.synchronize()
+        for k, name in enumerate(PHASES):
+            out[name] = float(np.mean([e[2 * k].elapsed_time(e[2 * k + 1]) for e in sets]))
+        return out
+
+    t_next = t_lo + steps
+    # t_next is a multiple of 8 plus 1 + warmup: find the next partial and full steps
+    tp = next(t for t in range(t_next, n_total) if not is_full(t))
+    for t in range(t_next, tp):
+        one(t)
+    ph_part = phase_pass(tp, 4)
+    tf = next(t for t in range(tp + 4, n_total) if is_full(t))
+    for t in range(tp + 4, tf):
+        one(t)
+    ph_full = phase_pass(tf, 1)
+    n_part, L = cfg.block_len + cfg.k, cfg.L
+    Hq, Hkv, dh = m.n_q_heads, m.n_kv_heads, m.head_dim
+
+    def attn(rows, t_ms):
+        flops = 4.0 * rows * L * Hq * dh
+        tf_s = flops / (t_ms * 1e-3) / 1e12
+        return {"us": round(t_ms * 1e3, 2), "gflop": round(flops / 1e9, 2),
+                "tflops": round(tf_s, 1), "mfma_frac": round(tf_s / BF16_PEAK_TFLOPS, 4),
+                "kv_bytes": 2 * Hkv * L * dh * 2}
+
+    out = {
+        "L": L, "steps_per_s": round(steps / wall, 2), "ms_per_step": round(wall * 1e3 / steps, 4),
+        "partial_step_us": round(part_ms * 1e3, 2), "full_step_us": round(full_ms * 1e3, 2),
+        "n_partial": int((fl == 0).sum()), "n_full": int((fl == 1).sum()),
+        "partial_phases_us": {k: round(v * 1e3, 2) for k, v in ph_part.items()
+                              if k not in ("ffn", "lmhead")},
+        "full_phases_us": {k: round(v * 1e3, 2) for k, v in ph_full.items()
+                           if k not in ("ffn", "lmhead")},
+        "attention_partial": attn(n_part, ph_part["attn"]),
+        "attention_full": attn(L, ph_full["attn"]),
+    }
+    _log(f"{cfg.name}: {out['steps_per_s']} steps/s; partial {out['partial_step_us']} us, "
+         f"full {out['full_step_us']} us; attention partial {out['attention_partial']}, "
+         f"full {out['attention_full']}")
+    if cpu_baseline:
+        out["cpu_baseline"] = long_context_cpu_baseline(cfg, w, toks, masked, hist)
+    del ds, dm, dec
+    torch.cuda.empty_cache()
+    return out
+
+
+def long_context_cpu_baseline(cfg, w, toks, masked, hist, budget_s: float = 15.0) -> dict:
+    """The oracle's partial steady-state steps (96 rows against a seeded cache)."""
+    import numpy as np
+
+    import oracle as O
+    from synth import generators as G
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    model = O.Model.from_arrays(cfg.model, cfg.dtype, w)
+    st = O.init_state(model, toks, masked)
+    m = cfg.model
+    st.K = [G.random_matrix(cfg.seed, (21,), (m.n_kv_heads, cfg.L, m.head_dim), 1.0, cfg.dtype).astype(np.float64)]
+    st.V = [G.random_matrix(cfg.seed, (22,), (m.n_kv_heads, cfg.L, m.head_dim), 1.0, cfg.dtype).astype(np.float64)]
+    st.history, st.flag = list(hist), 0
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and n < 8:
+        z = G.decision_logits(cfg, 1 + n)               # peaked rows: every step stays partial
+        O.step_external(model, st, cfg.tau, cfg.k, cfg.prefix_len, cfg.block_len, z)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 4), "unit": "partial steps/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} partial steps (96 rows, L = {cfg.L}) from a seeded cache, NumPy float64, {dt:.1f} s"}
+
+
 # --------------------------------------------------------------------------- profiling
 def profile_mode() -> int:
     """A short, fixed sequence for hardware-counter runs (rocprofv3 --pmc):
@@ -357,6 +503,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=22)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-entropy", action="store_true")
+    ap.add_argument("--skip-long", action="store_true", help="skip the long-context legs")
+    ap.add_argument("--skip-step", action="store_true",
+                    help="skip the step leg (diagnostics only: no headline value)")
     ap.add_argument("--profile-mode", action="store_true",
                     help="run the fixed short sequence used for hardware-counter runs")
     args = ap.parse_args()
@@ -370,32 +519,47 @@ def main() -> int:
         return 2
     if args.profile_mode:
         return profile_mode()
-    res = step_leg(args.steps, args.warmup, not args.no_cpu_baseline)
-    line = {
-        "metric": METRIC,
-        "value": round(res["value"], 2),
-        "unit": "steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(res["ms_per_step"], 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "llada8b_layer_L1024_tau1.0", "L": 1024, "prompt": 512, "gen": 512,
-                   "block": 32, "d_model": 4096, "heads": "32x128", "vocab": 126464, "k": 64,
-                   "tau": 1.0, "layers": 1},
-        "roofline": res["roofline"],
-        "partial_fraction": round(res["partial_fraction"], 3),
-        "phases_us": res["phases_us"],
-        "decision_overhead_frac": round(res["decision_overhead_frac"], 4),
-        "tau_sweep": res["tau_sweep"],
-        "speedup_vs_vanilla_at_tau_1": res["speedup_vs_vanilla_at_tau_1"],
-    }
-    if "cpu_baseline" in res:
-        line["cpu_baseline"] = res["cpu_baseline"]
+    if args.skip_step:
+        line = {"metric": METRIC, "value": None, "unit": "steps/s", "n_gpus": 1,
+                "note": "diagnostic run without the step leg (no headline value)"}
+    else:
+        res = step_leg(args.steps, args.warmup, not args.no_cpu_baseline)
+        line = {
+            "metric": METRIC,
+            "value": round(res["value"], 2),
+            "unit": "steps/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(res["ms_per_step"], 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "llada8b_layer_L1024_tau1.0", "L": 1024, "prompt": 512, "gen": 512,
+                       "block": 32, "d_model": 4096, "heads": "32x128", "vocab": 126464, "k": 64,
+                       "tau": 1.0, "layers": 1},
+            "roofline": res["roofline"],
+            "partial_fraction": round(res["partial_fraction"], 3),
+            "phases_us": res["phases_us"],
+            "decision_overhead_frac": round(res["decision_overhead_frac"], 4),
+            "tau_sweep": res["tau_sweep"],
+            "speedup_vs_vanilla_at_tau_1": res["speedup_vs_vanilla_at_tau_1"],
+        }
+        if "cpu_baseline" in res:
+            line["cpu_baseline"] = res["cpu_baseline"]
+    if not args.skip_long:
+        from synth import configs as C
+        from synth import generators as G
+        _log("generating the Dream-shaped token table")
+        tok = G.tok_emb(C.DREAM_8K)
+        line["long_context"] = {
+            "workload": "dream7b_layer_steady_state (d 3584, 28/4 x 128, V 152064, 96 rows, full every 8th)",
+            "L8224": long_context_leg(C.DREAM_8K, tok, cpu_baseline=not args.no_cpu_baseline),
+            "L32800": long_context_leg(C.DREAM_32K, tok, cpu_baseline=False),
+        }
+        del tok
     if not args.skip_entropy:
         ent = entropy_leg(50, 5, not args.no_cpu_baseline)
         line["entropy_pass"] = {"GB_per_s": round(ent["GB_per_s"], 1), "us_per_pass": round(ent["kernel_ms"] * 1e3, 2),

@@ -223,7 +223,7 @@ StepLayout step_layout(const ec_model* m, int32_t max_block, void* ws) {
     need(ec::Epi::kSwiGLU, m->L_cap, m->d_ffn, m->d);
     need(ec::Epi::kResidual, m->L_cap, m->d, m->d_ffn);
   }
-  need(ec::Epi::kLogits, max_block, m->V, m->d);
+  if (m->w_lm) need(ec::Epi::kLogits, max_block, m->V, m->d);
   s.gemm_ws = c.take<void>(gws);
   s.ent_ws = c.take<void>(ec::entropy_ws_bytes(max_block, m->V, m->dtype));
   s.cand_pos = c.take<int32_t>(size_t(max_block) * 4);
@@ -254,8 +254,9 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   if (!m || !st || !c || !ws) return EC_E_NULL;
   if (!dtype_ok(m->dtype)) return EC_E_DTYPE;
   if (!model_ok(m)) return EC_E_SHAPE;
-  if (!m->tok_emb || !m->pos_emb || !m->layers || !m->w_lm) return EC_E_NULL;
-  if (m->d_ffn && !m->norm_final) return EC_E_NULL;
+  if (!m->tok_emb || !m->pos_emb || !m->layers) return EC_E_NULL;
+  const bool external = (m->w_lm == nullptr);   // no LM head: the caller decodes
+  if (m->d_ffn && !external && !m->norm_final) return EC_E_NULL;
   for (int l = 0; l < m->n_layers; ++l) {
     const ec_layer& ly = m->layers[l];
     if (!ly.w_qkv || !ly.w_o) return EC_E_NULL;
@@ -273,12 +274,14 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
       c->block_start + c->block_len > st->L || c->k < 0 || c->k > st->history_cap ||
       c->n_unmask < 0 || st->history_cap < 1)
     return EC_E_SHAPE;
+  if (external && (c->n_unmask < 1 || c->n_unmask > c->block_len)) return EC_E_SHAPE;
   const int km = ec::gemm_k_multiple(m->dtype);
   if (m->d % km != 0 || (m->Hq * m->dh) % km != 0 || m->d_ffn % km != 0 || m->d_ffn % 32 != 0 ||
       !head_dim_ok(m->dh) || m->Hq / m->Hkv > 16 ||
       c->block_len > ec::choose_max_candidates() || st->L > ec::select_max_L())
     return EC_E_UNSUPPORTED;
-  if (!al16(ws) || !al16(m->tok_emb) || !al16(m->pos_emb) || !al16(m->w_lm) || !al16(st->logits) ||
+  if (!al16(ws) || !al16(m->tok_emb) || !al16(m->pos_emb) || (!external && !al16(m->w_lm)) ||
+      !al16(st->logits) ||
       (int64_t(m->V) * int64_t(esize(m->dtype))) % 16 != 0 ||
       (int64_t(m->L_cap) * int64_t(esize(m->dtype))) % 16 != 0)
     return EC_E_ALIGN;
@@ -349,6 +352,22 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
       EC_TRY(ec::launch_gemm_rows(gd, s.gemm_ws, stream));
       if (first) EC_TRY(tm.end(EC_PHASE_FFN));
     }
+  }
+
+  if (external) {
+    // The caller decoded c->n_unmask rows itself and left their logits in
+    // st->logits: take E over all of them and decide; tokens, mask and
+    // history stay as they are.
+    EC_TRY(tm.begin(EC_PHASE_LMHEAD));
+    EC_TRY(tm.end(EC_PHASE_LMHEAD));
+    EC_TRY(tm.begin(EC_PHASE_ENTROPY));
+    EC_TRY(ec::launch_entropy(st->logits, dt, c->n_unmask, nullptr, m->V, m->V, st->row_entropy,
+                              st->row_argmax, st->row_top1, nullptr, nullptr, 0, c->tau, st->e_max,
+                              st->full_flag, s.ent_ws, stream));
+    EC_TRY(tm.end(EC_PHASE_ENTROPY));
+    EC_TRY(tm.begin(EC_PHASE_DECIDE));
+    EC_TRY(tm.end(EC_PHASE_DECIDE));
+    return EC_OK;
   }
 
   EC_TRY(tm.begin(EC_PHASE_LMHEAD));

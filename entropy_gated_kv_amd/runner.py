@@ -38,7 +38,7 @@ class DeviceModel:
         pos = np.zeros((L_cap, shape.d), dtype=np.float32)
         pos[: weights["pos_emb"].shape[0]] = weights["pos_emb"]
         self.pos_emb = up(pos)
-        self.w_lm = up(weights["w_lm"])
+        self.w_lm = up(weights.get("w_lm"))          # None: no LM head (the caller decodes)
         self.norm_final = up(weights.get("norm_final"))
         ls = weights.get("logit_scale")
         self.logit_scale = None
@@ -62,7 +62,7 @@ class DeviceModel:
         m.tok_emb, m.pos_emb = self.tok_emb.data_ptr(), self.pos_emb.data_ptr()
         m.layers = C.cast(self._layer_arr, C.POINTER(L.ec_layer))
         m.norm_final = None if self.norm_final is None else self.norm_final.data_ptr()
-        m.w_lm = self.w_lm.data_ptr()
+        m.w_lm = None if self.w_lm is None else self.w_lm.data_ptr()
         m.logit_scale = None if self.logit_scale is None else self.logit_scale.data_ptr()
         self.struct = m
 
@@ -119,6 +119,21 @@ class DeviceSequence:
              phase_events=None) -> None:
         cfg = L.ec_step_cfg(float(tau), int(k), int(n_unmask), int(block_start), int(block_len))
         L.ec_step(self.model.struct, self.struct, cfg, self.ws, phase_events)
+
+    def step_external(self, tau: float, k: int, block_start: int, block_len: int, decoded_logits,
+                      phase_events=None) -> None:
+        """A step of a model without LM head: `decoded_logits` ([n, V] device
+        tensor, contiguous, the model's dtype) are the rows the caller decoded."""
+        if self.model.w_lm is not None:
+            raise ValueError("step_external needs a model without LM head")
+        if not decoded_logits.is_contiguous() or decoded_logits.shape[1] != self.model.shape.vocab:
+            raise ValueError("decoded_logits must be a contiguous [n, V] tensor")
+        saved = self.struct.logits
+        self.struct.logits = decoded_logits.data_ptr()
+        try:
+            self.step(tau, k, block_start, block_len, decoded_logits.shape[0], phase_events)
+        finally:
+            self.struct.logits = saved
 
     # -- state transfer (tests: teacher forcing and read-back) -------------------
     def load_state(self, tokens, masked, history: Sequence[int], flag: int,

@@ -209,6 +209,15 @@ int32_t ec_bidir_attention(const void* q, const int32_t* n_rows, int32_t max_row
  *   tokens[c] = argmax_c, is_masked[c] = 0 for c in chosen;
  *   chosen positions appended to the history ring in ascending order
  *   *e_max = max H over chosen (-inf if none); *full_flag = (*e_max > tau) || isnan
+ * Without an LM head (model->w_lm == NULL) the caller decodes: before the call
+ * it writes the logits of the n_unmask rows it decoded this step into
+ * state->logits ([n_unmask, V], 1 <= n_unmask <= block_len); the step then runs
+ * select, embed and the layers as above and ends with
+ *   H, argmax, p1 of those rows; *e_max = max H over all of them;
+ *   *full_flag = (*e_max > tau) || isnan
+ * leaving tokens, is_masked, history, chosen and n_chosen untouched and
+ * skipping the final norm (nothing reads it).  This is the steady-state
+ * long-context step, where the decoded rows come from outside the layer.
  * The first step of a sequence must run with *full_flag = 1 (no cache yet).
  * ws (ec_step_workspace_bytes(model, max_block) bytes) must be zero-filled
  * before its first use; steps leave its counters zeroed.
@@ -234,7 +243,7 @@ typedef struct ec_model {
   const void* pos_emb;        /* [L_cap, d]                                */
   const ec_layer* layers;     /* host array [n_layers]                     */
   const void* norm_final;     /* [d] (d_ffn > 0 only)                      */
-  const void* w_lm;           /* [V, d]                                    */
+  const void* w_lm;           /* [V, d], or NULL: no LM head (see above)   */
   const float* logit_scale;   /* [L_cap] device float32, or NULL (= 1)     */
 } ec_model;
 

@@ -34,4 +34,5 @@ from .entropy import (softmax_entropy, row_stats, max_entropy, decide, entropy_m
                       choose)
 from .selection import select_rows, candidates  # noqa: F401
 from .layers import linear, kv_refresh, bidir_attention, rmsnorm, swiglu  # noqa: F401
-from .step import Model, State, StepTrace, step, generate, init_state  # noqa: F401
+from .step import (Model, State, StepTrace, step, step_external, generate, init_state,  # noqa: F401
+                   forward_rows)

@@ -46,21 +46,24 @@ class Model:
     d_ffn: int
     eps: float
     dtype: str
-    tok_emb: np.ndarray                  # [V + 1, d]; row V is MASK
+    tok_emb: np.ndarray                  # [V + 1, d] float32 (storage-exact); row V is MASK
     pos_emb: np.ndarray                  # [L, d]
     layers: List[dict]
-    w_lm: np.ndarray                     # [V, d]
+    w_lm: Optional[np.ndarray]           # [V, d], or None (the caller decodes)
     norm_final: Optional[np.ndarray] = None
     logit_scale: Optional[np.ndarray] = None   # [L] or None
 
     @classmethod
     def from_arrays(cls, shape, dtype: str, w: dict) -> "Model":
         f = lambda a: None if a is None else np.asarray(a, dtype=np.float64)  # noqa: E731
+        # The token table (up to ~150k x 4k) stays in float32, which holds every
+        # storage value exactly; gathered rows are widened to float64.
         return cls(n_layers=shape.n_layers, d=shape.d, n_q=shape.n_q_heads, n_kv=shape.n_kv_heads,
                    dh=shape.head_dim, V=shape.vocab, d_ffn=shape.d_ffn, eps=shape.rms_eps,
-                   dtype=dtype, tok_emb=f(w["tok_emb"]), pos_emb=f(w["pos_emb"]),
+                   dtype=dtype, tok_emb=np.asarray(w["tok_emb"], dtype=np.float32),
+                   pos_emb=f(w["pos_emb"]),
                    layers=[{k: f(v) for k, v in lw.items()} for lw in w["layers"]],
-                   w_lm=f(w["w_lm"]), norm_final=f(w.get("norm_final")),
+                   w_lm=f(w.get("w_lm")), norm_final=f(w.get("norm_final")),
                    logit_scale=f(w.get("logit_scale")))
 
 
@@ -109,7 +112,7 @@ def forward_rows(model: Model, state: State, rows: np.ndarray) -> np.ndarray:
     """
     dt = model.dtype
     n = len(rows)
-    x = to_storage(model.tok_emb[state.tokens[rows]] + model.pos_emb[rows], dt)
+    x = to_storage(model.tok_emb[state.tokens[rows]].astype(np.float64) + model.pos_emb[rows], dt)
     scale = 1.0 / math.sqrt(model.dh)
     for l, lw in enumerate(model.layers):
         a = to_storage(rmsnorm(x, lw["norm_attn"], model.eps), dt) if model.d_ffn else x
@@ -151,6 +154,28 @@ def step(model: Model, state: State, tau: float, k: int, block_start: int, block
     state.flag = decide(E, tau)
     return StepTrace(flag_used, rows, cand, z if keep_logits else None, H, A, P, chosen, E,
                      state.flag, x[ci] if keep_logits else None)
+
+
+def step_external(model: Model, state: State, tau: float, k: int, block_start: int,
+                  block_len: int, decoded_logits) -> StepTrace:
+    """A step whose decoding happens outside the layer stack.
+
+    The forward pass is the same as in `step` (selected rows, caches refreshed);
+    the caller supplies the logits of the rows it decoded this step, and the
+    decision is taken from them alone: E = the largest entropy among those rows
+    (EntropyCache (zh) §2.2), the next step is full iff E > tau.  Tokens, mask
+    and history are left to the caller; the steady-state long-context step is
+    this case (its decoded rows are synthetic).
+    """
+    flag_used = state.flag
+    rows = select_rows(flag_used, state.masked, block_start, block_len, state.history, k)
+    forward_rows(model, state, rows)
+    z = np.asarray(decoded_logits, dtype=np.float64)
+    H, A, P = row_stats(z)
+    E = max_entropy(H, range(z.shape[0]))
+    state.flag = decide(E, tau)
+    cand = candidates(state.masked, block_start, block_len)
+    return StepTrace(flag_used, rows, cand, z, H, A, P, np.zeros(0, dtype=np.int64), E, state.flag)
 
 
 def generate(model: Model, state: State, schedule: Sequence[Tuple[int, int, int]], tau: float,

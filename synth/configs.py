@@ -163,6 +163,17 @@ class LongContextConfig:
     def L(self) -> int:
         return self.prefix_len + self.block_len
 
+    # the sequence helpers shared with StepConfig: prefix = prompt, block = gen
+    @property
+    def prompt_len(self) -> int:
+        return self.prefix_len
+
+    @property
+    def gen_len(self) -> int:
+        return self.block_len
+
+    lm_head = False
+
 
 def _dream(prefix: int) -> LongContextConfig:
     return LongContextConfig(

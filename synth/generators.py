@@ -51,9 +51,13 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
     Used only to put generated data into the storage format; inputs are finite.
     """
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(a.shape)
+    u = a.view(np.uint32).copy()             # finite inputs: the sums below stay < 2^32
+    t = u >> 16
+    t &= 1
+    t += 0x7FFF
+    u += t
+    u &= np.uint32(0xFFFF0000)
+    return u.view(np.float32).reshape(a.shape)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -167,14 +171,20 @@ def initial_sequence(cfg) -> Tuple[np.ndarray, np.ndarray]:
     return toks, masked
 
 
-def model_weights(cfg, layers: Optional[Iterable[int]] = None) -> Dict[str, object]:
-    """All weights of a (small) model as float32 arrays of storage-exact values."""
+def model_weights(cfg, layers: Optional[Iterable[int]] = None,
+                  tok_table: Optional[np.ndarray] = None) -> Dict[str, object]:
+    """All weights of a model as float32 arrays of storage-exact values.
+
+    `tok_table`: an already generated tok_emb(cfg) to reuse (it depends only on
+    the seed, vocabulary and width)."""
     m = cfg.model
     layers = range(m.n_layers) if layers is None else layers
+    if tok_table is not None and tok_table.shape != (m.vocab + 1, m.d):
+        raise ValueError("tok_table has the wrong shape")
     out: Dict[str, object] = {
-        "tok_emb": tok_emb(cfg),
+        "tok_emb": tok_emb(cfg) if tok_table is None else tok_table,
         "pos_emb": pos_emb(cfg),
-        "w_lm": layer_weight(cfg, 0, "w_lm"),
+        "w_lm": layer_weight(cfg, 0, "w_lm") if getattr(cfg, "lm_head", True) else None,
         "logit_scale": logit_scale(cfg),
         "layers": [],
     }
@@ -253,6 +263,12 @@ def decision_logits(cfg: LongContextConfig, step: int) -> np.ndarray:
     g = _rng(cfg.seed, (S_LOGITS, 2, step))
     z = g.standard_normal((cfg.decision_rows, cfg.model.vocab), dtype=np.float32) * np.float32(s)
     return _store(z, cfg.dtype)
+
+
+def long_context_history(cfg: LongContextConfig) -> np.ndarray:
+    """The steady-state decode history: the k prefix positions just before the
+    masked block, oldest first."""
+    return np.arange(cfg.prefix_len - cfg.k, cfg.prefix_len, dtype=np.int32)
 
 
 def random_logits(seed: int, rows: int, V: int, dtype: str, scale_lo: float = 0.1,

@@ -63,3 +63,19 @@ def test_dream_long_context_sampled():
                                  K[g:g + 1].astype(np.float64), V[g:g + 1].astype(np.float64),
                                  1 / math.sqrt(dh))
         assert_close(got[r, h], want[0, 0], "bf16", f"attention row {r} head {h}")
+
+
+def test_dream_long_context_full_step_sampled():
+    """Every row of the 32800-row cache as a query (the full-step launch, whose
+    last packed-row tile is ragged), checked on sampled (row, head) pairs."""
+    n, Hq, Hkv, dh, Lq = 32800, 28, 4, 128, 32800
+    q, K, V, got = run_attn("bf16", n, Hq, Hkv, dh, Lq, Lq, seed=12)
+    rng = np.random.default_rng(1)
+    rows = list(rng.integers(0, n, 10)) + [0, n - 1, n - 2]
+    heads = list(rng.integers(0, Hq, 10)) + [0, Hq - 1, 13]
+    for r, h in zip(rows, heads):
+        g = h // (Hq // Hkv)
+        want = O.bidir_attention(q[r:r + 1, h:h + 1].astype(np.float64),
+                                 K[g:g + 1].astype(np.float64), V[g:g + 1].astype(np.float64),
+                                 1 / math.sqrt(dh))
+        assert_close(got[r, h], want[0, 0], "bf16", f"attention row {r} head {h}")

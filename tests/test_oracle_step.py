@@ -164,3 +164,56 @@ def test_history_appends_each_steps_positions_in_ascending_order():
     tr = O.step(model, st, math.inf, cfg.k, *sched[8])
     recent = set(st.history[-len(tr.chosen) - cfg.k:-len(tr.chosen)])
     assert recent <= set(tr.rows.tolist())
+
+
+def test_external_decoding_step_agrees_with_step():
+    """Handing step_external the logits that step() decoded (the chosen rows)
+    must reproduce step()'s rows, caches, E and decision, and leave tokens,
+    mask and history alone."""
+    cfg = small_single()
+    model, st = build(cfg)
+    sched = C.unmask_schedule(cfg)
+    for bs, bl, n in sched[:5]:
+        O.step(model, st, 1.0, cfg.k, bs, bl, n)
+    for bs, bl, n in sched[5:9]:
+        a, b = st.copy(), st.copy()
+        tr = O.step(model, a, 1.0, cfg.k, bs, bl, n)
+        ext = tr.logits[np.searchsorted(tr.cand, tr.chosen)]
+        te = O.step_external(model, b, 1.0, cfg.k, bs, bl, ext)
+        np.testing.assert_array_equal(te.rows, tr.rows)
+        for l in range(cfg.model.n_layers):
+            assert np.array_equal(a.K[l], b.K[l]) and np.array_equal(a.V[l], b.V[l])
+        assert te.E == tr.E and b.flag == a.flag == te.flag_next
+        assert np.array_equal(b.tokens, st.tokens) and np.array_equal(b.masked, st.masked)
+        assert b.history == st.history
+        st = a
+
+
+def small_long_context():
+    return C.scaled(C.DREAM_8K, name="long_small", model_d=64, model_n_q_heads=7,
+                    model_n_kv_heads=1, model_head_dim=16, model_vocab=500, prefix_len=96,
+                    block_len=8, k=16)
+
+
+def test_long_context_steady_state_rows_and_forced_full_steps():
+    """Steady state: partial steps recompute exactly the masked block plus the
+    k history positions before it; the synthetic decision rows (flat on every
+    8th step, peaked otherwise) force a full step after each flat step."""
+    cfg = small_long_context()
+    w = G.model_weights(cfg)
+    assert w["w_lm"] is None
+    model = O.Model.from_arrays(cfg.model, cfg.dtype, w)
+    toks, masked = G.initial_sequence(cfg)
+    st = O.init_state(model, toks, masked)
+    st.history = [int(p) for p in G.long_context_history(cfg)]
+    steady = np.union1d(np.arange(cfg.prefix_len, cfg.L), G.long_context_history(cfg))
+    assert len(steady) == cfg.block_len + cfg.k
+    for t in range(0, 18):
+        tr = O.step_external(model, st, cfg.tau, cfg.k, cfg.prefix_len, cfg.block_len,
+                             G.decision_logits(cfg, t))
+        full = t == 0 or (t - 1) % cfg.full_every == cfg.full_every - 1
+        np.testing.assert_array_equal(tr.rows, np.arange(cfg.L) if full else steady, err_msg=str(t))
+        flat = t % cfg.full_every == cfg.full_every - 1
+        # flat rows: H close to ln V; peaked rows: H well below tau
+        assert (tr.E > math.log(cfg.model.vocab) - 0.1) if flat else (tr.E < cfg.tau - 0.5), (t, tr.E)
+        assert tr.flag_next == int(flat)
