@@ -25,6 +25,10 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC]
+# Per-source device options.  attention.hip: MFMA results in ordinary VGPRs
+# (the accumulator-register form makes the compiler copy the output tile
+# between register files on every kv tile).
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc() -> str:
@@ -37,7 +41,8 @@ def _hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc()] + COMMON + DEVICE_FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([_hipcc()] + COMMON + DEVICE_FLAGS + EXTRA.get(src, []) + lang +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

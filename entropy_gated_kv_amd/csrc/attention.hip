@@ -10,21 +10,31 @@
 // transposed, [Hkv, dh, L_cap].  Query heads of one KV head are packed into the
 // M dimension (packed row rho = r * G + gi, head g * G + gi, G = Hq / Hkv).
 //
-// A workgroup (4 waves, 32 packed query rows each) owns one KV head, 128 packed
-// rows and a range of kv.  Per 64-row kv tile (K and V^T tiles staged in LDS,
-// double-buffered) each wave computes
-//   S^T = K Q^T        (v_mfma_f32_32x32x16_bf16 / 32x32x2_f32; rows = kv)
-// so a lane holds one query column and 32 kv scores: the running max and sum
-// need only in-lane work plus one exchange with lane ^ 32.  K rows are loaded
-// in a permuted order (bits 2 and 3 of the row index swapped) so that each
-// lane's 16 accumulator values of a 32-row block are two runs of 8 consecutive
-// kv; those runs are then directly the k-operand of
-//   O^T += V^T P^T     (A = V^T tile rows from LDS, B = P^T from registers)
-// with P rounded to the storage dtype (bf16 MFMA) or kept fp32.
-// Two launches, each gated on the device row count: a split-KV variant for
-// up to 128 selected rows (partial steps: enough kv splits to fill the chip,
-// partial outputs merged by log-sum-exp in a second kernel) and an unsplit
-// variant for more rows (full steps), which normalises and stores directly.
+// Both kernels compute, per 64-row kv tile,
+//   S^T = K Q^T        (rows = kv, columns = packed queries)
+// so a lane holds one query column and 32 kv scores of each 32-query block:
+// the running max and sum need only in-lane work plus one exchange between
+// the two wave halves.  K rows are read in a permuted order (bits 2 and 3 of
+// the row index swapped) so that each lane's 16 accumulator values of a 32-row
+// block are two runs of 8 consecutive kv; those runs are then directly the
+// k-operand of
+//   O^T += V^T P^T     (A = V^T tile rows from LDS, B = P^T from registers).
+//
+// bfloat16 (attn_bf16_kernel): each wave owns QB blocks of 32 packed query
+// rows, so every K / V^T fragment read from LDS feeds QB MFMAs.  K and V^T
+// tiles go from global memory straight into LDS (global_load_lds_dwordx4, no
+// register staging) through a ring of three stages, two tiles ahead of the
+// compute; the 16-byte chunks of each LDS row are XOR-swizzled so that the
+// fragment reads are free of bank conflicts without padding.  P is rounded to
+// bf16 by v_cvt_pk_bf16_f32.  The output is rescaled only when a query's
+// running maximum grows by more than 2^8 (log2 domain), so P stays <= 256.
+// Partial steps (<= 128 selected rows) split the kv range: one workgroup per
+// CU, the split count chosen on the device from the actual row count, then a
+// log-sum-exp merge kernel.  Full steps run unsplit, their workgroups ordered
+// so that each XCD walks the query tiles of the same KV head together.
+//
+// float32 (attn_kernel, small workloads only): four waves of 32 packed rows,
+// K and V^T staged through registers into a double-buffered padded LDS tile.
 #include <math.h>
 
 #include "ec_device.h"
@@ -389,20 +399,459 @@ hipError_t launch_typed(const AttnArgs& a, void* ws, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ===================================================================== bfloat16
+constexpr int kStages = 3;
+
+template <int DH>
+struct BG {
+  static constexpr int RB = DH * 2;                 // bytes of one K row
+  static constexpr int CR = RB / 16;                // 16-byte chunks per K row
+  static constexpr int RPW = 256 / RB;              // K rows per 256-byte bank window
+  static constexpr int KT = kKV * RB;               // K tile bytes
+  static constexpr int VT = DH * kKV * 2;           // V^T tile bytes (DH rows of 128 B)
+  static constexpr int STAGE = KT + VT;
+  static constexpr int KIW = KT / 1024 / 4;         // 1-KiB loads per wave per K tile
+  static constexpr int VIW = VT / 1024 / 4;         // ... per V^T tile
+  static constexpr int LOADS = KIW + VIW;           // per wave per tile
+  static constexpr int ITERS = RB > 128 ? RB / 128 : 1;
+  static constexpr int VH = RB / (32 * ITERS);      // 16-byte vectors per lane half per iteration
+  static constexpr int NK = ITERS * VH;             // MFMAs per 32-row kv block (k = DH)
+  static constexpr int DB = DH / 32;
+  static_assert(KIW >= 1 && VIW >= 1, "the K and V^T tiles split over four waves");
+};
+
+// XOR swizzle of the 16-byte chunks of an LDS row: K rows (RB bytes), V^T rows
+// (128 bytes).  Consecutive rows of a 32-row fragment read then hit distinct
+// 16-byte bank groups.
+template <int DH>
+__device__ __forceinline__ int swk(int r) { return (r / BG<DH>::RPW) % BG<DH>::CR; }
+__device__ __forceinline__ int swv(int e) { return (e >> 1) & 7; }
+
+// One 1-KiB global -> LDS copy: lane l's 16 bytes at sbase + voff land at LDS
+// byte lds + 16 l.  M0 (the LDS base of the copy) is saved and restored.  The
+// copies are not visible to the compiler's wait tracking: callers wait with
+// wait_loads<N>() and a barrier before reading what they wrote.
+__device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(voff), "s"(sbase)
+      : "memory");
+}
+// Wait until at most N of this wave's copies are in flight, then synchronise
+// the workgroup; the empty asm statements keep LDS reads on their side.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_sync() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Copy kv tile [t0, t0 + 64) of one KV head into a stage: this wave's share of
+// the K rows (clamped below L) and of the V^T rows (chunks at or past L point
+// at chunk 0 of the row: finite data, multiplied by P = 0).
+template <int DH>
+__device__ __forceinline__ void load_tile(const char* kbase, const char* vbase, int L, int L_cap,
+                                          int t0, uint32_t stage, int wave, int lane) {
+  using B = BG<DH>;
+#pragma unroll
+  for (int i = 0; i < B::KIW; ++i) {
+    const int ii = wave * B::KIW + i;
+    const int r = ii * (1024 / B::RB) + lane / B::CR;
+    const int c = (lane % B::CR) ^ swk<DH>(r);
+    const int kv = min(t0 + r, L - 1);
+    lds_copy16(kbase, uint32_t(kv) * B::RB + uint32_t(c) * 16, stage + ii * 1024);
+  }
+#pragma unroll
+  for (int i = 0; i < B::VIW; ++i) {
+    const int ii = wave * B::VIW + i;
+    const int e = ii * 8 + lane / 8;
+    const int c = (lane % 8) ^ swv(e);
+    int kvs = t0 + c * 8;
+    if (kvs >= L) kvs = 0;
+    lds_copy16(vbase, (uint32_t(e) * uint32_t(L_cap) + uint32_t(kvs)) * 2u, stage + B::KT + ii * 1024);
+  }
+}
+
+// Zero the V^T entries at kv >= L of the stage holding the last tile (the
+// cache past L may hold anything, and 0 * NaN would poison the output).
+template <int DH>
+__device__ __forceinline__ void zero_vt_tail(char* stage, int t0, int L, int tid) {
+  const int x0 = L - t0, cols = kKV - x0;
+  for (int q = tid; q < DH * cols; q += kThreads) {
+    const int e = q / cols, x = x0 + q % cols;
+    *reinterpret_cast<uint16_t*>(stage + BG<DH>::KT + e * 128 + (((x >> 3) ^ swv(e)) << 4) + (x & 7) * 2) = 0;
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 (v_cvt_pk_bf16_f32: round to nearest even)
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+// value of lane l ^ 32 combined with lane l's own (v_permlane32_swap)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+struct BP {
+  const bf16_t* q;
+  const int32_t* n_rows;
+  int max_rows;
+  const bf16_t* kc;
+  const bf16_t* vc;
+  int L, L_cap, Hq, Hkv, G;
+  float sl2;            // scale * log2(e)
+  bf16_t* out;
+  float* opart;         // split partial O  [smax][Hkv][mcap][DH]
+  float* mlpart;        // split (m, l)     [smax][Hkv][mcap][2]
+  int mcap;             // packed-row capacity of the split workspace
+  int smax;             // split capacity of the split workspace
+  int partial;          // 1: split-KV variant (n <= 128), 0: unsplit
+};
+
+// Split plan of the partial variant, computed on the device from the actual
+// row count: qa query tiles, S splits of `per` kv tiles, for `grid` groups.
+struct DPlan { int qa, S, per; };
+__device__ __forceinline__ DPlan device_plan(int n, int G, int QT, int Hkv, int tiles, int grid,
+                                             int smax) {
+  DPlan d;
+  d.qa = (n * G + QT - 1) / QT;
+  int S = grid / (Hkv * d.qa);
+  S = max(1, min(S, min(smax, (tiles + 1) / 2)));          // at least two kv tiles per split
+  d.per = (tiles + S - 1) / S;
+  d.S = (tiles + d.per - 1) / d.per;
+  return d;
+}
+
+// Work index of a workgroup: the groups one XCD runs (blockIdx = x mod 8) take
+// consecutive indices, so they share KV tiles through that XCD's L2.  The
+// grid is a multiple of 8, which makes the map a bijection.
+__device__ __forceinline__ int xcd_work_index(int b, int grid) { return (b & 7) * (grid >> 3) + (b >> 3); }
+
+template <int DH, int QB>
+__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(BP p) {
+  using B = BG<DH>;
+  constexpr int QT = 4 * 32 * QB;                          // packed query rows per workgroup
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int n = min(*p.n_rows, p.max_rows);
+  if (n <= 0) return;
+  if (p.partial ? (n > kPartialMaxRows) : (n <= kPartialMaxRows)) return;
+  const int M = n * p.G;
+  const int tiles_all = (p.L + kKV - 1) / kKV;
+  const int j = xcd_work_index(blockIdx.x, gridDim.x);
+  int g, qt, kv0, kv1, split = 0;
+  if (p.partial) {
+    const DPlan d = device_plan(n, p.G, QT, p.Hkv, tiles_all, gridDim.x, p.smax);
+    if (j >= p.Hkv * d.S * d.qa) return;
+    qt = j % d.qa;
+    split = (j / d.qa) % d.S;
+    g = j / (d.qa * d.S);
+    kv0 = split * d.per * kKV;
+    kv1 = min(p.L, kv0 + d.per * kKV);
+  } else {
+    const int qtn = (M + QT - 1) / QT;
+    if (j >= p.Hkv * qtn) return;
+    qt = j % qtn;
+    g = j / qtn;
+    kv0 = 0;
+    kv1 = p.L;
+  }
+  if (kv0 >= kv1) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const char* kbase = reinterpret_cast<const char*>(p.kc + int64_t(g) * p.L_cap * DH);
+  const char* vbase = reinterpret_cast<const char*>(p.vc + int64_t(g) * DH * p.L_cap);
+  // LDS byte address of the dynamic LDS block (the copies take it in M0)
+  const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) char*)(smem)));
+  const int ntiles = (kv1 - kv0 + kKV - 1) / kKV;
+
+  // the first two tiles go out before anything else
+  load_tile<DH>(kbase, vbase, p.L, p.L_cap, kv0, lds0, wave, lane);
+  if (ntiles > 1) load_tile<DH>(kbase, vbase, p.L, p.L_cap, kv0 + kKV, lds0 + B::STAGE, wave, lane);
+
+  // Q^T fragments (k-permuted like K): [qb][it * VH + v]
+  const int rho0 = qt * QT + wave * 32 * QB;               // first packed row of this wave
+  u32x4 qf[QB][B::NK];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int rho = rho0 + qb * 32 + (lane & 31);
+    const bool ok = rho < M;
+    const int r = ok ? rho / p.G : 0, head = g * p.G + (ok ? rho % p.G : 0);
+    const char* qrow = reinterpret_cast<const char*>(p.q + (int64_t(r) * p.Hq + head) * DH);
+#pragma unroll
+    for (int it = 0; it < B::ITERS; ++it)
+#pragma unroll
+      for (int v = 0; v < B::VH; ++v)
+        qf[qb][it * B::VH + v] = ok ? *reinterpret_cast<const u32x4*>(qrow + it * 128 + (h * B::VH + v) * 16)
+                                    : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  f32x16 o[QB][B::DB];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int d = 0; d < B::DB; ++d) o[qb][d] = f32x16{};
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = kv0 + t * kKV;
+    if (t + 1 < ntiles) wait_loads_and_sync<B::LOADS>();
+    else wait_loads_and_sync<0>();
+    // stage (t + 2) % 3 was last read in iteration t - 1, which every wave has left
+    if (t + 2 < ntiles)
+      load_tile<DH>(kbase, vbase, p.L, p.L_cap, t0 + 2 * kKV, lds0 + ((t + 2) % kStages) * B::STAGE,
+                    wave, lane);
+    char* stage = smem + (t % kStages) * B::STAGE;
+    const bool tail = t0 + kKV > kv1;                       // only the last tile of the last split
+    if (tail) {
+      zero_vt_tail<DH>(stage, t0, p.L, tid);
+      __syncthreads();
+    }
+
+    // ---- S^T = K Q^T: two 32-row kv blocks, each K fragment used QB times
+    f32x16 sc[QB][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int r = kb * 32 + perm_row(lane & 31);
+      const char* krow = stage + r * B::RB;
+      const int sw = swk<DH>(r);
+      u32x4 kf[B::NK];
+#pragma unroll
+      for (int it = 0; it < B::ITERS; ++it)
+#pragma unroll
+        for (int v = 0; v < B::VH; ++v)
+          kf[it * B::VH + v] =
+              *reinterpret_cast<const u32x4*>(krow + (((it * 8 + h * B::VH + v) ^ sw) << 4));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int k = 0; k < B::NK; ++k) acc = mfma_bf16(kf[k], qf[qb][k], acc);
+        sc[qb][kb] = acc;
+      }
+    }
+
+    // ---- online softmax in the log2 domain; element i of block kb is
+    // kv kb*32 + 16*(i/8) + 8h + i%8
+    u32x4 pf[QB][2][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (tail) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (t0 + kb * 32 + 16 * (i >> 3) + 8 * h + (i & 7) >= kv1) sc[qb][kb][i] = -INFINITY;
+      }
+      float mx = sc[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[qb][kb][i]);
+      const float mt = halves_max(mx) * p.sl2;
+      const bool need = mt > m_run[qb] + 8.f;               // false for -inf and NaN
+      if (__ballot(need) != 0) {
+        const float m_new = need ? mt : m_run[qb];
+        const float alpha = need ? fast_exp2(m_run[qb] - m_new) : 1.f;
+#pragma unroll
+        for (int d = 0; d < B::DB; ++d)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[qb][d][i] *= alpha;
+        l_run[qb] *= alpha;
+        m_run[qb] = m_new;
+      }
+      const float msub = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float e = fast_exp2(fmaf(sc[qb][kb][i], p.sl2, -msub));
+          sc[qb][kb][i] = e;
+          ls += e;
+        }
+      l_run[qb] += ls;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int b = 8 * jj;
+          pf[qb][kb][jj] = u32x4{cvt_bf16x2(sc[qb][kb][b], sc[qb][kb][b + 1]),
+                                 cvt_bf16x2(sc[qb][kb][b + 2], sc[qb][kb][b + 3]),
+                                 cvt_bf16x2(sc[qb][kb][b + 4], sc[qb][kb][b + 5]),
+                                 cvt_bf16x2(sc[qb][kb][b + 6], sc[qb][kb][b + 7])};
+        }
+    }
+
+    // ---- O^T += V^T P^T: each V^T fragment used QB times
+#pragma unroll
+    for (int d = 0; d < B::DB; ++d) {
+      const int e = d * 32 + (lane & 31);
+      const char* vrow = stage + B::KT + e * 128;
+      const int sw = swv(e);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + (((kb * 4 + jj * 2 + h) ^ sw) << 4));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) o[qb][d] = mfma_bf16(vf, pf[qb][kb][jj], o[qb][d]);
+        }
+    }
+  }
+
+  // O^T element i of block d: dh row d*32 + 8*(i/4) + 4h + i%4, query = this lane
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = halves_sum(l_run[qb]);
+    const int rho = rho0 + qb * 32 + (lane & 31);
+    if (rho >= M) continue;
+    if (p.partial) {
+      const int64_t prow = (int64_t(split) * p.Hkv + g) * p.mcap + rho;
+      float* op = p.opart + prow * DH;
+#pragma unroll
+      for (int d = 0; d < B::DB; ++d)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<f32x4*>(op + d * 32 + 8 * i4 + 4 * h) =
+              f32x4{o[qb][d][4 * i4], o[qb][d][4 * i4 + 1], o[qb][d][4 * i4 + 2], o[qb][d][4 * i4 + 3]};
+      if (h == 0) { p.mlpart[prow * 2] = m_run[qb]; p.mlpart[prow * 2 + 1] = l_tot; }
+    } else {
+      const int r = rho / p.G, head = g * p.G + rho % p.G;
+      char* O = reinterpret_cast<char*>(p.out + (int64_t(r) * p.Hq + head) * DH);
+      const float inv = 1.f / l_tot;
+#pragma unroll
+      for (int d = 0; d < B::DB; ++d)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<u32x2*>(O + (d * 32 + 8 * i4 + 4 * h) * 2) =
+              u32x2{cvt_bf16x2(o[qb][d][4 * i4] * inv, o[qb][d][4 * i4 + 1] * inv),
+                    cvt_bf16x2(o[qb][d][4 * i4 + 2] * inv, o[qb][d][4 * i4 + 3] * inv)};
+    }
+  }
+}
+
+// log-sum-exp merge of the kv splits of the bf16 partial variant
+template <int DH>
+__global__ __launch_bounds__(256) void attn_bf16_merge_kernel(BP p, int QT, int grid) {
+  const int n = min(*p.n_rows, p.max_rows);
+  if (n <= 0 || n > kPartialMaxRows) return;
+  const int M = n * p.G;
+  const DPlan d = device_plan(n, p.G, QT, p.Hkv, (p.L + kKV - 1) / kKV, grid, p.smax);
+  const int idx = blockIdx.x * 256 + threadIdx.x;          // (g, rho, e)
+  const int e = idx % DH;
+  const int rho = (idx / DH) % p.mcap;
+  const int g = idx / (DH * p.mcap);
+  if (g >= p.Hkv || rho >= M) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < d.S; ++s) mx = fmaxf(mx, p.mlpart[((int64_t(s) * p.Hkv + g) * p.mcap + rho) * 2]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < d.S; ++s) {
+    const int64_t prow = (int64_t(s) * p.Hkv + g) * p.mcap + rho;
+    const float ms = p.mlpart[prow * 2];
+    if (ms == -INFINITY) continue;
+    const float w = fast_exp2(ms - mx);
+    num += w * p.opart[prow * DH + e];
+    den += w * p.mlpart[prow * 2 + 1];
+  }
+  const int r = rho / p.G, head = g * p.G + rho % p.G;
+  Elem<bf16_t>::store(p.out, (int64_t(r) * p.Hq + head) * DH + e, num / den);
+}
+
+struct BPlan { int grid_p, qb_p, mcap, smax; };
+
+BPlan plan_bf16(int L, int Hkv, int G) {
+  BPlan b;
+  const int cus = device_cu_count();
+  b.grid_p = (cus + 7) / 8 * 8;
+  b.qb_p = G >= 2 ? 2 : 1;
+  const int qt = 128 * b.qb_p;
+  b.mcap = (kPartialMaxRows * G + qt - 1) / qt * qt;
+  const int tiles = (L + kKV - 1) / kKV;
+  b.smax = max(1, min(b.grid_p / Hkv, (tiles + 1) / 2));
+  return b;
+}
+
+size_t bf16_ws_bytes(int L, int Hkv, int G, int dh) {
+  const BPlan b = plan_bf16(L, Hkv, G);
+  return size_t(b.smax) * Hkv * b.mcap * (size_t(dh) + 2) * sizeof(float);
+}
+
+template <int DH, int QB>
+hipError_t launch_bf16_kernel(const BP& p, unsigned grid, hipStream_t s) {
+  const size_t lds = size_t(kStages) * BG<DH>::STAGE;
+  hipLaunchKernelGGL((attn_bf16_kernel<DH, QB>), dim3(grid), dim3(kThreads), lds, s, p);
+  return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_bf16(const AttnArgs& a, void* ws, hipStream_t s) {
+  BP p;
+  p.q = static_cast<const bf16_t*>(a.q); p.n_rows = a.n_rows_dev; p.max_rows = a.max_rows;
+  p.kc = static_cast<const bf16_t*>(a.k_cache); p.vc = static_cast<const bf16_t*>(a.v_cache);
+  p.L = a.L; p.L_cap = a.L_cap; p.Hq = a.Hq; p.Hkv = a.Hkv; p.G = a.Hq / a.Hkv;
+  p.sl2 = a.scale * kLog2e; p.out = static_cast<bf16_t*>(a.out);
+  const BPlan b = plan_bf16(a.L, a.Hkv, p.G);
+  if (ws == nullptr) return hipErrorInvalidValue;
+  p.mcap = b.mcap; p.smax = b.smax;
+  p.opart = static_cast<float*>(ws);
+  p.mlpart = p.opart + size_t(b.smax) * a.Hkv * b.mcap * DH;
+  // split-KV variant (n <= 128): one workgroup per CU, then the merge
+  p.partial = 1;
+  hipError_t e = b.qb_p == 2 ? launch_bf16_kernel<DH, 2>(p, unsigned(b.grid_p), s)
+                             : launch_bf16_kernel<DH, 1>(p, unsigned(b.grid_p), s);
+  if (e != hipSuccess) return e;
+  const int64_t total = int64_t(a.Hkv) * b.mcap * DH;
+  hipLaunchKernelGGL((attn_bf16_merge_kernel<DH>), dim3(unsigned((total + 255) / 256)), dim3(256), 0,
+                     s, p, 128 * b.qb_p, b.grid_p);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.max_rows <= kPartialMaxRows) return e;
+  // unsplit variant (n > 128): two query blocks per wave when that still
+  // gives every CU two workgroups
+  p.partial = 0;
+  const int64_t m2 = (int64_t(a.max_rows) * p.G + 255) / 256 * a.Hkv;
+  const int qb = m2 >= 2 * device_cu_count() ? 2 : 1;
+  const int64_t groups = (int64_t(a.max_rows) * p.G + 128 * qb - 1) / (128 * qb) * a.Hkv;
+  const unsigned grid = unsigned((groups + 7) / 8 * 8);
+  return qb == 2 ? launch_bf16_kernel<DH, 2>(p, grid, s) : launch_bf16_kernel<DH, 1>(p, grid, s);
+}
+
 }  // namespace
 
 size_t attn_ws_bytes(int max_rows, int L, int Hq, int Hkv, int dh) {
   (void)max_rows;
+  // the larger of the two paths' needs (the dtype is not known here)
   const SplitPlan sp = plan_split(L, Hkv, Hq / Hkv);
-  if (sp.S <= 1) return 0;
-  return size_t(sp.S) * Hkv * sp.mcap * (size_t(dh) + 2) * sizeof(float);
+  const size_t f32 = sp.S <= 1 ? 0 : size_t(sp.S) * Hkv * sp.mcap * (size_t(dh) + 2) * sizeof(float);
+  const size_t b16 = bf16_ws_bytes(L, Hkv, Hq / Hkv, dh);
+  return f32 > b16 ? f32 : b16;
 }
 
 hipError_t launch_attention(const AttnArgs& a, void* ws, hipStream_t s) {
   if (a.dtype == 1) {
-    if (a.dh == 128) return launch_typed<bf16_t, 128>(a, ws, s);
-    if (a.dh == 64) return launch_typed<bf16_t, 64>(a, ws, s);
-    if (a.dh == 32) return launch_typed<bf16_t, 32>(a, ws, s);
+    if (a.dh == 128) return launch_bf16<128>(a, ws, s);
+    if (a.dh == 64) return launch_bf16<64>(a, ws, s);
+    if (a.dh == 32) return launch_bf16<32>(a, ws, s);
   } else {
     if (a.dh == 128) return launch_typed<float, 128>(a, ws, s);
     if (a.dh == 64) return launch_typed<float, 64>(a, ws, s);
