@@ -402,7 +402,7 @@ hipError_t launch_typed(const AttnArgs& a, void* ws, hipStream_t s) {
 // ===================================================================== bfloat16
 constexpr int kStages = 3;
 
-template <int DH>
+template <int DH, int NW>
 struct BG {
   static constexpr int RB = DH * 2;                 // bytes of one K row
   static constexpr int CR = RB / 16;                // 16-byte chunks per K row
@@ -410,27 +410,28 @@ struct BG {
   static constexpr int KT = kKV * RB;               // K tile bytes
   static constexpr int VT = DH * kKV * 2;           // V^T tile bytes (DH rows of 128 B)
   static constexpr int STAGE = KT + VT;
-  static constexpr int KIW = KT / 1024 / 4;         // 1-KiB loads per wave per K tile
-  static constexpr int VIW = VT / 1024 / 4;         // ... per V^T tile
+  static constexpr int KIW = KT / 1024 / NW;        // 1-KiB copies per wave per K tile
+  static constexpr int VIW = VT / 1024 / NW;        // ... per V^T tile
   static constexpr int LOADS = KIW + VIW;           // per wave per tile
   static constexpr int ITERS = RB > 128 ? RB / 128 : 1;
   static constexpr int VH = RB / (32 * ITERS);      // 16-byte vectors per lane half per iteration
   static constexpr int NK = ITERS * VH;             // MFMAs per 32-row kv block (k = DH)
   static constexpr int DB = DH / 32;
-  static_assert(KIW >= 1 && VIW >= 1, "the K and V^T tiles split over four waves");
+  static_assert(KIW >= 1 && VIW >= 1 && KIW * NW * 1024 == KT && VIW * NW * 1024 == VT,
+                "the K and V^T tiles split evenly over the waves");
 };
 
 // XOR swizzle of the 16-byte chunks of an LDS row: K rows (RB bytes), V^T rows
 // (128 bytes).  Consecutive rows of a 32-row fragment read then hit distinct
 // 16-byte bank groups.
 template <int DH>
-__device__ __forceinline__ int swk(int r) { return (r / BG<DH>::RPW) % BG<DH>::CR; }
+__device__ __forceinline__ int swk(int r) { return (r / (256 / (DH * 2))) % (DH / 8); }
 __device__ __forceinline__ int swv(int e) { return (e >> 1) & 7; }
 
 // One 1-KiB global -> LDS copy: lane l's 16 bytes at sbase + voff land at LDS
 // byte lds + 16 l.  M0 (the LDS base of the copy) is saved and restored.  The
 // copies are not visible to the compiler's wait tracking: callers wait with
-// wait_loads<N>() and a barrier before reading what they wrote.
+// wait_loads_and_sync<N>() before reading what they wrote.
 __device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uint32_t lds) {
   uint32_t save;
   asm volatile(
@@ -451,40 +452,70 @@ __device__ __forceinline__ void wait_loads_and_sync() {
   asm volatile("" ::: "memory");
 }
 
-// Copy kv tile [t0, t0 + 64) of one KV head into a stage: this wave's share of
-// the K rows (clamped below L) and of the V^T rows (chunks at or past L point
-// at chunk 0 of the row: finite data, multiplied by P = 0).
-template <int DH>
-__device__ __forceinline__ void load_tile(const char* kbase, const char* vbase, int L, int L_cap,
-                                          int t0, uint32_t stage, int wave, int lane) {
-  using B = BG<DH>;
+// This wave's share of one tile's copies: per-lane source offsets relative to
+// the tile start and the kv row / column each lane reads.
+template <int DH, int NW>
+struct CopyPlan {
+  uint32_t koff[BG<DH, NW>::KIW];   // K:   r * RB + chunk * 16
+  int kr[BG<DH, NW>::KIW];          //      kv row within the tile
+  uint32_t voff[BG<DH, NW>::VIW];   // V^T: (e * L_cap) * 2 + chunk * 16
+  int vc[BG<DH, NW>::VIW];          //      first kv of the chunk within the tile
+};
+
+template <int DH, int NW>
+__device__ __forceinline__ CopyPlan<DH, NW> copy_plan(int L_cap, int wave, int lane) {
+  using B = BG<DH, NW>;
+  CopyPlan<DH, NW> cp;
 #pragma unroll
   for (int i = 0; i < B::KIW; ++i) {
     const int ii = wave * B::KIW + i;
     const int r = ii * (1024 / B::RB) + lane / B::CR;
     const int c = (lane % B::CR) ^ swk<DH>(r);
-    const int kv = min(t0 + r, L - 1);
-    lds_copy16(kbase, uint32_t(kv) * B::RB + uint32_t(c) * 16, stage + ii * 1024);
+    cp.kr[i] = r;
+    cp.koff[i] = uint32_t(r) * B::RB + uint32_t(c) * 16;
   }
 #pragma unroll
   for (int i = 0; i < B::VIW; ++i) {
     const int ii = wave * B::VIW + i;
     const int e = ii * 8 + lane / 8;
     const int c = (lane % 8) ^ swv(e);
-    int kvs = t0 + c * 8;
-    if (kvs >= L) kvs = 0;
-    lds_copy16(vbase, (uint32_t(e) * uint32_t(L_cap) + uint32_t(kvs)) * 2u, stage + B::KT + ii * 1024);
+    cp.vc[i] = c * 8;
+    cp.voff[i] = uint32_t(e) * uint32_t(L_cap) * 2u + uint32_t(c) * 16;
+  }
+  return cp;
+}
+
+// Copy kv tile [t0, t0 + 64) into a stage.  CLAMP (a tile reaching past L):
+// K rows clamp to L - 1 and V^T chunks at or past L read chunk 0 of their row
+// (finite data, multiplied by P = 0).
+template <int DH, int NW, bool CLAMP>
+__device__ __forceinline__ void load_tile(const char* kbase, const char* vbase, int L,
+                                          const CopyPlan<DH, NW>& cp, int t0, uint32_t stage,
+                                          int wave) {
+  using B = BG<DH, NW>;
+#pragma unroll
+  for (int i = 0; i < B::KIW; ++i) {
+    uint32_t off = cp.koff[i] + uint32_t(t0) * B::RB;
+    if (CLAMP && t0 + cp.kr[i] > L - 1) off -= uint32_t(t0 + cp.kr[i] - (L - 1)) * B::RB;
+    lds_copy16(kbase, off, stage + (wave * B::KIW + i) * 1024);
+  }
+#pragma unroll
+  for (int i = 0; i < B::VIW; ++i) {
+    uint32_t off = cp.voff[i] + uint32_t(t0) * 2u;
+    if (CLAMP && t0 + cp.vc[i] >= L) off -= uint32_t(t0 + cp.vc[i]) * 2u;
+    lds_copy16(vbase, off, stage + B::KT + (wave * B::VIW + i) * 1024);
   }
 }
 
 // Zero the V^T entries at kv >= L of the stage holding the last tile (the
 // cache past L may hold anything, and 0 * NaN would poison the output).
-template <int DH>
+template <int DH, int NW>
 __device__ __forceinline__ void zero_vt_tail(char* stage, int t0, int L, int tid) {
   const int x0 = L - t0, cols = kKV - x0;
-  for (int q = tid; q < DH * cols; q += kThreads) {
+  for (int q = tid; q < DH * cols; q += NW * kWave) {
     const int e = q / cols, x = x0 + q % cols;
-    *reinterpret_cast<uint16_t*>(stage + BG<DH>::KT + e * 128 + (((x >> 3) ^ swv(e)) << 4) + (x & 7) * 2) = 0;
+    *reinterpret_cast<uint16_t*>(stage + BG<DH, NW>::KT + e * 128 + (((x >> 3) ^ swv(e)) << 4) +
+                                 (x & 7) * 2) = 0;
   }
 }
 
@@ -499,7 +530,13 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
   const f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
-// value of lane l ^ 32 combined with lane l's own (v_permlane32_swap)
+// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 against (1, 1))
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+}
+// lane l's value combined with lane l ^ 32's (v_permlane32_swap returns the
+// lower-half value first, the upper-half value second, in every lane)
 __device__ __forceinline__ float halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -544,10 +581,107 @@ __device__ __forceinline__ DPlan device_plan(int n, int G, int QT, int Hkv, int 
 // grid is a multiple of 8, which makes the map a bijection.
 __device__ __forceinline__ int xcd_work_index(int b, int grid) { return (b & 7) * (grid >> 3) + (b >> 3); }
 
-template <int DH, int QB>
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(BP p) {
-  using B = BG<DH>;
-  constexpr int QT = 4 * 32 * QB;                          // packed query rows per workgroup
+// One 64-row kv tile of one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// TAIL: the tile reaches past the split's end kv1 (masked scores).
+template <int DH, int QB, int NW, bool TAIL>
+__device__ __forceinline__ void attn_tile(const char* stage, int t0, int kv1, float sl2, int lane,
+                                          const u32x4 (&qf)[QB][BG<DH, NW>::NK],
+                                          f32x16 (&o)[QB][BG<DH, NW>::DB], float (&m_run)[QB],
+                                          float (&l_run)[QB]) {
+  using B = BG<DH, NW>;
+  const int h = lane >> 5;
+  // ---- S^T = K Q^T: two 32-row kv blocks, each K fragment used QB times
+  f32x16 sc[QB][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int r = kb * 32 + perm_row(lane & 31);
+    const char* krow = stage + r * B::RB;
+    const int sw = swk<DH>(r);
+    u32x4 kf[B::NK];
+#pragma unroll
+    for (int it = 0; it < B::ITERS; ++it)
+#pragma unroll
+      for (int v = 0; v < B::VH; ++v)
+        kf[it * B::VH + v] =
+            *reinterpret_cast<const u32x4*>(krow + (((it * 8 + h * B::VH + v) ^ sw) << 4));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int k = 0; k < B::NK; ++k) acc = mfma_bf16(kf[k], qf[qb][k], acc);
+      sc[qb][kb] = acc;
+    }
+  }
+
+  // ---- online softmax in the log2 domain; element i of block kb is
+  // kv kb*32 + 16*(i/8) + 8h + i%8
+  u32x4 pf[QB][2][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (TAIL) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (t0 + kb * 32 + 16 * (i >> 3) + 8 * h + (i & 7) >= kv1) sc[qb][kb][i] = -INFINITY;
+    }
+    float mx = sc[qb][0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[qb][kb][i]);
+    const float mt = halves_max(mx) * sl2;
+    const bool need = mt > m_run[qb] + 8.f;                 // false for -inf and NaN
+    if (__ballot(need) != 0) {
+      const float m_new = need ? mt : m_run[qb];
+      const float alpha = need ? fast_exp2(m_run[qb] - m_new) : 1.f;
+#pragma unroll
+      for (int d = 0; d < B::DB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[qb][d][i] *= alpha;
+      l_run[qb] *= alpha;
+      m_run[qb] = m_new;
+    }
+    const float msub = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+    float ls = l_run[qb];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = 8 * jj + 2 * k;
+          w[k] = cvt_bf16x2(fast_exp2(fmaf(sc[qb][kb][i], sl2, -msub)),
+                            fast_exp2(fmaf(sc[qb][kb][i + 1], sl2, -msub)));
+          ls = add_bf16x2(w[k], ls);       // the sum of exactly what the MFMA multiplies
+        }
+        pf[qb][kb][jj] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    l_run[qb] = ls;
+  }
+
+  // ---- O^T += V^T P^T: each V^T fragment used QB times
+#pragma unroll
+  for (int d = 0; d < B::DB; ++d) {
+    const int e = d * 32 + (lane & 31);
+    const char* vrow = stage + B::KT + e * 128;
+    const int sw = swv(e);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + (((kb * 4 + jj * 2 + h) ^ sw) << 4));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[qb][d] = mfma_bf16(vf, pf[qb][kb][jj], o[qb][d]);
+      }
+  }
+}
+
+template <int DH, int QB, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
+  using B = BG<DH, NW>;
+  constexpr int QT = NW * 32 * QB;                         // packed query rows per workgroup
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int n = min(*p.n_rows, p.max_rows);
   if (n <= 0) return;
@@ -581,10 +715,19 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(BP p) {
   // LDS byte address of the dynamic LDS block (the copies take it in M0)
   const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) char*)(smem)));
   const int ntiles = (kv1 - kv0 + kKV - 1) / kKV;
+  const bool last_partial = kv0 + ntiles * kKV > kv1;      // the last tile reaches past kv1
+  const CopyPlan<DH, NW> cp = copy_plan<DH, NW>(p.L_cap, wave, lane);
+  auto issue = [&](int t) {                                 // copies of tile t into stage t % 3
+    const uint32_t st = lds0 + (t % kStages) * B::STAGE;
+    if (last_partial && t == ntiles - 1)
+      load_tile<DH, NW, true>(kbase, vbase, p.L, cp, kv0 + t * kKV, st, wave);
+    else
+      load_tile<DH, NW, false>(kbase, vbase, p.L, cp, kv0 + t * kKV, st, wave);
+  };
 
   // the first two tiles go out before anything else
-  load_tile<DH>(kbase, vbase, p.L, p.L_cap, kv0, lds0, wave, lane);
-  if (ntiles > 1) load_tile<DH>(kbase, vbase, p.L, p.L_cap, kv0 + kKV, lds0 + B::STAGE, wave, lane);
+  issue(0);
+  if (ntiles > 1) issue(1);
 
   // Q^T fragments (k-permuted like K): [qb][it * VH + v]
   const int rho0 = qt * QT + wave * 32 * QB;               // first packed row of this wave
@@ -613,110 +756,26 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(BP p) {
     l_run[qb] = 0.f;
   }
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int t0 = kv0 + t * kKV;
-    if (t + 1 < ntiles) wait_loads_and_sync<B::LOADS>();
-    else wait_loads_and_sync<0>();
+  // full tiles: every kv of the tile lies below kv1
+  for (int t = 0; t < ntiles - 1; ++t) {
+    wait_loads_and_sync<B::LOADS>();                        // tile t landed (t + 1 may be in flight)
     // stage (t + 2) % 3 was last read in iteration t - 1, which every wave has left
-    if (t + 2 < ntiles)
-      load_tile<DH>(kbase, vbase, p.L, p.L_cap, t0 + 2 * kKV, lds0 + ((t + 2) % kStages) * B::STAGE,
-                    wave, lane);
+    if (t + 2 < ntiles) issue(t + 2);
+    attn_tile<DH, QB, NW, false>(smem + (t % kStages) * B::STAGE, kv0 + t * kKV, kv1, p.sl2, lane,
+                                 qf, o, m_run, l_run);
+  }
+  {                                                         // the last tile
+    const int t = ntiles - 1, t0 = kv0 + t * kKV;
+    wait_loads_and_sync<0>();
     char* stage = smem + (t % kStages) * B::STAGE;
-    const bool tail = t0 + kKV > kv1;                       // only the last tile of the last split
-    if (tail) {
-      zero_vt_tail<DH>(stage, t0, p.L, tid);
-      __syncthreads();
-    }
-
-    // ---- S^T = K Q^T: two 32-row kv blocks, each K fragment used QB times
-    f32x16 sc[QB][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int r = kb * 32 + perm_row(lane & 31);
-      const char* krow = stage + r * B::RB;
-      const int sw = swk<DH>(r);
-      u32x4 kf[B::NK];
-#pragma unroll
-      for (int it = 0; it < B::ITERS; ++it)
-#pragma unroll
-        for (int v = 0; v < B::VH; ++v)
-          kf[it * B::VH + v] =
-              *reinterpret_cast<const u32x4*>(krow + (((it * 8 + h * B::VH + v) ^ sw) << 4));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int k = 0; k < B::NK; ++k) acc = mfma_bf16(kf[k], qf[qb][k], acc);
-        sc[qb][kb] = acc;
+    if (last_partial) {
+      if (t0 + kKV > p.L) {
+        zero_vt_tail<DH, NW>(stage, t0, p.L, tid);
+        __syncthreads();
       }
-    }
-
-    // ---- online softmax in the log2 domain; element i of block kb is
-    // kv kb*32 + 16*(i/8) + 8h + i%8
-    u32x4 pf[QB][2][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      if (tail) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (t0 + kb * 32 + 16 * (i >> 3) + 8 * h + (i & 7) >= kv1) sc[qb][kb][i] = -INFINITY;
-      }
-      float mx = sc[qb][0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[qb][kb][i]);
-      const float mt = halves_max(mx) * p.sl2;
-      const bool need = mt > m_run[qb] + 8.f;               // false for -inf and NaN
-      if (__ballot(need) != 0) {
-        const float m_new = need ? mt : m_run[qb];
-        const float alpha = need ? fast_exp2(m_run[qb] - m_new) : 1.f;
-#pragma unroll
-        for (int d = 0; d < B::DB; ++d)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[qb][d][i] *= alpha;
-        l_run[qb] *= alpha;
-        m_run[qb] = m_new;
-      }
-      const float msub = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(fmaf(sc[qb][kb][i], p.sl2, -msub));
-          sc[qb][kb][i] = e;
-          ls += e;
-        }
-      l_run[qb] += ls;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int b = 8 * jj;
-          pf[qb][kb][jj] = u32x4{cvt_bf16x2(sc[qb][kb][b], sc[qb][kb][b + 1]),
-                                 cvt_bf16x2(sc[qb][kb][b + 2], sc[qb][kb][b + 3]),
-                                 cvt_bf16x2(sc[qb][kb][b + 4], sc[qb][kb][b + 5]),
-                                 cvt_bf16x2(sc[qb][kb][b + 6], sc[qb][kb][b + 7])};
-        }
-    }
-
-    // ---- O^T += V^T P^T: each V^T fragment used QB times
-#pragma unroll
-    for (int d = 0; d < B::DB; ++d) {
-      const int e = d * 32 + (lane & 31);
-      const char* vrow = stage + B::KT + e * 128;
-      const int sw = swv(e);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const u32x4 vf = *reinterpret_cast<const u32x4*>(vrow + (((kb * 4 + jj * 2 + h) ^ sw) << 4));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][d] = mfma_bf16(vf, pf[qb][kb][jj], o[qb][d]);
-        }
+      attn_tile<DH, QB, NW, true>(stage, t0, kv1, p.sl2, lane, qf, o, m_run, l_run);
+    } else {
+      attn_tile<DH, QB, NW, false>(stage, t0, kv1, p.sl2, lane, qf, o, m_run, l_run);
     }
   }
 
@@ -751,41 +810,63 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(BP p) {
   }
 }
 
-// log-sum-exp merge of the kv splits of the bf16 partial variant
+// log-sum-exp merge of the kv splits of the bf16 partial variant: one wave per
+// packed query row, each lane DH / 64 (or one) consecutive output elements.
 template <int DH>
 __global__ __launch_bounds__(256) void attn_bf16_merge_kernel(BP p, int QT, int grid) {
+  constexpr int EPL = DH >= 64 ? DH / 64 : 1;              // elements per lane
   const int n = min(*p.n_rows, p.max_rows);
   if (n <= 0 || n > kPartialMaxRows) return;
   const int M = n * p.G;
   const DPlan d = device_plan(n, p.G, QT, p.Hkv, (p.L + kKV - 1) / kKV, grid, p.smax);
-  const int idx = blockIdx.x * 256 + threadIdx.x;          // (g, rho, e)
-  const int e = idx % DH;
-  const int rho = (idx / DH) % p.mcap;
-  const int g = idx / (DH * p.mcap);
-  if (g >= p.Hkv || rho >= M) return;
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // (g, rho)
+  const int g = row / M, rho = row % M;
+  if (g >= p.Hkv) return;
+  const int lane = threadIdx.x & 63;
+  const int e0 = lane * EPL;
+  const bool act = e0 < DH;
+  const int64_t stride = int64_t(p.Hkv) * p.mcap;           // rows between consecutive splits
+  const int64_t r0 = int64_t(g) * p.mcap + rho;
   float mx = -INFINITY;
-  for (int s = 0; s < d.S; ++s) mx = fmaxf(mx, p.mlpart[((int64_t(s) * p.Hkv + g) * p.mcap + rho) * 2]);
-  float num = 0.f, den = 0.f;
+  for (int s = 0; s < d.S; ++s) mx = fmaxf(mx, p.mlpart[(s * stride + r0) * 2]);
+  float num[EPL], den = 0.f;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) num[k] = 0.f;
   for (int s = 0; s < d.S; ++s) {
-    const int64_t prow = (int64_t(s) * p.Hkv + g) * p.mcap + rho;
-    const float ms = p.mlpart[prow * 2];
-    if (ms == -INFINITY) continue;
-    const float w = fast_exp2(ms - mx);
-    num += w * p.opart[prow * DH + e];
-    den += w * p.mlpart[prow * 2 + 1];
+    const int64_t pr = s * stride + r0;
+    const float ms = p.mlpart[pr * 2];
+    const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mx);
+    den += w * p.mlpart[pr * 2 + 1];
+    if (act) {
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) num[k] += w * p.opart[pr * DH + e0 + k];
+    }
   }
+  if (!act) return;
   const int r = rho / p.G, head = g * p.G + rho % p.G;
-  Elem<bf16_t>::store(p.out, (int64_t(r) * p.Hq + head) * DH + e, num / den);
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k)
+    Elem<bf16_t>::store(p.out, (int64_t(r) * p.Hq + head) * DH + e0 + k, num[k] * inv);
 }
 
-struct BPlan { int grid_p, qb_p, mcap, smax; };
+// Launch shapes: waves per workgroup and 32-row query blocks per wave.
+struct BShape { int nw, qb; };
 
-BPlan plan_bf16(int L, int Hkv, int G) {
+BShape partial_shape(int G, int dh) {
+  if (dh == 32) return {4, G >= 2 ? 2 : 1};
+  return G >= 2 ? BShape{8, 1} : BShape{4, 1};
+}
+BShape full_shape(int dh) { return dh == 32 ? BShape{4, 2} : BShape{8, 1}; }
+
+struct BPlan { int grid_p, mcap, smax; BShape sp; };
+
+BPlan plan_bf16(int L, int Hkv, int G, int dh) {
   BPlan b;
   const int cus = device_cu_count();
   b.grid_p = (cus + 7) / 8 * 8;
-  b.qb_p = G >= 2 ? 2 : 1;
-  const int qt = 128 * b.qb_p;
+  b.sp = partial_shape(G, dh);
+  const int qt = b.sp.nw * 32 * b.sp.qb;
   b.mcap = (kPartialMaxRows * G + qt - 1) / qt * qt;
   const int tiles = (L + kKV - 1) / kKV;
   b.smax = max(1, min(b.grid_p / Hkv, (tiles + 1) / 2));
@@ -793,15 +874,24 @@ BPlan plan_bf16(int L, int Hkv, int G) {
 }
 
 size_t bf16_ws_bytes(int L, int Hkv, int G, int dh) {
-  const BPlan b = plan_bf16(L, Hkv, G);
+  const BPlan b = plan_bf16(L, Hkv, G, dh);
   return size_t(b.smax) * Hkv * b.mcap * (size_t(dh) + 2) * sizeof(float);
 }
 
-template <int DH, int QB>
+template <int DH, int QB, int NW>
 hipError_t launch_bf16_kernel(const BP& p, unsigned grid, hipStream_t s) {
-  const size_t lds = size_t(kStages) * BG<DH>::STAGE;
-  hipLaunchKernelGGL((attn_bf16_kernel<DH, QB>), dim3(grid), dim3(kThreads), lds, s, p);
+  const size_t lds = size_t(kStages) * BG<DH, NW>::STAGE;
+  hipLaunchKernelGGL((attn_bf16_kernel<DH, QB, NW>), dim3(grid), dim3(NW * 64), lds, s, p);
   return hipGetLastError();
+}
+
+template <int DH>
+hipError_t launch_bf16_shape(const BP& p, BShape sh, unsigned grid, hipStream_t s) {
+  if (sh.nw == 8) {
+    if constexpr (DH >= 64) return launch_bf16_kernel<DH, 1, 8>(p, grid, s);
+    return hipErrorInvalidValue;
+  }
+  return sh.qb == 2 ? launch_bf16_kernel<DH, 2, 4>(p, grid, s) : launch_bf16_kernel<DH, 1, 4>(p, grid, s);
 }
 
 template <int DH>
@@ -811,29 +901,26 @@ hipError_t launch_bf16(const AttnArgs& a, void* ws, hipStream_t s) {
   p.kc = static_cast<const bf16_t*>(a.k_cache); p.vc = static_cast<const bf16_t*>(a.v_cache);
   p.L = a.L; p.L_cap = a.L_cap; p.Hq = a.Hq; p.Hkv = a.Hkv; p.G = a.Hq / a.Hkv;
   p.sl2 = a.scale * kLog2e; p.out = static_cast<bf16_t*>(a.out);
-  const BPlan b = plan_bf16(a.L, a.Hkv, p.G);
+  const BPlan b = plan_bf16(a.L, a.Hkv, p.G, DH);
   if (ws == nullptr) return hipErrorInvalidValue;
   p.mcap = b.mcap; p.smax = b.smax;
   p.opart = static_cast<float*>(ws);
   p.mlpart = p.opart + size_t(b.smax) * a.Hkv * b.mcap * DH;
   // split-KV variant (n <= 128): one workgroup per CU, then the merge
   p.partial = 1;
-  hipError_t e = b.qb_p == 2 ? launch_bf16_kernel<DH, 2>(p, unsigned(b.grid_p), s)
-                             : launch_bf16_kernel<DH, 1>(p, unsigned(b.grid_p), s);
+  hipError_t e = launch_bf16_shape<DH>(p, b.sp, unsigned(b.grid_p), s);
   if (e != hipSuccess) return e;
-  const int64_t total = int64_t(a.Hkv) * b.mcap * DH;
-  hipLaunchKernelGGL((attn_bf16_merge_kernel<DH>), dim3(unsigned((total + 255) / 256)), dim3(256), 0,
-                     s, p, 128 * b.qb_p, b.grid_p);
+  const int64_t rows = int64_t(a.Hkv) * kPartialMaxRows * p.G;   // (g, rho) rows, upper bound
+  hipLaunchKernelGGL((attn_bf16_merge_kernel<DH>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, p,
+                     b.sp.nw * 32 * b.sp.qb, b.grid_p);
   e = hipGetLastError();
   if (e != hipSuccess || a.max_rows <= kPartialMaxRows) return e;
-  // unsplit variant (n > 128): two query blocks per wave when that still
-  // gives every CU two workgroups
+  // unsplit variant (n > 128)
   p.partial = 0;
-  const int64_t m2 = (int64_t(a.max_rows) * p.G + 255) / 256 * a.Hkv;
-  const int qb = m2 >= 2 * device_cu_count() ? 2 : 1;
-  const int64_t groups = (int64_t(a.max_rows) * p.G + 128 * qb - 1) / (128 * qb) * a.Hkv;
-  const unsigned grid = unsigned((groups + 7) / 8 * 8);
-  return qb == 2 ? launch_bf16_kernel<DH, 2>(p, grid, s) : launch_bf16_kernel<DH, 1>(p, grid, s);
+  const BShape sh = full_shape(DH);
+  const int qt = sh.nw * 32 * sh.qb;
+  const int64_t groups = (int64_t(a.max_rows) * p.G + qt - 1) / qt * a.Hkv;
+  return launch_bf16_shape<DH>(p, sh, unsigned((groups + 7) / 8 * 8), s);
 }
 
 }  // namespace
