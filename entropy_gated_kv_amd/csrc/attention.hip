@@ -23,11 +23,15 @@
 // bfloat16 (attn_bf16_kernel): each wave owns QB blocks of 32 packed query
 // rows, so every K / V^T fragment read from LDS feeds QB MFMAs.  K and V^T
 // tiles go from global memory straight into LDS (global_load_lds_dwordx4, no
-// register staging) through a ring of three stages, two tiles ahead of the
+// register staging) through a ring of NS stages, NS - 1 tiles ahead of the
 // compute; the 16-byte chunks of each LDS row are XOR-swizzled so that the
-// fragment reads are free of bank conflicts without padding.  P is rounded to
-// bf16 by v_cvt_pk_bf16_f32.  The output is rescaled only when a query's
-// running maximum grows by more than 2^8 (log2 domain), so P stays <= 256.
+// fragment reads are free of bank conflicts without padding.  In the
+// pipelined schedule a wave issues the QK MFMAs of tile t + 1 before the
+// softmax of tile t, so the matrix pipe and the vector ALU overlap within the
+// wave as well as across the two waves of each SIMD.  P is rounded to bf16 by
+// v_cvt_pk_bf16_f32 and its row sums taken with v_dot2_f32_bf16 from the same
+// packed values.  The output is rescaled only when a query's running maximum
+// grows by more than 2^8 (log2 domain), so P stays <= 256.
 // Partial steps (<= 128 selected rows) split the kv range: one workgroup per
 // CU, the split count chosen on the device from the actual row count, then a
 // log-sum-exp merge kernel.  Full steps run unsplit, their workgroups ordered
@@ -400,7 +404,6 @@ hipError_t launch_typed(const AttnArgs& a, void* ws, hipStream_t s) {
 }
 
 // ===================================================================== bfloat16
-constexpr int kStages = 3;
 
 template <int DH, int NW>
 struct BG {
@@ -581,17 +584,14 @@ __device__ __forceinline__ DPlan device_plan(int n, int G, int QT, int Hkv, int 
 // grid is a multiple of 8, which makes the map a bijection.
 __device__ __forceinline__ int xcd_work_index(int b, int grid) { return (b & 7) * (grid >> 3) + (b >> 3); }
 
-// One 64-row kv tile of one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// TAIL: the tile reaches past the split's end kv1 (masked scores).
-template <int DH, int QB, int NW, bool TAIL>
-__device__ __forceinline__ void attn_tile(const char* stage, int t0, int kv1, float sl2, int lane,
-                                          const u32x4 (&qf)[QB][BG<DH, NW>::NK],
-                                          f32x16 (&o)[QB][BG<DH, NW>::DB], float (&m_run)[QB],
-                                          float (&l_run)[QB]) {
+// The three phases of one 64-row kv tile for one wave.
+//
+// S^T = K Q^T: two 32-row kv blocks, each K fragment used QB times.
+template <int DH, int QB, int NW>
+__device__ __forceinline__ void qk_block(const char* stage, int lane,
+                                         const u32x4 (&qf)[QB][BG<DH, NW>::NK], f32x16 (&sc)[QB][2]) {
   using B = BG<DH, NW>;
   const int h = lane >> 5;
-  // ---- S^T = K Q^T: two 32-row kv blocks, each K fragment used QB times
-  f32x16 sc[QB][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int r = kb * 32 + perm_row(lane & 31);
@@ -612,10 +612,20 @@ __device__ __forceinline__ void attn_tile(const char* stage, int t0, int kv1, fl
       sc[qb][kb] = acc;
     }
   }
+}
 
-  // ---- online softmax in the log2 domain; element i of block kb is
-  // kv kb*32 + 16*(i/8) + 8h + i%8
-  u32x4 pf[QB][2][2];
+// Online softmax in the log2 domain, branch-free: element i of block kb is kv
+// kb*32 + 16*(i/8) + 8h + i%8.  A query's reference maximum m_run moves only
+// when the tile's maximum exceeds it by more than 8 (so P <= 2^8); alpha is
+// then the factor the output must be scaled by before this tile's P V is
+// added (1 otherwise), and the return value says whether any lane needs it.
+// TAIL: kv at or past kv1 are masked.
+template <int QB, bool TAIL>
+__device__ __forceinline__ bool softmax_block(f32x16 (&sc)[QB][2], int t0, int kv1, float sl2, int lane,
+                                              float (&m_run)[QB], float (&l_run)[QB], float (&alpha)[QB],
+                                              u32x4 (&pf)[QB][2][2]) {
+  const int h = lane >> 5;
+  bool any = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     if (TAIL) {
@@ -632,18 +642,12 @@ __device__ __forceinline__ void attn_tile(const char* stage, int t0, int kv1, fl
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[qb][kb][i]);
     const float mt = halves_max(mx) * sl2;
     const bool need = mt > m_run[qb] + 8.f;                 // false for -inf and NaN
-    if (__ballot(need) != 0) {
-      const float m_new = need ? mt : m_run[qb];
-      const float alpha = need ? fast_exp2(m_run[qb] - m_new) : 1.f;
-#pragma unroll
-      for (int d = 0; d < B::DB; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[qb][d][i] *= alpha;
-      l_run[qb] *= alpha;
-      m_run[qb] = m_new;
-    }
-    const float msub = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-    float ls = l_run[qb];
+    const float m_new = need ? mt : m_run[qb];
+    alpha[qb] = need ? fast_exp2(m_run[qb] - m_new) : 1.f;
+    m_run[qb] = m_new;
+    any = any || need;
+    const float msub = (m_new == -INFINITY) ? 0.f : m_new;
+    float ls = l_run[qb] * alpha[qb];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -660,8 +664,25 @@ __device__ __forceinline__ void attn_tile(const char* stage, int t0, int kv1, fl
       }
     l_run[qb] = ls;
   }
+  return __ballot(any) != 0;
+}
 
-  // ---- O^T += V^T P^T: each V^T fragment used QB times
+template <int DH, int QB, int NW>
+__device__ __forceinline__ void scale_output(const float (&alpha)[QB], f32x16 (&o)[QB][BG<DH, NW>::DB]) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int d = 0; d < BG<DH, NW>::DB; ++d)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[qb][d][i] *= alpha[qb];
+}
+
+// O^T += V^T P^T: each V^T fragment used QB times.
+template <int DH, int QB, int NW>
+__device__ __forceinline__ void pv_block(const char* stage, int lane, const u32x4 (&pf)[QB][2][2],
+                                         f32x16 (&o)[QB][BG<DH, NW>::DB]) {
+  using B = BG<DH, NW>;
+  const int h = lane >> 5;
 #pragma unroll
   for (int d = 0; d < B::DB; ++d) {
     const int e = d * 32 + (lane & 31);
@@ -678,8 +699,38 @@ __device__ __forceinline__ void attn_tile(const char* stage, int t0, int kv1, fl
   }
 }
 
-template <int DH, int QB, int NW>
+// One whole tile in sequence (the unpipelined schedule).
+template <int DH, int QB, int NW, bool TAIL>
+__device__ __forceinline__ void attn_tile(const char* stage, int t0, int kv1, float sl2, int lane,
+                                          const u32x4 (&qf)[QB][BG<DH, NW>::NK],
+                                          f32x16 (&o)[QB][BG<DH, NW>::DB], float (&m_run)[QB],
+                                          float (&l_run)[QB]) {
+  f32x16 sc[QB][2];
+  qk_block<DH, QB, NW>(stage, lane, qf, sc);
+  float alpha[QB];
+  u32x4 pf[QB][2][2];
+  if (softmax_block<QB, TAIL>(sc, t0, kv1, sl2, lane, m_run, l_run, alpha, pf))
+    scale_output<DH, QB, NW>(alpha, o);
+  pv_block<DH, QB, NW>(stage, lane, pf, o);
+}
+
+// Wait until at most `younger` tiles (0..2) issued after the one needed are in
+// flight, then synchronise the workgroup.
+template <int LOADS>
+__device__ __forceinline__ void wait_tiles_and_sync(int younger) {
+  if (younger >= 2) wait_loads_and_sync<2 * LOADS>();
+  else if (younger == 1) wait_loads_and_sync<LOADS>();
+  else wait_loads_and_sync<0>();
+}
+
+// PIPE: software-pipelined schedule.  Each step issues the QK MFMAs of tile
+// t + 1 before the softmax of tile t, so the matrix pipe works on the next
+// tile while the vector ALU exponentiates the current one; the output is then
+// rescaled if needed and P V of tile t accumulated.
+template <int DH, int QB, int NW, int NS, bool PIPE>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
+  static_assert(NS >= 2 && NS <= 4, "two to four LDS stages");
+  static_assert(!PIPE || NS >= 3, "the pipelined schedule reads two stages per step");
   using B = BG<DH, NW>;
   constexpr int QT = NW * 32 * QB;                         // packed query rows per workgroup
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -717,17 +768,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
   const int ntiles = (kv1 - kv0 + kKV - 1) / kKV;
   const bool last_partial = kv0 + ntiles * kKV > kv1;      // the last tile reaches past kv1
   const CopyPlan<DH, NW> cp = copy_plan<DH, NW>(p.L_cap, wave, lane);
-  auto issue = [&](int t) {                                 // copies of tile t into stage t % 3
-    const uint32_t st = lds0 + (t % kStages) * B::STAGE;
+  auto issue = [&](int t) {                                 // copies of tile t into stage t % NS
+    const uint32_t st = lds0 + (t % NS) * B::STAGE;
     if (last_partial && t == ntiles - 1)
       load_tile<DH, NW, true>(kbase, vbase, p.L, cp, kv0 + t * kKV, st, wave);
     else
       load_tile<DH, NW, false>(kbase, vbase, p.L, cp, kv0 + t * kKV, st, wave);
   };
 
-  // the first two tiles go out before anything else
-  issue(0);
-  if (ntiles > 1) issue(1);
+  // the first NS - 1 tiles go out before anything else
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < ntiles) issue(t);
 
   // Q^T fragments (k-permuted like K): [qb][it * VH + v]
   const int rho0 = qt * QT + wave * 32 * QB;               // first packed row of this wave
@@ -756,18 +808,71 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
     l_run[qb] = 0.f;
   }
 
+  if constexpr (PIPE) {
+    const bool zero_last = (kv0 + (ntiles - 1) * kKV) + kKV > p.L;   // V^T columns past L in the last tile
+    auto stage = [&](int t) { return smem + (t % NS) * B::STAGE; };
+    f32x16 scA[QB][2], scB[QB][2];
+    // prologue: tile 0 landed, its scores
+    wait_tiles_and_sync<B::LOADS>(min(NS - 1, ntiles) - 1);
+    if (zero_last && ntiles == 1) {
+      zero_vt_tail<DH, NW>(stage(0), kv0, p.L, tid);
+      __syncthreads();
+    }
+    qk_block<DH, QB, NW>(stage(0), lane, qf, scA);
+    // step t < ntiles - 1: scores of tile t in cur, of tile t + 1 into nxt
+    auto step = [&](int t, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2]) {
+      wait_tiles_and_sync<B::LOADS>(min(NS - 3, ntiles - t - 2));   // tile t + 1 landed
+      // stage (t + NS - 1) % NS was last read in step t - 1, which every wave has left
+      if (t + NS - 1 < ntiles) issue(t + NS - 1);
+      if (zero_last && t + 1 == ntiles - 1) {
+        zero_vt_tail<DH, NW>(stage(t + 1), kv0 + (t + 1) * kKV, p.L, tid);
+        __syncthreads();
+      }
+      qk_block<DH, QB, NW>(stage(t + 1), lane, qf, nxt);
+      float alpha[QB];
+      u32x4 pf[QB][2][2];
+      if (softmax_block<QB, false>(cur, kv0 + t * kKV, kv1, p.sl2, lane, m_run, l_run, alpha, pf))
+        scale_output<DH, QB, NW>(alpha, o);
+      pv_block<DH, QB, NW>(stage(t), lane, pf, o);
+    };
+    auto finish = [&](f32x16 (&cur)[QB][2]) {               // the last tile
+      const int t = ntiles - 1;
+      float alpha[QB];
+      u32x4 pf[QB][2][2];
+      const bool any = last_partial
+          ? softmax_block<QB, true>(cur, kv0 + t * kKV, kv1, p.sl2, lane, m_run, l_run, alpha, pf)
+          : softmax_block<QB, false>(cur, kv0 + t * kKV, kv1, p.sl2, lane, m_run, l_run, alpha, pf);
+      if (any) scale_output<DH, QB, NW>(alpha, o);
+      pv_block<DH, QB, NW>(stage(t), lane, pf, o);
+    };
+    int t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+      step(t, scA, scB);
+      step(t + 1, scB, scA);
+    }
+    if (t + 1 < ntiles) {
+      step(t, scA, scB);
+      finish(scB);
+    } else {
+      finish(scA);
+    }
+  } else {
   // full tiles: every kv of the tile lies below kv1
   for (int t = 0; t < ntiles - 1; ++t) {
-    wait_loads_and_sync<B::LOADS>();                        // tile t landed (t + 1 may be in flight)
-    // stage (t + 2) % 3 was last read in iteration t - 1, which every wave has left
-    if (t + 2 < ntiles) issue(t + 2);
-    attn_tile<DH, QB, NW, false>(smem + (t % kStages) * B::STAGE, kv0 + t * kKV, kv1, p.sl2, lane,
+    // tile t landed; the min(NS - 2, ntiles - 1 - t) tiles issued after it may be in flight
+    const int younger = min(NS - 2, ntiles - 1 - t);
+    if (NS >= 4 && younger >= 2) wait_loads_and_sync<2 * B::LOADS>();
+    else if (NS >= 3 && younger >= 1) wait_loads_and_sync<B::LOADS>();
+    else wait_loads_and_sync<0>();
+    // stage (t + NS - 1) % NS was last read in iteration t - 1, which every wave has left
+    if (t + NS - 1 < ntiles) issue(t + NS - 1);
+    attn_tile<DH, QB, NW, false>(smem + (t % NS) * B::STAGE, kv0 + t * kKV, kv1, p.sl2, lane,
                                  qf, o, m_run, l_run);
   }
   {                                                         // the last tile
     const int t = ntiles - 1, t0 = kv0 + t * kKV;
     wait_loads_and_sync<0>();
-    char* stage = smem + (t % kStages) * B::STAGE;
+    char* stage = smem + (t % NS) * B::STAGE;
     if (last_partial) {
       if (t0 + kKV > p.L) {
         zero_vt_tail<DH, NW>(stage, t0, p.L, tid);
@@ -777,6 +882,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
     } else {
       attn_tile<DH, QB, NW, false>(stage, t0, kv1, p.sl2, lane, qf, o, m_run, l_run);
     }
+  }
   }
 
   // O^T element i of block d: dh row d*32 + 8*(i/4) + 4h + i%4, query = this lane
@@ -811,7 +917,12 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
 }
 
 // log-sum-exp merge of the kv splits of the bf16 partial variant: one wave per
-// packed query row, each lane DH / 64 (or one) consecutive output elements.
+// packed query row.  Lane s holds split s's (m, l) (S <= 64), so the weights
+// w_s = 2^(m_s - max m) and the denominator come from one round of loads and
+// two wave reductions; the partial outputs are then summed with every lane
+// owning DH / 64 (or one) consecutive elements, eight splits' loads in flight.
+constexpr int kMaxSplits = 64;
+
 template <int DH>
 __global__ __launch_bounds__(256) void attn_bf16_merge_kernel(BP p, int QT, int grid) {
   constexpr int EPL = DH >= 64 ? DH / 64 : 1;              // elements per lane
@@ -823,23 +934,35 @@ __global__ __launch_bounds__(256) void attn_bf16_merge_kernel(BP p, int QT, int 
   const int g = row / M, rho = row % M;
   if (g >= p.Hkv) return;
   const int lane = threadIdx.x & 63;
-  const int e0 = lane * EPL;
-  const bool act = e0 < DH;
   const int64_t stride = int64_t(p.Hkv) * p.mcap;           // rows between consecutive splits
   const int64_t r0 = int64_t(g) * p.mcap + rho;
-  float mx = -INFINITY;
-  for (int s = 0; s < d.S; ++s) mx = fmaxf(mx, p.mlpart[(s * stride + r0) * 2]);
-  float num[EPL], den = 0.f;
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < d.S) {
+    ms = p.mlpart[(lane * stride + r0) * 2];
+    ls = p.mlpart[(lane * stride + r0) * 2 + 1];
+  }
+  const float mx = wave_max(ms);
+  const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mx);
+  const float den = wave_sum(w * ls);
+  const int e0 = lane * EPL;
+  const bool act = e0 < DH;
+  float num[EPL];
 #pragma unroll
   for (int k = 0; k < EPL; ++k) num[k] = 0.f;
-  for (int s = 0; s < d.S; ++s) {
-    const int64_t pr = s * stride + r0;
-    const float ms = p.mlpart[pr * 2];
-    const float w = (ms == -INFINITY) ? 0.f : fast_exp2(ms - mx);
-    den += w * p.mlpart[pr * 2 + 1];
-    if (act) {
+  const float* op = p.opart + r0 * DH + (act ? e0 : 0);
+  for (int s0 = 0; s0 < d.S; s0 += 8) {
+    float v[8][EPL];
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) num[k] += w * p.opart[pr * DH + e0 + k];
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, d.S - 1);                  // clamped: weight 0 below
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) v[u][k] = op[s * stride * DH + k];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wu = (s0 + u < d.S) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s0 + u)) : 0.f;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) num[k] = fmaf(wu, v[u][k], num[k]);
     }
   }
   if (!act) return;
@@ -850,26 +973,30 @@ __global__ __launch_bounds__(256) void attn_bf16_merge_kernel(BP p, int QT, int 
     Elem<bf16_t>::store(p.out, (int64_t(r) * p.Hq + head) * DH + e0 + k, num[k] * inv);
 }
 
-// Launch shapes: waves per workgroup and 32-row query blocks per wave.
-struct BShape { int nw, qb; };
+// Launch shapes: waves per workgroup, 32-row query blocks per wave, LDS
+// stages, and (partial variant) workgroups per CU in the grid.
+struct BShape { int nw, qb, ns, wpc, pipe; };
 
+// Measured on the Dream- and LLaDA-shaped workloads: eight waves of one query
+// block, four stages and the pipelined schedule for head dims 64 / 128 (two
+// waves per SIMD, next-tile QK under the current softmax); four waves for
+// MHA partial steps (one query tile per head) and for head dim 32.
 BShape partial_shape(int G, int dh) {
-  if (dh == 32) return {4, G >= 2 ? 2 : 1};
-  return G >= 2 ? BShape{8, 1} : BShape{4, 1};
+  if (dh == 32) return {4, G >= 2 ? 2 : 1, 3, 1, 0};
+  return G >= 2 ? BShape{8, 1, 4, 1, 1} : BShape{4, 1, 3, 1, 0};
 }
-BShape full_shape(int dh) { return dh == 32 ? BShape{4, 2} : BShape{8, 1}; }
+BShape full_shape(int dh) { return dh == 32 ? BShape{4, 2, 3, 1, 0} : BShape{8, 1, 4, 1, 1}; }
 
 struct BPlan { int grid_p, mcap, smax; BShape sp; };
 
 BPlan plan_bf16(int L, int Hkv, int G, int dh) {
   BPlan b;
-  const int cus = device_cu_count();
-  b.grid_p = (cus + 7) / 8 * 8;
   b.sp = partial_shape(G, dh);
+  b.grid_p = (device_cu_count() * b.sp.wpc + 7) / 8 * 8;
   const int qt = b.sp.nw * 32 * b.sp.qb;
   b.mcap = (kPartialMaxRows * G + qt - 1) / qt * qt;
   const int tiles = (L + kKV - 1) / kKV;
-  b.smax = max(1, min(b.grid_p / Hkv, (tiles + 1) / 2));
+  b.smax = max(1, min(min(b.grid_p / Hkv, kMaxSplits), (tiles + 1) / 2));
   return b;
 }
 
@@ -878,20 +1005,22 @@ size_t bf16_ws_bytes(int L, int Hkv, int G, int dh) {
   return size_t(b.smax) * Hkv * b.mcap * (size_t(dh) + 2) * sizeof(float);
 }
 
-template <int DH, int QB, int NW>
+template <int DH, int QB, int NW, int NS, bool PIPE>
 hipError_t launch_bf16_kernel(const BP& p, unsigned grid, hipStream_t s) {
-  const size_t lds = size_t(kStages) * BG<DH, NW>::STAGE;
-  hipLaunchKernelGGL((attn_bf16_kernel<DH, QB, NW>), dim3(grid), dim3(NW * 64), lds, s, p);
+  const size_t lds = size_t(NS) * BG<DH, NW>::STAGE;
+  hipLaunchKernelGGL((attn_bf16_kernel<DH, QB, NW, NS, PIPE>), dim3(grid), dim3(NW * 64), lds, s, p);
   return hipGetLastError();
 }
 
+// the shapes this library instantiates
 template <int DH>
 hipError_t launch_bf16_shape(const BP& p, BShape sh, unsigned grid, hipStream_t s) {
-  if (sh.nw == 8) {
-    if constexpr (DH >= 64) return launch_bf16_kernel<DH, 1, 8>(p, grid, s);
-    return hipErrorInvalidValue;
+  if constexpr (DH >= 64) {
+    if (sh.nw == 8 && sh.qb == 1 && sh.ns == 4 && sh.pipe) return launch_bf16_kernel<DH, 1, 8, 4, true>(p, grid, s);
   }
-  return sh.qb == 2 ? launch_bf16_kernel<DH, 2, 4>(p, grid, s) : launch_bf16_kernel<DH, 1, 4>(p, grid, s);
+  if (sh.nw == 4 && sh.qb == 1 && sh.ns == 3 && !sh.pipe) return launch_bf16_kernel<DH, 1, 4, 3, false>(p, grid, s);
+  if (sh.nw == 4 && sh.qb == 2 && sh.ns == 3 && !sh.pipe) return launch_bf16_kernel<DH, 2, 4, 3, false>(p, grid, s);
+  return hipErrorInvalidValue;
 }
 
 template <int DH>
