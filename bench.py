@@ -15,6 +15,10 @@ Workloads:
             value = denoise steps/s.  Also: tau sweep, vanilla (tau = -inf).
   entropy   4096 x 126464 bf16 logits, one entropy pass (GB/s); reported as
             the "entropy_pass" object next to the step line.
+  stack32   the 32-layer LLaDA-shaped stack (RMSNorm + SwiGLU 12288), L = 2048:
+            end-to-end steps/s at tau = 1.0 and vanilla ("stack32").
+  long      the Dream-shaped layer at L = 8224 / 32800, steady state: partial
+            and full step times, attention MFMA fraction ("long_context").
 """
 from __future__ import annotations
 
@@ -449,6 +453,80 @@ def long_context_cpu_baseline(cfg, w, toks, masked, hist, budget_s: float = 15.0
             "sample": f"{n} partial steps (96 rows, L = {cfg.L}) from a seeded cache, NumPy float64, {dt:.1f} s"}
 
 
+# --------------------------------------------------------------------------- 32-layer stack
+def stack_leg(n_steps: int = 66) -> dict:
+    """End-to-end denoise steps/s of the 32-layer LLaDA-shaped stack (RMSNorm,
+    MHA 32 x 128, SwiGLU 12288, L = 2048 = 1792 + 256 in blocks of 32, k = 64,
+    V = 126464) over the first `n_steps` steps of the schedule at tau = 1.0,
+    and the same steps with tau = -inf (vanilla: every step full).  Weights
+    are generated and uploaded one layer at a time."""
+    import numpy as np
+    import torch
+
+    from entropy_gated_kv_amd.runner import DeviceModel, DeviceSequence
+    from synth import configs as C
+    from synth import generators as G
+
+    cfg = C.LLADA_STACK
+    m = cfg.model
+    t_gen = time.perf_counter()
+
+    _log(f"{cfg.name}: generating and uploading weights layer by layer")
+    w = G.model_weights_streamed(cfg)
+    dm = DeviceModel(m, cfg.dtype, cfg.L, w)
+    del w
+    _log(f"{cfg.name}: weights in HBM after {time.perf_counter() - t_gen:.1f} s")
+    toks, masked = G.initial_sequence(cfg)
+    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len)
+    sched = C.unmask_schedule(cfg)[:n_steps]
+    init = (ds.tokens.clone(), ds.is_masked.clone())
+
+    def reset():
+        ds.tokens.copy_(init[0])
+        ds.is_masked.copy_(init[1])
+        ds.history_len.zero_()
+        ds.full_flag.fill_(1)
+
+    def run(tau, flags=None, events=None):
+        for i, (bs, bl, nn) in enumerate(sched):
+            if flags is not None:
+                flags[i].copy_(ds.full_flag[0])
+            if events is not None:
+                events[i][0].record()
+            ds.step(tau, cfg.k, bs, bl, nn)
+            if events is not None:
+                events[i][1].record()
+
+    reset()
+    for bs, bl, nn in sched[:3]:                 # warm-up (one full, two partial steps)
+        ds.step(1.0, cfg.k, bs, bl, nn)
+    out = {"workload": "llada8b_stack32_L2048 (32 layers, d 4096, 32x128, SwiGLU 12288, V 126464, "
+                       "k 64, tau 1.0)", "steps": len(sched)}
+    for tau, key in ((1.0, "entropycache"), (float("-inf"), "vanilla")):
+        reset()
+        flags = torch.zeros(len(sched), dtype=torch.int32, device="cuda")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sched]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run(tau, flags, ev)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        fl = flags.cpu().numpy()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        rec = {"steps_per_s": round(len(sched) / wall, 3), "ms_per_step": round(wall * 1e3 / len(sched), 3),
+               "partial_fraction": round(float(1.0 - fl.mean()), 3)}
+        if (fl == 1).any():
+            rec["full_step_ms"] = round(float(ms[fl == 1].mean()), 3)
+        if (fl == 0).any():
+            rec["partial_step_ms"] = round(float(ms[fl == 0].mean()), 3)
+        out[key] = rec
+        _log(f"{cfg.name} tau={tau}: {rec}")
+    out["speedup_vs_vanilla"] = round(out["entropycache"]["steps_per_s"] / out["vanilla"]["steps_per_s"], 3)
+    del ds, dm
+    torch.cuda.empty_cache()
+    return out
+
+
 # --------------------------------------------------------------------------- profiling
 def profile_mode() -> int:
     """A short, fixed sequence for hardware-counter runs (rocprofv3 --pmc):
@@ -504,6 +582,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-entropy", action="store_true")
     ap.add_argument("--skip-long", action="store_true", help="skip the long-context legs")
+    ap.add_argument("--skip-stack", action="store_true", help="skip the 32-layer stack leg")
     ap.add_argument("--skip-step", action="store_true",
                     help="skip the step leg (diagnostics only: no headline value)")
     ap.add_argument("--profile-mode", action="store_true",
@@ -549,6 +628,8 @@ def main() -> int:
         }
         if "cpu_baseline" in res:
             line["cpu_baseline"] = res["cpu_baseline"]
+    if not args.skip_stack:
+        line["stack32"] = stack_leg()
     if not args.skip_long:
         from synth import configs as C
         from synth import generators as G

@@ -201,6 +201,34 @@ def model_weights(cfg, layers: Optional[Iterable[int]] = None,
     return out
 
 
+def model_weights_streamed(cfg, tok_table: Optional[np.ndarray] = None) -> Dict[str, object]:
+    """model_weights(cfg) with "layers" as a generator: each layer's arrays are
+    drawn only when the consumer asks for them, so a large stack can be
+    uploaded layer by layer (values identical to model_weights)."""
+    m = cfg.model
+
+    def layers():
+        for l in range(m.n_layers):
+            lw = {"w_qkv": layer_weight(cfg, l, "w_qkv"), "w_o": layer_weight(cfg, l, "w_o")}
+            if m.d_ffn:
+                lw.update(
+                    norm_attn=norm_gain(cfg), norm_ffn=norm_gain(cfg),
+                    w_gate=layer_weight(cfg, l, "w_gate"), w_up=layer_weight(cfg, l, "w_up"),
+                    w_down=layer_weight(cfg, l, "w_down"))
+            yield lw
+
+    out: Dict[str, object] = {
+        "tok_emb": tok_emb(cfg) if tok_table is None else tok_table,
+        "pos_emb": pos_emb(cfg),
+        "w_lm": layer_weight(cfg, 0, "w_lm") if getattr(cfg, "lm_head", True) else None,
+        "logit_scale": logit_scale(cfg),
+        "layers": layers(),
+    }
+    if m.d_ffn:
+        out["norm_final"] = norm_gain(cfg)
+    return out
+
+
 # -- synthetic logits (entropy-only workload and long-context decision rows) ---
 
 def entropy_row_scales(cfg: EntropyOnlyConfig) -> np.ndarray:

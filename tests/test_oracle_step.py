@@ -217,3 +217,16 @@ def test_long_context_steady_state_rows_and_forced_full_steps():
         # flat rows: H close to ln V; peaked rows: H well below tau
         assert (tr.E > math.log(cfg.model.vocab) - 0.1) if flat else (tr.E < cfg.tau - 0.5), (t, tr.E)
         assert tr.flag_next == int(flat)
+
+
+def test_streamed_weights_equal_model_weights():
+    cfg = small_stack(3)
+    a, b = G.model_weights(cfg), G.model_weights_streamed(cfg)
+    la = a.pop("layers")
+    lb = list(b.pop("layers"))
+    assert len(la) == len(lb) == 3
+    for x, y in zip(la, lb):
+        assert x.keys() == y.keys() and all(np.array_equal(x[k], y[k]) for k in x)
+    assert a.keys() == b.keys()
+    for k in a:
+        assert (a[k] is None and b[k] is None) or np.array_equal(a[k], b[k]), k
