@@ -431,30 +431,6 @@ template <int DH>
 __device__ __forceinline__ int swk(int r) { return (r / (256 / (DH * 2))) % (DH / 8); }
 __device__ __forceinline__ int swv(int e) { return (e >> 1) & 7; }
 
-// One 1-KiB global -> LDS copy: lane l's 16 bytes at sbase + voff land at LDS
-// byte lds + 16 l.  M0 (the LDS base of the copy) is saved and restored.  The
-// copies are not visible to the compiler's wait tracking: callers wait with
-// wait_loads_and_sync<N>() before reading what they wrote.
-__device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uint32_t lds) {
-  uint32_t save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(save)
-      : "s"(lds), "v"(voff), "s"(sbase)
-      : "memory");
-}
-// Wait until at most N of this wave's copies are in flight, then synchronise
-// the workgroup; the empty asm statements keep LDS reads on their side.
-template <int N>
-__device__ __forceinline__ void wait_loads_and_sync() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // This wave's share of one tile's copies: per-lane source offsets relative to
 // the tile start and the kv row / column each lane reads.
 template <int DH, int NW>
@@ -714,15 +690,6 @@ __device__ __forceinline__ void attn_tile(const char* stage, int t0, int kv1, fl
   pv_block<DH, QB, NW>(stage, lane, pf, o);
 }
 
-// Wait until at most `younger` tiles (0..2) issued after the one needed are in
-// flight, then synchronise the workgroup.
-template <int LOADS>
-__device__ __forceinline__ void wait_tiles_and_sync(int younger) {
-  if (younger >= 2) wait_loads_and_sync<2 * LOADS>();
-  else if (younger == 1) wait_loads_and_sync<LOADS>();
-  else wait_loads_and_sync<0>();
-}
-
 // PIPE: software-pipelined schedule.  Each step issues the QK MFMAs of tile
 // t + 1 before the softmax of tile t, so the matrix pipe works on the next
 // tile while the vector ALU exponentiates the current one; the output is then
@@ -763,8 +730,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const char* kbase = reinterpret_cast<const char*>(p.kc + int64_t(g) * p.L_cap * DH);
   const char* vbase = reinterpret_cast<const char*>(p.vc + int64_t(g) * DH * p.L_cap);
-  // LDS byte address of the dynamic LDS block (the copies take it in M0)
-  const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) char*)(smem)));
+  const uint32_t lds0 = lds_addr(smem);
   const int ntiles = (kv1 - kv0 + kKV - 1) / kKV;
   const bool last_partial = kv0 + ntiles * kKV > kv1;      // the last tile reaches past kv1
   const CopyPlan<DH, NW> cp = copy_plan<DH, NW>(p.L_cap, wave, lane);
@@ -813,7 +779,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
     auto stage = [&](int t) { return smem + (t % NS) * B::STAGE; };
     f32x16 scA[QB][2], scB[QB][2];
     // prologue: tile 0 landed, its scores
-    wait_tiles_and_sync<B::LOADS>(min(NS - 1, ntiles) - 1);
+    wait_groups_and_sync<B::LOADS>(min(NS - 1, ntiles) - 1);
     if (zero_last && ntiles == 1) {
       zero_vt_tail<DH, NW>(stage(0), kv0, p.L, tid);
       __syncthreads();
@@ -821,7 +787,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
     qk_block<DH, QB, NW>(stage(0), lane, qf, scA);
     // step t < ntiles - 1: scores of tile t in cur, of tile t + 1 into nxt
     auto step = [&](int t, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2]) {
-      wait_tiles_and_sync<B::LOADS>(min(NS - 3, ntiles - t - 2));   // tile t + 1 landed
+      wait_groups_and_sync<B::LOADS>(min(NS - 3, ntiles - t - 2));   // tile t + 1 landed
       // stage (t + NS - 1) % NS was last read in step t - 1, which every wave has left
       if (t + NS - 1 < ntiles) issue(t + NS - 1);
       if (zero_last && t + 1 == ntiles - 1) {
@@ -861,9 +827,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
   for (int t = 0; t < ntiles - 1; ++t) {
     // tile t landed; the min(NS - 2, ntiles - 1 - t) tiles issued after it may be in flight
     const int younger = min(NS - 2, ntiles - 1 - t);
-    if (NS >= 4 && younger >= 2) wait_loads_and_sync<2 * B::LOADS>();
-    else if (NS >= 3 && younger >= 1) wait_loads_and_sync<B::LOADS>();
-    else wait_loads_and_sync<0>();
+    if (NS >= 4 && younger >= 2) wait_copies_and_sync<2 * B::LOADS>();
+    else if (NS >= 3 && younger >= 1) wait_copies_and_sync<B::LOADS>();
+    else wait_copies_and_sync<0>();
     // stage (t + NS - 1) % NS was last read in iteration t - 1, which every wave has left
     if (t + NS - 1 < ntiles) issue(t + NS - 1);
     attn_tile<DH, QB, NW, false>(smem + (t % NS) * B::STAGE, kv0 + t * kKV, kv1, p.sl2, lane,
@@ -871,7 +837,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
   }
   {                                                         // the last tile
     const int t = ntiles - 1, t0 = kv0 + t * kKV;
-    wait_loads_and_sync<0>();
+    wait_copies_and_sync<0>();
     char* stage = smem + (t % NS) * B::STAGE;
     if (last_partial) {
       if (t0 + kKV > p.L) {

@@ -21,12 +21,9 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// float -> bfloat16, round to nearest even; NaN stays a quiet NaN.
+// float -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32); NaN stays NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
@@ -106,6 +103,45 @@ __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
+}
+
+// ---- global -> LDS copies (gfx950 global_load_lds_dwordx4)
+// One 1-KiB copy: lane l's 16 bytes at sbase + voff land at LDS byte
+// lds + 16 l.  M0 (the LDS base of the copy) is saved and restored.  The
+// copies are not visible to the compiler's wait tracking: callers wait with
+// wait_copies_and_sync<N>() (or wait_groups_and_sync) before reading what
+// they wrote, and must issue no other vector memory operation in between
+// whose completion they rely on.
+__device__ __forceinline__ void lds_copy16(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(lds), "v"(voff), "s"(sbase)
+      : "memory");
+}
+// Wait until at most N of this wave's copies are in flight, then synchronise
+// the workgroup; the empty asm statements keep LDS reads on their side.
+template <int N>
+__device__ __forceinline__ void wait_copies_and_sync() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// Copies are issued in groups of PER (one pipeline stage per wave): wait until
+// at most `younger` (0..2) groups issued after the one needed are in flight.
+template <int PER>
+__device__ __forceinline__ void wait_groups_and_sync(int younger) {
+  if (younger >= 2) wait_copies_and_sync<2 * PER>();
+  else if (younger == 1) wait_copies_and_sync<PER>();
+  else wait_copies_and_sync<0>();
+}
+// LDS byte address of a dynamic LDS block (the copies take it in M0)
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return uint32_t(size_t((__attribute__((address_space(3))) const char*)(p)));
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

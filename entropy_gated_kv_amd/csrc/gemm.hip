@@ -435,6 +435,137 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(GP p) {
     }
 }
 
+// ============================================================================ tiled, bf16
+// 128 x 128 output tiles, 64 k per stage, 2 x 2 waves of 64 x 64.  The A and
+// W tiles (128 rows of 128 B each) go global -> LDS with
+// global_load_lds_dwordx4 through NS stages, NS - 1 stages ahead of the MFMAs,
+// one workgroup barrier per stage; the eight 16-byte chunks of each LDS row are
+// XOR-swizzled by (row / 2) mod 8, which makes the fragment reads of 32
+// consecutive rows conflict-free.  Rows past the selected count read the last
+// selected row and columns past N read the last weight row (finite data whose
+// products are never stored).  Requires every copy offset to fit 32 bits
+// (launch_typed checks and otherwise uses the kernel above).
+constexpr int kTBK = 64;                     // k per stage
+constexpr int kTRowB = kTBK * 2;             // bytes of one tile row (128)
+
+__device__ __forceinline__ int tswz(int r) { return (r >> 1) & 7; }
+
+template <bool DUAL, int EPI, int NS>
+__global__ __launch_bounds__(kThreads) void gemm_tiled_bf16_kernel(GP p) {
+  constexpr int NB = DUAL ? 2 : 1;                       // weight matrices
+  constexpr int TILE = kBM * kTRowB;                     // 16 KiB
+  constexpr int STAGE = TILE * (1 + NB);
+  constexpr int CPW = TILE / 1024 / 4;                   // copies per wave per tile (4)
+  constexpr int LOADS = CPW * (1 + NB);                  // copies per wave per stage
+  static_assert(NS >= 2 && NS <= 4, "two to four stages");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int n_rows = min(*p.n_rows, p.max_rows);
+  if (n_rows <= kSkinnyMaxRows) return;                  // the skinny kernel handles it
+  const int tiles_m = (p.max_rows + kBM - 1) / kBM;
+  const int tiles_n = (p.N + kBN - 1) / kBN;
+  // XCD-aware order: each XCD gets a contiguous run of tiles, row tiles
+  // fastest, so a weight tile is shared through that XCD's L2.
+  const int total = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int per_xcd = (total + 7) / 8;
+  const int t = (b % 8) * per_xcd + b / 8;
+  if (t >= total) return;
+  const int tm = t % tiles_m, tn = t / tiles_m;
+  const int row0 = tm * kBM, col0 = tn * kBN;
+  if (row0 >= n_rows) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
+  const uint32_t lds0 = lds_addr(smem);
+
+  // copy plan: copy i of this wave fills LDS rows ii*8 .. ii*8+7 of a tile
+  // (ii = wave * CPW + i); lane -> row ii*8 + lane/8, slot lane%8, which holds
+  // chunk slot ^ tswz(row) of that row
+  uint32_t aoff[CPW], woff[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int r = (wave * CPW + i) * 8 + lane / 8;
+    const int c = (lane % 8) ^ tswz(r);
+    const int gr = min(row0 + r, n_rows - 1);
+    const int ar = (p.a_idx != nullptr) ? p.a_idx[gr] : gr;
+    aoff[i] = (uint32_t(ar) * uint32_t(p.lda) + uint32_t(c) * 8) * 2u;
+    const int gn = min(col0 + r, p.N - 1);
+    woff[i] = (uint32_t(gn) * uint32_t(p.K) + uint32_t(c) * 8) * 2u;
+  }
+  const void* Wm[2] = {p.W, DUAL ? p.W2 : p.W};
+  auto issue = [&](int it) {
+    const uint32_t st = lds0 + (it % NS) * STAGE;
+    const uint32_t kb = uint32_t(it) * kTBK * 2u;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) lds_copy16(p.A, aoff[i] + kb, st + (wave * CPW + i) * 1024);
+#pragma unroll
+    for (int w = 0; w < NB; ++w)
+#pragma unroll
+      for (int i = 0; i < CPW; ++i)
+        lds_copy16(Wm[w], woff[i] + kb, st + (1 + w) * TILE + (wave * CPW + i) * 1024);
+  };
+
+  // fragment offsets within a stage: block i/j (32 rows), k-step s (16 k = chunks 2s, 2s+1)
+  int afr[2], wfr[2], asw[2], wsw[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ra = wr + i * 32 + (lane & 31), rw = wc + i * 32 + (lane & 31);
+    afr[i] = ra * kTRowB; asw[i] = tswz(ra);
+    wfr[i] = TILE + rw * kTRowB; wsw[i] = tswz(rw);
+  }
+
+  f32x16 acc[NB][2][2];
+#pragma unroll
+  for (int w = 0; w < NB; ++w)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[w][i][j] = f32x16{};
+
+  const int nit = p.K / kTBK;
+#pragma unroll
+  for (int it = 0; it < NS - 1; ++it)
+    if (it < nit) issue(it);
+  for (int it = 0; it < nit; ++it) {
+    wait_groups_and_sync<LOADS>(min(NS - 2, nit - 1 - it));     // stage it landed
+    // stage (it + NS - 1) % NS was last read in iteration it - 1, which every wave has left
+    if (it + NS - 1 < nit) issue(it + NS - 1);
+    const char* st = smem + (it % NS) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < kTBK / 16; ++ks) {
+      u32x4 a[2], bw[NB][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const u32x4*>(st + afr[i] + (((2 * ks + h) ^ asw[i]) << 4));
+#pragma unroll
+      for (int w = 0; w < NB; ++w)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bw[w][j] = *reinterpret_cast<const u32x4*>(st + w * TILE + wfr[j] + (((2 * ks + h) ^ wsw[j]) << 4));
+#pragma unroll
+      for (int w = 0; w < NB; ++w)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) Mma<bf16_t>::run(acc[w][i][j], a[i], bw[w][j]);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = col0 + wc + j * 32 + (lane & 31);
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = row0 + wr + i * 32 + acc_row(e, lane);
+        if (r < n_rows) epilogue<bf16_t, EPI>(p, r, n, acc[0][i][j][e], DUAL ? acc[NB - 1][i][j][e] : 0.f);
+      }
+    }
+}
+
 // ---------------------------------------------------------------------------- planning
 int mbx_of(int max_rows) { return max_rows <= 32 ? 2 : 8; }
 
@@ -526,6 +657,24 @@ hipError_t launch_typed(const GemmArgs& a, void* ws, hipStream_t s, bool allow_s
 
   const int tiles = ((a.max_rows + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
   const unsigned grid = unsigned((tiles + 7) / 8 * 8);
+  if constexpr (sizeof(T) == 2) {
+    // the direct-to-LDS kernel takes 32-bit copy offsets
+    const bool fits = uint64_t(a.max_rows + 128) * uint64_t(a.lda) * 2u < (uint64_t(1) << 32) &&
+                      uint64_t(a.N) * uint64_t(a.K) * 2u < (uint64_t(1) << 32) && a.a_idx == nullptr;
+    if (fits) {
+      // two stages (64 KiB: two workgroups per CU) measured fastest for the
+      // single-weight epilogues; the SwiGLU pair keeps three (one per CU)
+      const size_t stage = size_t(kBM) * kTRowB * (dual ? 3 : 2);
+      switch (a.epi) {
+        case Epi::kStore: hipLaunchKernelGGL((gemm_tiled_bf16_kernel<false, 0, 2>), dim3(grid), dim3(kThreads), 2 * stage, s, p); break;
+        case Epi::kQKV: hipLaunchKernelGGL((gemm_tiled_bf16_kernel<false, 1, 2>), dim3(grid), dim3(kThreads), 2 * stage, s, p); break;
+        case Epi::kResidual: hipLaunchKernelGGL((gemm_tiled_bf16_kernel<false, 2, 2>), dim3(grid), dim3(kThreads), 2 * stage, s, p); break;
+        case Epi::kSwiGLU: hipLaunchKernelGGL((gemm_tiled_bf16_kernel<true, 3, 3>), dim3(grid), dim3(kThreads), 3 * stage, s, p); break;
+        case Epi::kLogits: hipLaunchKernelGGL((gemm_tiled_bf16_kernel<false, 4, 2>), dim3(grid), dim3(kThreads), 2 * stage, s, p); break;
+      }
+      return hipGetLastError();
+    }
+  }
   const size_t lds_t = size_t(2) * kBM * ROWB * (dual ? 3 : 2);
   switch (a.epi) {
     case Epi::kStore: hipLaunchKernelGGL((gemm_tiled_kernel<T, false, 0>), dim3(grid), dim3(kThreads), lds_t, s, p); break;
