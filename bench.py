@@ -123,7 +123,7 @@ def entropy_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         "flag": int(F.item()),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic("entropy_kernel<bf16>", "entropy.hip", 1),
+                     "traffic": _traffic("entropy_partials_kernel<bf16>", "entropy.hip", 1),
                      "kernel": "entropy pass: entropy_partials_kernel<bf16> + combine + decide"},
     }
     _log(f"entropy pass: {kern_ms * 1e3:.1f} us/launch, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
