@@ -3,7 +3,8 @@
 Q and the refreshed cache rows within 2e-3 (fp32) / 2e-2 (bf16) abs and rel;
 cache rows not selected must be bitwise unchanged (sentinel-filled caches).
 Row counts cover 1..4 row blocks of the skinny kernel, the 128-row boundary,
-the tiled kernel with a ragged last tile, and the LLaDA-shaped full size.
+the tiled kernel with a ragged last tile (in each of its tile
+configurations), and the LLaDA-shaped full size.
 """
 import numpy as np
 import pytest
@@ -57,6 +58,18 @@ def test_bf16_gqa_shapes(n, dh):
     Lc = 520
     rows = np.sort(np.random.default_rng(n + dh).choice(Lc, n, replace=False))
     run_case("bf16", 512, 8, 2, dh, Lc, rows, seed=n + dh)
+
+
+@pytest.mark.parametrize("consecutive", [True, False], ids=["full", "scattered"])
+@pytest.mark.parametrize("tile", ["0", "1", "2", "3"])
+def test_bf16_every_tile_config(tile, consecutive, monkeypatch):
+    """Each tile configuration of the tiled kernel (forced), with a ragged
+    last row tile and column tile; consecutive rows take the packed
+    transposed-V stores."""
+    monkeypatch.setenv("EC_GEMM_TILE", tile)
+    Lc, n = 644, 600
+    rows = np.arange(n) + 4 if consecutive else np.sort(np.random.default_rng(9).choice(Lc, n, replace=False))
+    run_case("bf16", 512, 8, 2, 128, Lc, rows, seed=int(tile) + 40)
 
 
 @pytest.mark.parametrize("n", [96, 1024])

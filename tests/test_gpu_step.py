@@ -164,7 +164,11 @@ def test_bf16_single_layer_teacher_forced():
     assert n_partial > 3 and ties <= 2
 
 
-def test_bf16_two_layer_stack_teacher_forced():
+@pytest.mark.parametrize("tile", [None, "0", "1", "2", "3"])
+def test_bf16_two_layer_stack_teacher_forced(tile, monkeypatch):
+    # full steps (160 rows) run the tiled GEMMs: the chosen tile, then each forced
+    if tile is not None:
+        monkeypatch.setenv("EC_GEMM_TILE", tile)
     ties, n_partial = check_teacher_forced(gpu_stack_cfg(), 24, 1.0)
     assert n_partial > 3 and ties <= 2
 
