@@ -196,18 +196,13 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
     n_ev = 2 * len(PHASES)
 
     def event_set(only_lm):
-        evs = []
+        """Events for one step: every phase, or (only_lm) the LM head alone."""
+        evs = [None] * n_ev
         for k in range(n_ev):
-            e = torch.cuda.Event(enable_timing=True)
-            e.record()                      # materialise the event handle
-            evs.append(e)
-        if only_lm:                         # other phases share one scratch pair
-            scratch = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            for e in scratch:
-                e.record()
-            for k in range(n_ev):
-                if k // 2 != LM:
-                    evs[k] = scratch[k % 2]
+            if only_lm and k // 2 != LM:
+                continue
+            evs[k] = torch.cuda.Event(enable_timing=True)
+            evs[k].record()                 # materialise the event handle
         return evs
 
     reset()
@@ -215,22 +210,22 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
     reset()
     torch.cuda.synchronize()
     timed_events = [event_set(True) for _ in range(steps)]
-    flags = torch.zeros(steps, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run(steps, tau, timed_events, flags)
+    run(steps, tau, timed_events)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fl = flags.cpu().numpy()
     lm_ms = float(np.mean([ev[2 * LM].elapsed_time(ev[2 * LM + 1]) for ev in timed_events]))
 
-    # untimed pass with every phase bracketed, for the breakdown
+    # untimed replay of the same (deterministic) steps with every phase
+    # bracketed, for the breakdown and the step modes
     reset()
     torch.cuda.synchronize()
-    n_bd = min(steps, len(sched))
-    bd_events = [event_set(False) for _ in range(n_bd)]
-    run(n_bd, tau, bd_events)
+    bd_events = [event_set(False) for _ in range(steps)]
+    flags = torch.zeros(steps, dtype=torch.int32, device="cuda")
+    run(steps, tau, bd_events, flags)
     torch.cuda.synchronize()
+    fl = flags.cpu().numpy()
     phase_ms = {}
     for k, name in enumerate(PHASES):
         if name == "ffn":

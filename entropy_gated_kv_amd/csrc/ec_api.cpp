@@ -236,8 +236,8 @@ StepLayout step_layout(const ec_model* m, int32_t max_block, void* ws) {
 struct PhaseTimer {
   hipEvent_t* ev;
   hipStream_t s;
-  hipError_t begin(int p) const { return ev ? hipEventRecord(ev[2 * p], s) : hipSuccess; }
-  hipError_t end(int p) const { return ev ? hipEventRecord(ev[2 * p + 1], s) : hipSuccess; }
+  hipError_t begin(int p) const { return (ev && ev[2 * p]) ? hipEventRecord(ev[2 * p], s) : hipSuccess; }
+  hipError_t end(int p) const { return (ev && ev[2 * p + 1]) ? hipEventRecord(ev[2 * p + 1], s) : hipSuccess; }
 };
 
 }  // namespace
@@ -285,9 +285,6 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
       (int64_t(m->V) * int64_t(esize(m->dtype))) % 16 != 0 ||
       (int64_t(m->L_cap) * int64_t(esize(m->dtype))) % 16 != 0)
     return EC_E_ALIGN;
-  if (phase_events)
-    for (int i = 0; i < 2 * EC_PHASE_COUNT; ++i)
-      if (!phase_events[i]) return EC_E_NULL;
   const int32_t max_block = c->block_len;
   const StepLayout s = step_layout(m, max_block, ws);
   if (ws_bytes < s.total) return EC_E_WORKSPACE;

@@ -86,7 +86,7 @@ struct GemmArgs {
   const int32_t* scale_pos = nullptr;
 };
 size_t gemm_ws_bytes(const GemmArgs& a);
-// Reduction dimensions (d, Hq*dh, d_ffn) must be multiples of this (256 bf16, 128 fp32).
+// Reduction dimensions (d, Hq*dh, d_ffn) must be multiples of this (128 bf16, 64 fp32).
 int gemm_k_multiple(int dtype);
 hipError_t launch_gemm_rows(const GemmArgs& a, void* ws, hipStream_t s);
 

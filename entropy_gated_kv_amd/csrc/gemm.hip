@@ -119,9 +119,12 @@ __device__ __forceinline__ int acc_row(int j, int lane) { return 8 * (j >> 2) + 
 // MFMA 16x16x32 bf16 / 16x16x4 fp32.  A wave owns 16 weight rows (output
 // columns).  Lane (n = l%16, g = l/16) loads, per iteration, NV vectors of
 // 16 B at k-offset (v*4 + g)*VPL, v = 0..NV-1: the four lanes of a row read
-// 64 contiguous bytes per instruction and the wave walks 512 B of each of its
+// 64 contiguous bytes per instruction and the wave walks 256 B of each of its
 // 16 rows per iteration -- the access pattern that keeps HBM streaming at
 // ~5.5 TB/s on this part, where 32 rows x 32 B per instruction reach ~3 TB/s.
+// Four vectors per iteration rather than eight: the smaller W ring and A
+// stage leave registers for two waves per SIMD at up to 128 rows (one wave
+// with eight), which measured 25% faster at 96 rows.
 // For bf16 that is exactly the MFMA's own operand layout (k = 32v + 8g + i);
 // for fp32 each 16-B vector feeds four 16x16x4 MFMAs.  W fragments sit in a
 // ring of three register buffers (loads run two iterations ahead); the
@@ -143,7 +146,7 @@ template <> struct Mma16<float> {
   }
 };
 
-constexpr int kNV = 8;                       // 16-B vectors per lane per iteration
+constexpr int kNV = 4;                       // 16-B vectors per lane per iteration
 constexpr int kSkinnyNT = 64;                // output columns per workgroup
 template <typename T> constexpr int skit() { return kNV * 4 * (16 / int(sizeof(T))); }  // k per iteration
 

@@ -188,10 +188,10 @@ def ec_step(model: ec_model, state: ec_state, cfg: ec_step_cfg, ws, phase_events
     ev = None
     if phase_events is not None:
         handles = []
-        for e in phase_events:
-            if not e.cuda_event:          # torch creates events on first record
+        for e in phase_events:            # None: that record is skipped
+            if e is not None and not e.cuda_event:   # torch creates events on first record
                 e.record()
-            handles.append(e.cuda_event)
+            handles.append(None if e is None else e.cuda_event)
         arr = (C.c_void_p * len(handles))(*handles)
         ev = C.cast(arr, C.c_void_p)
     _check("ec_step", load().ec_step(C.byref(model), C.byref(state), C.byref(cfg), _ptr(ws),

@@ -148,7 +148,7 @@ int32_t ec_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32
  * outputs are rounded to dtype (nearest even).  rows[r] < L_cap, distinct.
  * ws holds split-K partial sums: ec_kv_refresh_workspace_bytes(...) bytes
  * (may be 0, then ws may be NULL).
- * Supported: d a multiple of 256 (bf16) or 128 (fp32), dh in {32, 64, 128},
+ * Supported: d a multiple of 128 (bf16) or 64 (fp32), dh in {32, 64, 128},
  * Hq % Hkv == 0.
  * Errors: EC_E_NULL, EC_E_SHAPE, EC_E_DTYPE, EC_E_ALIGN, EC_E_WORKSPACE,
  * EC_E_UNSUPPORTED, EC_E_LAUNCH.
@@ -279,9 +279,10 @@ typedef struct ec_step_cfg {
 } ec_step_cfg;
 
 /* Optional per-phase timing: when non-NULL, phase_events holds 2*EC_PHASE_COUNT
- * created events and ec_step records events[2*i] and events[2*i+1] around
+ * event handles and ec_step records events[2*i] and events[2*i+1] around
  * phase i on the stream.  Per-layer phases (QKV, attention, O-projection, FFN)
- * are bracketed in the first layer only.  A NULL handle is EC_E_NULL. */
+ * are bracketed in the first layer only.  A NULL entry skips that record, so a
+ * caller can time one phase without recording events around the others. */
 enum {
   EC_PHASE_SELECT = 0, EC_PHASE_EMBED, EC_PHASE_QKV, EC_PHASE_ATTN, EC_PHASE_OPROJ,
   EC_PHASE_FFN, EC_PHASE_LMHEAD, EC_PHASE_ENTROPY, EC_PHASE_DECIDE, EC_PHASE_COUNT

@@ -75,8 +75,8 @@ def test_select_and_refresh_and_attention_checks(lib):
     assert lib.ec_select_rows(None, FAKE, 10, 0, 4, FAKE, FAKE, 16, 4, FAKE, FAKE, None) == -1
     assert lib.ec_kv_refresh(FAKE, 256, FAKE, FAKE, 4, FAKE, 256, 4, 4, 48, 1, FAKE, FAKE, FAKE,
                              16, None, 0, None) == -7              # head dim 48
-    assert lib.ec_kv_refresh(FAKE, 128, FAKE, FAKE, 4, FAKE, 128, 4, 4, 32, 1, FAKE, FAKE, FAKE,
-                             16, None, 0, None) == -7              # bf16 needs d % 256 == 0
+    assert lib.ec_kv_refresh(FAKE, 64, FAKE, FAKE, 4, FAKE, 64, 4, 4, 32, 1, FAKE, FAKE, FAKE,
+                             16, None, 0, None) == -7              # bf16 needs d % 128 == 0
     assert lib.ec_kv_refresh(FAKE, 128, FAKE, FAKE, 4, FAKE, 128, 4, 3, 32, 1, FAKE, FAKE, FAKE,
                              16, None, 0, None) == -2              # Hq % Hkv
     assert lib.ec_kv_refresh(FAKE, 128, FAKE, FAKE, 4, FAKE, 128, 4, 4, 32, 2, FAKE, FAKE, FAKE,
