@@ -176,7 +176,7 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         ds.history_len.zero_()
         ds.full_flag.fill_(1)
 
-    def run(n_steps, tau_, events=None, flags=None):
+    def run(n_steps, tau_, events=None, flags=None, k=cfg.k):
         i = 0
         while i < n_steps:
             for j, (bs, bl, n) in enumerate(sched):
@@ -185,7 +185,7 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
                 if flags is not None:
                     flags[i].copy_(ds.full_flag[0])
                 ev = None if events is None else events[i]
-                ds.step(tau_, cfg.k, bs, bl, n, phase_events=ev)
+                ds.step(tau_, k, bs, bl, n, phase_events=ev)
                 i += 1
             else:
                 reset()
@@ -262,21 +262,40 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
          f"partial fraction {out['partial_fraction']:.2f}; LM head {lm_ms * 1e3:.1f} us = {lm_gbs:.0f} GB/s")
     _log("phases (us, separate pass): " + ", ".join(f"{k} {v * 1e3:.1f}" for k, v in phase_ms.items()))
 
-    # tau sweep and vanilla: one whole generation each
-    sweep = {}
-    for t in (0.5, 1.0, 2.0, float("-inf")):
+    # tau sweep and vanilla, then the history length k at tau = 1: one whole
+    # generation each.  Every run also reports how many of its decoded tokens
+    # equal vanilla decoding's (a proxy, on synthetic weights, for how far
+    # reusing stale K/V moves the decisions).
+    def generation(t, k):
         reset()
         torch.cuda.synchronize()
         fl2 = torch.zeros(len(sched), dtype=torch.int32, device="cuda")
         t1 = time.perf_counter()
-        run(len(sched), t, None, fl2)
+        run(len(sched), t, None, fl2, k)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t1
-        sweep[str(t)] = {"steps_per_s": round(len(sched) / dt, 2),
-                         "partial_fraction": round(float(1.0 - fl2.float().mean().item()), 3)}
+        return ({"steps_per_s": round(len(sched) / dt, 2),
+                 "partial_fraction": round(float(1.0 - fl2.float().mean().item()), 3)},
+                ds.tokens.cpu().numpy())
+
+    vanilla, van_tok = generation(float("-inf"), cfg.k)
+    gen = np.asarray(masked, dtype=bool)                     # generated positions
+    sweep = {}
+    for t in (0.5, 1.0, 2.0):
+        rec, tok = generation(t, cfg.k)
+        rec["token_agreement_vs_vanilla"] = round(float((tok[gen] == van_tok[gen]).mean()), 4)
+        sweep[str(t)] = rec
+    sweep["-inf"] = vanilla
     out["tau_sweep"] = sweep
     out["speedup_vs_vanilla_at_tau_1"] = round(sweep["1.0"]["steps_per_s"] / sweep["-inf"]["steps_per_s"], 3)
     _log(f"tau sweep: {sweep}")
+    kab = {}
+    for k in (1, 16, 64, 256):
+        rec, tok = generation(1.0, k)
+        rec["token_agreement_vs_vanilla"] = round(float((tok[gen] == van_tok[gen]).mean()), 4)
+        kab[str(k)] = rec
+    out["k_ablation_tau_1"] = kab
+    _log(f"k ablation (tau 1.0): {kab}")
     if cpu_baseline:
         out["cpu_baseline"] = step_cpu_baseline(cfg, w, toks, masked, sched, tau)
     return out
@@ -621,6 +640,7 @@ def main() -> int:
             "decision_overhead_frac": round(res["decision_overhead_frac"], 4),
             "tau_sweep": res["tau_sweep"],
             "speedup_vs_vanilla_at_tau_1": res["speedup_vs_vanilla_at_tau_1"],
+            "k_ablation_tau_1": res["k_ablation_tau_1"],
         }
         if "cpu_baseline" in res:
             line["cpu_baseline"] = res["cpu_baseline"]

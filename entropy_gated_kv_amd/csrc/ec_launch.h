@@ -9,12 +9,12 @@ namespace ec {
 
 // ---- entropy pass ----------------------------------------------------------
 struct EntropyPartial {   // online softmax statistics of one V segment
-  float m;                // max over the segment (NaN never; +/-inf possible)
+  float m;                // max over the segment (+/-inf possible)
   float z;                // sum 2^u, u = (x - m) log2(e)
   float s2;               // sum 2^u * u
   int32_t idx;            // lowest index holding m (INT32_MAX: none)
 };
-// Rows are split into segments of 2048 16-byte vectors (16384 bf16 / 8192 fp32).
+// Rows are split into segments of 512 16-byte vectors (4096 bf16 / 2048 fp32).
 int entropy_segments(int64_t V, int dtype);
 size_t entropy_ws_bytes(int64_t n_rows, int64_t V, int dtype);
 
