@@ -296,6 +296,30 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         kab[str(k)] = rec
     out["k_ablation_tau_1"] = kab
     _log(f"k ablation (tau 1.0): {kab}")
+
+    # KV drift on full steps (untimed): the E that triggered each full step
+    # next to the Value drift that step measured
+    reset()
+    ds.enable_drift()
+    pairs = []
+    e_prev = None
+    for bs, bl, nn in sched:
+        full = int(ds.full_flag.item())
+        ds.step(tau, cfg.k, bs, bl, nn)
+        if full and e_prev is not None:
+            dm_, dx_ = ds.kv_drift[0].tolist()
+            pairs.append((e_prev, dm_, dx_))
+        e_prev = float(ds.e_max.item())
+    ds.struct.kv_drift = None
+    if pairs:
+        a = np.array(pairs)
+        r = float(np.corrcoef(a[:, 0], a[:, 1])[0, 1]) if len(a) > 2 else float("nan")
+        out["kv_drift_tau_1"] = {
+            "full_steps": len(pairs), "drift_mean": round(float(a[:, 1].mean()), 5),
+            "drift_max": round(float(a[:, 2].max()), 5), "corr_trigger_E_vs_mean_drift": round(r, 4),
+            "note": "1 - cos of stale vs recomputed Value vectors per position (layer 0); "
+                    "synthetic weights, so the correlation is not the pages' observation"}
+        _log(f"kv drift: {out['kv_drift_tau_1']}")
     if cpu_baseline:
         out["cpu_baseline"] = step_cpu_baseline(cfg, w, toks, masked, sched, tau)
     return out
@@ -641,6 +665,7 @@ def main() -> int:
             "tau_sweep": res["tau_sweep"],
             "speedup_vs_vanilla_at_tau_1": res["speedup_vs_vanilla_at_tau_1"],
             "k_ablation_tau_1": res["k_ablation_tau_1"],
+            "kv_drift_tau_1": res.get("kv_drift_tau_1"),
         }
         if "cpu_baseline" in res:
             line["cpu_baseline"] = res["cpu_baseline"]

@@ -188,6 +188,7 @@ struct StepLayout {
   void* attn_ws = nullptr;
   void* gemm_ws = nullptr;
   void* ent_ws = nullptr;
+  void* drift_ws = nullptr;   // stale Value cache of one layer + per-position distances
   int32_t* cand_pos = nullptr;
   int32_t* cand_idx = nullptr;
   int32_t* n_cand = nullptr;
@@ -226,6 +227,7 @@ StepLayout step_layout(const ec_model* m, int32_t max_block, void* ws) {
   if (m->w_lm) need(ec::Epi::kLogits, max_block, m->V, m->d);
   s.gemm_ws = c.take<void>(gws);
   s.ent_ws = c.take<void>(ec::entropy_ws_bytes(max_block, m->V, m->dtype));
+  s.drift_ws = c.take<void>(ec::value_drift_ws_bytes(m->dtype, m->Hkv * m->dh, m->L_cap));
   s.cand_pos = c.take<int32_t>(size_t(max_block) * 4);
   s.cand_idx = c.take<int32_t>(size_t(max_block) * 4);
   s.n_cand = c.take<int32_t>(4);
@@ -285,6 +287,8 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
       (int64_t(m->V) * int64_t(esize(m->dtype))) % 16 != 0 ||
       (int64_t(m->L_cap) * int64_t(esize(m->dtype))) % 16 != 0)
     return EC_E_ALIGN;
+  for (int l = 0; l < m->n_layers; ++l)
+    if (!al16(st->k_cache[l]) || !al16(st->v_cache[l])) return EC_E_ALIGN;
   const int32_t max_block = c->block_len;
   const StepLayout s = step_layout(m, max_block, ws);
   if (ws_bytes < s.total) return EC_E_WORKSPACE;
@@ -318,7 +322,14 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
     g.max_rows = L; g.W = ly.w_qkv; g.N = (m->Hq + 2 * m->Hkv) * m->dh; g.K = m->d;
     g.rows = st->rows; g.q_out = s.q; g.k_cache = st->k_cache[l]; g.v_cache = st->v_cache[l];
     g.Hq = m->Hq; g.Hkv = m->Hkv; g.dh = m->dh; g.L_cap = m->L_cap;
+    const int vrows = m->Hkv * m->dh;
+    if (st->kv_drift)   // full steps only (the kernels read the flag): the stale Value cache
+      EC_TRY(ec::launch_value_drift_snapshot(dt, st->full_flag, st->v_cache[l], vrows, L, m->L_cap,
+                                             s.drift_ws, stream));
     EC_TRY(ec::launch_gemm_rows(g, s.gemm_ws, stream));
+    if (st->kv_drift)
+      EC_TRY(ec::launch_value_drift(dt, st->full_flag, st->v_cache[l], vrows, L, m->L_cap, s.drift_ws,
+                                    st->kv_drift + 2 * l, stream));
     if (first) { EC_TRY(tm.end(EC_PHASE_QKV)); EC_TRY(tm.begin(EC_PHASE_ATTN)); }
 
     ec::AttnArgs a;

@@ -90,6 +90,17 @@ size_t gemm_ws_bytes(const GemmArgs& a);
 int gemm_k_multiple(int dtype);
 hipError_t launch_gemm_rows(const GemmArgs& a, void* ws, hipStream_t s);
 
+// ---- KV drift of a full step (diagnostic) ------------------------------------------
+// Workspace: a copy of one layer's transposed Value cache [nrow = Hkv * dh, L_cap]
+// plus L_cap floats.  Both launches exit at once unless *flag (the step's mode) is 1.
+size_t value_drift_ws_bytes(int dtype, int nrow, int L_cap);
+// Before the layer's refresh: copy columns [0, L) of the Value cache into ws.
+hipError_t launch_value_drift_snapshot(int dtype, const int32_t* flag, const void* v_cache, int nrow,
+                                       int L, int L_cap, void* ws, hipStream_t s);
+// After it: out[0] = mean, out[1] = max over positions of 1 - cos(stale, fresh).
+hipError_t launch_value_drift(int dtype, const int32_t* flag, const void* v_cache, int nrow, int L,
+                              int L_cap, void* ws, float* out, hipStream_t s);
+
 // ---- bidirectional attention -----------------------------------------------------
 struct AttnArgs {
   int dtype = 0;

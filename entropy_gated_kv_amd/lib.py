@@ -19,6 +19,7 @@ EC_F32, EC_BF16 = 0, 1
 PHASES = ("select", "embed", "qkv", "attn", "oproj", "ffn", "lmhead", "entropy", "decide")
 
 _lib: Optional[C.CDLL] = None
+ABI_VERSION = 2                  # EC_ABI_VERSION of include/ec.h
 
 
 class EcError(RuntimeError):
@@ -49,7 +50,7 @@ class ec_state(C.Structure):
                 ("v_cache", C.POINTER(C.c_void_p)), ("rows", C.c_void_p), ("n_rows", C.c_void_p),
                 ("logits", C.c_void_p), ("row_entropy", C.c_void_p), ("row_argmax", C.c_void_p),
                 ("row_top1", C.c_void_p), ("chosen", C.c_void_p), ("n_chosen", C.c_void_p),
-                ("e_max", C.c_void_p)]
+                ("e_max", C.c_void_p), ("kv_drift", C.c_void_p)]
 
 
 class ec_step_cfg(C.Structure):
@@ -92,6 +93,8 @@ def load(path: Optional[str] = None) -> C.CDLL:
             f = getattr(lib, name)
             f.restype = res
             f.argtypes = args
+        if lib.ec_abi_version() != ABI_VERSION:   # the struct layouts below must match ec.h
+            raise RuntimeError(f"{p}: ABI version {lib.ec_abi_version()}, this binding expects {ABI_VERSION}")
         _lib = lib
     return _lib
 

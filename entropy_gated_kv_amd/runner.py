@@ -96,6 +96,7 @@ class DeviceSequence:
         self.chosen = torch.zeros(max_block, dtype=i32, device=dev)
         self.n_chosen = torch.zeros(1, dtype=i32, device=dev)
         self.e_max = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.kv_drift = None                      # enable_drift(): [n_layers, 2] on full steps
         nbytes = L.ec_step_workspace_bytes(model.struct, max_block)
         if nbytes == 0:
             raise RuntimeError("ec_step_workspace_bytes rejected the model shape")
@@ -113,7 +114,15 @@ class DeviceSequence:
         s.row_entropy, s.row_argmax = self.row_entropy.data_ptr(), self.row_argmax.data_ptr()
         s.row_top1, s.chosen = self.row_top1.data_ptr(), self.chosen.data_ptr()
         s.n_chosen, s.e_max = self.n_chosen.data_ptr(), self.e_max.data_ptr()
+        s.kv_drift = None
         self.struct = s
+
+    def enable_drift(self):
+        """Have full steps report each layer's Value drift (mean, max of 1 - cos)."""
+        import torch
+        self.kv_drift = torch.full((len(self.k_cache), 2), float("nan"), dtype=torch.float32,
+                                   device="cuda")
+        self.struct.kv_drift = self.kv_drift.data_ptr()
 
     def step(self, tau: float, k: int, block_start: int, block_len: int, n_unmask: int,
              phase_events=None) -> None:

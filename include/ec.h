@@ -54,7 +54,7 @@ const char* ec_status_string(int32_t status);
 
 /* ABI revision of this header; bumped on any signature or struct change. */
 int32_t ec_abi_version(void);
-#define EC_ABI_VERSION 1
+#define EC_ABI_VERSION 2
 
 /* --------------------------------------------------------------------------
  * Entropy pass (a1) and decision (a2).
@@ -268,6 +268,15 @@ typedef struct ec_state {
   int32_t* chosen;            /* [max_block] positions, ascending          */
   int32_t* n_chosen;          /* [1]                                       */
   float* e_max;               /* [1]                                       */
+  /* Optional diagnostic, or NULL: [n_layers][2] device float32.  On a full
+   * step, layer l's entries become the mean and the maximum over positions
+   * p < L of 1 - cos(stale_p, fresh_p), where stale_p / fresh_p are position
+   * p's Value vector (concatenated over the KV heads) before and after the
+   * step's refresh; positions with an all-zero vector are left out (NaN when
+   * none is left).  Partial steps leave it unchanged.  EntropyCache, Chinese
+   * summary page §2.1 and Portuguese page §2: the entropy of decoded tokens
+   * tracks this drift of the Value vectors.  Needs 16-byte aligned caches. */
+  float* kv_drift;
 } ec_state;
 
 typedef struct ec_step_cfg {

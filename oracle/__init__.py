@@ -17,7 +17,8 @@ Sources (cited by section, never by line):
   * "EntropyCache (pt)": the Portuguese-language page on the same paper
     (gist.science/pt/paper/2603.18489).  Technical summary §1 (problem:
     bidirectional attention, full forward per step) and §2 (methodology:
-    skip-or-recompute decision, decode history of the k most recent tokens).
+    skip-or-recompute decision, decode history of the k most recent tokens,
+    the observation that entropy predicts the KV drift).
 
 Where the pages leave a step open the oracle takes one stated reading; every
 reading is listed in the project's design notes and repeated at the function
@@ -34,5 +35,6 @@ from .entropy import (softmax_entropy, row_stats, max_entropy, decide, entropy_m
                       choose)
 from .selection import select_rows, candidates  # noqa: F401
 from .layers import linear, kv_refresh, bidir_attention, rmsnorm, swiglu  # noqa: F401
+from .drift import cosine_distance, value_drift  # noqa: F401
 from .step import (Model, State, StepTrace, step, step_external, generate, init_state,  # noqa: F401
                    forward_rows)

@@ -29,6 +29,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
+from .drift import value_drift
 from .entropy import choose, decide, max_entropy, row_stats
 from .layers import bidir_attention, kv_refresh, linear, rmsnorm, swiglu
 from .rounding import to_storage
@@ -94,6 +95,7 @@ class StepTrace:
     E: float
     flag_next: int
     x_cand: Optional[np.ndarray] = None   # final activations of the candidate rows
+    drift: Optional[np.ndarray] = None    # full steps: per layer (mean, max) Value drift
 
 
 def init_state(model: Model, tokens, masked) -> State:
@@ -105,10 +107,13 @@ def init_state(model: Model, tokens, masked) -> State:
                  [], 1, K, V)
 
 
-def forward_rows(model: Model, state: State, rows: np.ndarray) -> np.ndarray:
+def forward_rows(model: Model, state: State, rows: np.ndarray,
+                 drift: Optional[list] = None) -> np.ndarray:
     """Run every layer over the selected rows, refreshing their K/V in each cache.
 
     Returns the final activations of those rows (after the final norm, if any).
+    When `drift` is a list, each layer's (mean, max) Value drift between the
+    cache before and after its refresh is appended to it (oracle.drift).
     """
     dt = model.dtype
     n = len(rows)
@@ -116,8 +121,11 @@ def forward_rows(model: Model, state: State, rows: np.ndarray) -> np.ndarray:
     scale = 1.0 / math.sqrt(model.dh)
     for l, lw in enumerate(model.layers):
         a = to_storage(rmsnorm(x, lw["norm_attn"], model.eps), dt) if model.d_ffn else x
+        stale = state.V[l].copy() if drift is not None else None
         q = kv_refresh(a, rows, lw["w_qkv"], state.K[l], state.V[l], model.n_q, model.n_kv,
                        model.dh, dt)
+        if drift is not None:
+            drift.append(value_drift(stale, state.V[l]))
         o = to_storage(bidir_attention(q, state.K[l], state.V[l], scale), dt)
         x = to_storage(x + linear(o.reshape(n, model.n_q * model.dh), lw["w_o"]), dt)
         if model.d_ffn:
@@ -130,11 +138,14 @@ def forward_rows(model: Model, state: State, rows: np.ndarray) -> np.ndarray:
 
 
 def step(model: Model, state: State, tau: float, k: int, block_start: int, block_len: int,
-         n_unmask: int, keep_logits: bool = True) -> StepTrace:
-    """One denoising step; mutates `state` and returns what the step computed."""
+         n_unmask: int, keep_logits: bool = True, drift: bool = False) -> StepTrace:
+    """One denoising step; mutates `state` and returns what the step computed.
+
+    drift: on a full step, also report each layer's Value drift (oracle.drift)."""
     flag_used = state.flag
     rows = select_rows(flag_used, state.masked, block_start, block_len, state.history, k)
-    x = forward_rows(model, state, rows)
+    dl = [] if (drift and flag_used) else None
+    x = forward_rows(model, state, rows, dl)
     cand = candidates(state.masked, block_start, block_len)
     ci = np.searchsorted(rows, cand)
     z = linear(x[ci], model.w_lm)
@@ -153,7 +164,8 @@ def step(model: Model, state: State, tau: float, k: int, block_start: int, block
     E = max_entropy(H, pick)
     state.flag = decide(E, tau)
     return StepTrace(flag_used, rows, cand, z if keep_logits else None, H, A, P, chosen, E,
-                     state.flag, x[ci] if keep_logits else None)
+                     state.flag, x[ci] if keep_logits else None,
+                     None if dl is None else np.array(dl))
 
 
 def step_external(model: Model, state: State, tau: float, k: int, block_start: int,

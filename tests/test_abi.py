@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ec_abi_version() == 1
+    assert lib.ec_abi_version() == 2
     for s in range(-7, 1):
         assert lib.ec_status_string(s)
     assert lib.ec_status_string(99) == b"unknown status"
