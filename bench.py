@@ -297,6 +297,30 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
     out["k_ablation_tau_1"] = kab
     _log(f"k ablation (tau 1.0): {kab}")
 
+    # sliding-window decoding: the same unmask counts, the block being the 32
+    # positions from the first masked one (block_start = -1)
+    def sliding(t):
+        reset()
+        torch.cuda.synchronize()
+        fl2 = torch.zeros(len(sched), dtype=torch.int32, device="cuda")
+        t1 = time.perf_counter()
+        for i, (bs, bl, nn) in enumerate(sched):
+            fl2[i].copy_(ds.full_flag[0])
+            ds.step(t, cfg.k, -1, bl, nn)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t1
+        return ({"steps_per_s": round(len(sched) / dt, 2),
+                 "partial_fraction": round(float(1.0 - fl2.float().mean().item()), 3),
+                 "still_masked": int(ds.is_masked.sum().item())}, ds.tokens.cpu().numpy())
+
+    sl_van, sl_van_tok = sliding(float("-inf"))
+    sl_ec, sl_tok = sliding(tau)
+    done = gen & (ds.is_masked.cpu().numpy() == 0)
+    sl_ec["token_agreement_vs_vanilla"] = round(float((sl_tok[done] == sl_van_tok[done]).mean()), 4)
+    out["sliding_window_32"] = {"entropycache_tau_1": sl_ec, "vanilla": sl_van,
+                                "speedup_vs_vanilla": round(sl_ec["steps_per_s"] / sl_van["steps_per_s"], 3)}
+    _log(f"sliding window: {out['sliding_window_32']}")
+
     # KV drift on full steps (untimed): the E that triggered each full step
     # next to the Value drift that step measured
     reset()
@@ -666,6 +690,7 @@ def main() -> int:
             "speedup_vs_vanilla_at_tau_1": res["speedup_vs_vanilla_at_tau_1"],
             "k_ablation_tau_1": res["k_ablation_tau_1"],
             "kv_drift_tau_1": res.get("kv_drift_tau_1"),
+            "sliding_window_32": res.get("sliding_window_32"),
         }
         if "cpu_baseline" in res:
             line["cpu_baseline"] = res["cpu_baseline"]

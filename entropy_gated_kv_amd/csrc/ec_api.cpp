@@ -101,7 +101,8 @@ int32_t ec_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32
                        const int32_t* history_len, int32_t history_cap, int32_t k, int32_t* rows,
                        int32_t* n_rows, hipStream_t stream) {
   if (!full_flag || !is_masked || !history || !history_len || !rows || !n_rows) return EC_E_NULL;
-  if (L < 1 || block_start < 0 || block_len < 0 || block_start + block_len > L || k < 0 ||
+  if (L < 1 || block_start < -1 || block_len < 0 || block_len > L ||
+      (block_start >= 0 && block_start + block_len > L) || k < 0 ||
       history_cap < 1 || k > history_cap)
     return EC_E_SHAPE;
   if (L > ec::select_max_L()) return EC_E_UNSUPPORTED;
@@ -272,8 +273,9 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
     return EC_E_NULL;
   for (int l = 0; l < m->n_layers; ++l)
     if (!st->k_cache[l] || !st->v_cache[l]) return EC_E_NULL;
-  if (st->L < 1 || st->L > m->L_cap || c->block_start < 0 || c->block_len < 1 ||
-      c->block_start + c->block_len > st->L || c->k < 0 || c->k > st->history_cap ||
+  if (st->L < 1 || st->L > m->L_cap || c->block_start < -1 || c->block_len < 1 ||
+      c->block_len > st->L || (c->block_start >= 0 && c->block_start + c->block_len > st->L) ||
+      c->k < 0 || c->k > st->history_cap ||
       c->n_unmask < 0 || st->history_cap < 1)
     return EC_E_SHAPE;
   if (external && (c->n_unmask < 1 || c->n_unmask > c->block_len)) return EC_E_SHAPE;

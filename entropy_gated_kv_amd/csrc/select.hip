@@ -6,6 +6,12 @@
 // decode history of O(k) memory (Chinese page §2.3).  Every other position
 // reads its K/V from the cache.
 //
+// Sliding-window decoding (block_start < 0): the current block is the
+// block_len positions from the first masked one, found here on the device, so
+// the window moves with the unmasking without a host round trip.  The pages
+// name sliding-window decoding among the strategies the method applies to
+// (Portuguese page §5, Chinese page §5).
+//
 // One workgroup: the union is marked in an LDS bitmap over [0, L), then
 // compacted with a workgroup prefix sum over popcounts, which yields the rows
 // in ascending order with duplicates removed.  The same pass can report, for
@@ -49,9 +55,22 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(
   extern __shared__ uint32_t bits[];                 // ceil(L / 32) words
   __shared__ int s_wave[kThreads / kWave + 1];
   __shared__ int s_chunk[kThreads];                  // rows before each thread's word run
+  __shared__ int s_first;
   const int tid = threadIdx.x;
   const int nwords = (L + 31) / 32;
   const bool full = (*full_flag != 0);
+  if (block_start < 0) {
+    // sliding window: block_len positions from the first masked one, clipped at L
+    if (tid == 0) s_first = L;
+    __syncthreads();
+    int f = L;
+    for (int p = tid; p < L; p += kThreads)
+      if (is_masked[p]) { f = p; break; }
+    atomicMin(&s_first, f);
+    __syncthreads();
+    block_start = s_first;
+    block_len = min(block_len, L - block_start);
+  }
   const int bend = block_start + block_len;
 
   if (full) {

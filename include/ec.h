@@ -119,9 +119,13 @@ int32_t ec_entropy_max(const void* logits, int32_t dtype, int64_t n_rows, int64_
  * position ever decoded, 0-based) is at history[i % history_cap]; *history_len
  * is the total count appended.  Requires k <= history_cap.  Positions must be
  * < L; duplicates in the union are written once.
+ * Sliding-window decoding: block_start = -1 makes the block the block_len
+ * positions from the first masked position, clipped at L (empty when nothing
+ * is masked), found on the device (Portuguese page §5 and Chinese page §5 name
+ * sliding-window decoding among the strategies the method applies to).
  * Outputs: rows [L] (device, first *n_rows valid) and *n_rows (device).
- * Errors: EC_E_NULL, EC_E_SHAPE (L < 1, block outside [0, L), k < 0,
- * k > history_cap, history_cap < 1), EC_E_LAUNCH.
+ * Errors: EC_E_NULL, EC_E_SHAPE (L < 1, block outside [0, L), block_start < -1,
+ * block_len > L, k < 0, k > history_cap, history_cap < 1), EC_E_LAUNCH.
  * ------------------------------------------------------------------------ */
 int32_t ec_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
                        int32_t block_start, int32_t block_len,
@@ -283,7 +287,7 @@ typedef struct ec_step_cfg {
   float tau;
   int32_t k;
   int32_t n_unmask;
-  int32_t block_start;
+  int32_t block_start;        /* or -1: sliding window (see ec_select_rows) */
   int32_t block_len;          /* <= max_block of the workspace             */
 } ec_step_cfg;
 

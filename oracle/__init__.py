@@ -33,7 +33,7 @@ oracle's own definition: parity unpinned for that composite.
 from .rounding import to_storage, round_bf16  # noqa: F401
 from .entropy import (softmax_entropy, row_stats, max_entropy, decide, entropy_max,  # noqa: F401
                       choose)
-from .selection import select_rows, candidates  # noqa: F401
+from .selection import select_rows, candidates, sliding_window  # noqa: F401
 from .layers import linear, kv_refresh, bidir_attention, rmsnorm, swiglu  # noqa: F401
 from .drift import cosine_distance, value_drift  # noqa: F401
 from .step import (Model, State, StepTrace, step, step_external, generate, init_state,  # noqa: F401

@@ -33,7 +33,7 @@ from .drift import value_drift
 from .entropy import choose, decide, max_entropy, row_stats
 from .layers import bidir_attention, kv_refresh, linear, rmsnorm, swiglu
 from .rounding import to_storage
-from .selection import candidates, select_rows
+from .selection import candidates, select_rows, sliding_window
 
 
 @dataclasses.dataclass
@@ -141,7 +141,11 @@ def step(model: Model, state: State, tau: float, k: int, block_start: int, block
          n_unmask: int, keep_logits: bool = True, drift: bool = False) -> StepTrace:
     """One denoising step; mutates `state` and returns what the step computed.
 
-    drift: on a full step, also report each layer's Value drift (oracle.drift)."""
+    drift: on a full step, also report each layer's Value drift (oracle.drift).
+    block_start < 0: sliding-window decoding, the block being the block_len
+    positions from the first masked one (oracle.selection.sliding_window)."""
+    if block_start < 0:
+        block_start, block_len = sliding_window(state.masked, block_len)
     flag_used = state.flag
     rows = select_rows(flag_used, state.masked, block_start, block_len, state.history, k)
     dl = [] if (drift and flag_used) else None
@@ -179,6 +183,8 @@ def step_external(model: Model, state: State, tau: float, k: int, block_start: i
     and history are left to the caller; the steady-state long-context step is
     this case (its decoded rows are synthetic).
     """
+    if block_start < 0:
+        block_start, block_len = sliding_window(state.masked, block_len)
     flag_used = state.flag
     rows = select_rows(flag_used, state.masked, block_start, block_len, state.history, k)
     forward_rows(model, state, rows)

@@ -52,3 +52,24 @@ def test_history_ring_wraps():
     want = O.select_rows(0, masked, 272, 16, hist, 20)
     got = gpu_select(0, masked, 272, 16, hist, 20, 20)
     np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("L_", [1, 77, 1000, 32800])
+def test_sliding_window_matches_oracle(L_):
+    """block_start = -1: the block is the block_len positions from the first
+    masked one (found on the device), clipped at L; nothing masked: no block."""
+    for seed in range(5):
+        masked = G.random_mask(seed, L_, 0.3).astype(np.uint8)
+        if seed == 0:
+            masked[:] = 0                              # nothing masked
+        elif seed == 1:
+            masked[:] = 0
+            masked[-1] = 1                             # window clipped at L
+        decoded = np.flatnonzero(masked == 0)
+        hist = list(G.random_history(seed, decoded, min(len(decoded), 40)))
+        for bl in (1, 32):
+            bl = min(bl, L_)
+            bs, bl_eff = O.sliding_window(masked, bl)
+            want = O.select_rows(0, masked, bs, bl_eff, hist, 16)
+            got = gpu_select(0, masked, -1, bl, hist, 16, 64)
+            np.testing.assert_array_equal(got, want, err_msg=f"L={L_} seed={seed} bl={bl}")

@@ -101,6 +101,28 @@ def test_tiny_fp32_trajectory_free_running(tau):
         assert_close(v, st.V[l], "f32", "final V cache")
 
 
+@pytest.mark.parametrize("tau", [1.5, math.inf])
+def test_tiny_fp32_sliding_window_free_running(tau):
+    """Sliding-window decoding (block_start = -1, a 16-position window that
+    starts at the first masked position) free-running against the oracle."""
+    cfg = C.TINY
+    model, st, dm, ds = setup(cfg)
+    n_steps = 0
+    while st.masked.any() and n_steps < 40:
+        tr = O.step(model, st, tau, cfg.k, -1, 16, 2)
+        ds.step(tau, cfg.k, -1, 16, 2)
+        g = read(ds, len(tr.cand))
+        i = n_steps
+        np.testing.assert_array_equal(g["rows"], tr.rows, err_msg=f"step {i} rows")
+        np.testing.assert_array_equal(g["argmax"], tr.argmax, err_msg=f"step {i} argmax")
+        np.testing.assert_array_equal(g["chosen"], tr.chosen, err_msg=f"step {i} chosen")
+        np.testing.assert_array_equal(g["tokens"], st.tokens, err_msg=f"step {i} tokens")
+        assert g["flag"] == tr.flag_next, i
+        assert_close(g["logits"], tr.logits, "f32", f"step {i} logits")
+        n_steps += 1
+    assert not st.masked.any(), n_steps         # the window reached the end of the sequence
+
+
 def logit_tol(model, tr):
     sp = np.ones(len(tr.cand)) if model.logit_scale is None else model.logit_scale[tr.cand]
     prop = sp[:, None] * (np.abs(tr.x_cand) @ np.abs(model.w_lm).T) * 2.0 ** -7

@@ -43,3 +43,31 @@ def test_invariants_on_random_states():
             assert np.all(np.diff(rows) > 0)                   # ascending, no duplicates
             assert set(candidates(masked, bs, bl)) <= set(rows)
             assert not (set(rows) & set(range(bs + bl, L)))    # later blocks come from the cache
+
+
+def test_sliding_window_hand_worked():
+    from oracle.selection import sliding_window
+    masked = np.array([0, 0, 1, 0, 1, 1, 0, 1], dtype=np.uint8)
+    assert sliding_window(masked, 3) == (2, 3)                 # window [2, 5): candidates 2, 4
+    np.testing.assert_array_equal(candidates(masked, *sliding_window(masked, 3)), [2, 4])
+    assert sliding_window(masked, 10) == (2, 6)               # clipped at L
+    assert sliding_window(np.zeros(5), 4) == (5, 0)           # nothing masked: empty block
+    masked[2] = 0                                             # the leftmost is decoded: the window moves
+    assert sliding_window(masked, 3) == (4, 3)
+    np.testing.assert_array_equal(candidates(masked, *sliding_window(masked, 3)), [4, 5])
+
+
+def test_sliding_window_step_moves_with_the_leftmost_masked_position():
+    import oracle as O
+    from synth import configs as C
+    from synth import generators as G
+    cfg = C.scaled(C.TINY, name="slide", prompt_len=40, gen_len=24, block_len=24, k=4)
+    w = G.model_weights(cfg)
+    model = O.Model.from_arrays(cfg.model, "f32", w)
+    toks, masked = G.initial_sequence(cfg)
+    st = O.init_state(model, toks, masked)
+    for i in range(6):
+        first = int(np.flatnonzero(st.masked)[0])
+        tr = O.step(model, st, 2.0, cfg.k, -1, 8, 2)
+        assert tr.cand.min() == first and tr.cand.max() < first + 8, (i, first, tr.cand)
+        assert set(tr.chosen) <= set(tr.cand.tolist())
