@@ -11,17 +11,18 @@
 // the one that does not apply exits at once, so no row count crosses to the
 // host:
 //  * skinny (n <= 128, partial steps and the LM head): weights are streamed
-//    from HBM exactly once across the grid.  A workgroup owns 128 or 256
-//    output columns (32 or 64 per wave) and a K range; the selected rows' A
-//    slice is staged in LDS (double-buffered, 64 k per stage) and shared by the
-//    four waves; W fragments go global -> registers, one iteration ahead.  When
-//    the column tiles alone cannot fill the chip the K range is split over
-//    workgroups; the last workgroup of a tile sums the partials in split order
+//    from HBM exactly once across the grid.  A workgroup owns 64 output
+//    columns (16 per wave) and a K range; the selected rows' A slice is staged
+//    in LDS per iteration and shared by the four waves; W fragments go
+//    global -> registers two iterations ahead (16x16x32 MFMA).  When the
+//    column tiles alone cannot fill the chip the K range is split over
+//    workgroups and a second kernel sums the partials in split order
 //    (deterministic) and runs the epilogue.
-//  * tiled (n > 128, full steps): 128 x 128 output tiles, 64 k per stage,
-//    A and W tiles double-buffered in LDS, 2 x 2 waves of 64 x 64.
-// MFMA: v_mfma_f32_32x32x16_bf16 (bf16) or v_mfma_f32_32x32x2_f32 (fp32), fp32
-// accumulation.  Each lane's 16-byte loads cover consecutive k; the k order
+//  * tiled (n > 128, full steps): BM x BN output tiles (128 x 128 up to
+//    256 x 256, chosen per shape), A and W tiles copied global -> LDS
+//    directly, 64 k per stage (32x32x16 MFMA); an fp32 variant stages
+//    through registers.
+// Accumulation is fp32.  Each lane's 16-byte loads cover consecutive k; the k order
 // inside an MFMA is permuted identically for A and W, which leaves the sum
 // unchanged.
 #include <math.h>
