@@ -117,6 +117,7 @@ def entropy_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         "ms_per_step": wall * 1e3 / steps,
         "kernel_ms": kern_ms,
         "GB_per_s": gbs,
+        "rows_per_s": n / (kern_ms * 1e-3),
         "frac": gbs / HBM_PEAK_GBS,
         "bytes_per_launch": bytes_per,
         "e_max": float(E.item()),
@@ -227,10 +228,15 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
     torch.cuda.synchronize()
     fl = flags.cpu().numpy()
     phase_ms = {}
+    by_mode = {"partial": {}, "full": {}}
     for k, name in enumerate(PHASES):
         if name == "ffn":
             continue
-        phase_ms[name] = float(np.mean([ev[2 * k].elapsed_time(ev[2 * k + 1]) for ev in bd_events]))
+        t = np.array([ev[2 * k].elapsed_time(ev[2 * k + 1]) for ev in bd_events])
+        phase_ms[name] = float(t.mean())
+        for mode, want in (("partial", 0), ("full", 1)):
+            if (fl == want).any():
+                by_mode[mode][name] = float(t[fl == want].mean())
     # LM-head algorithmic bytes per launch: W_lm read once, the candidates'
     # activations read and their logits written (mean candidate count over the
     # timed steps: the block's still-masked positions at each step)
@@ -246,12 +252,37 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
     lm_bytes = int(V * d * 2 + m * d * 2 + m * V * 2)
     lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
     decide_ms = phase_ms["select"] + phase_ms["entropy"] + phase_ms["decide"]
+    # each phase against its roofline: max(bytes / HBM peak, flops / bf16 MFMA peak),
+    # partial steps at 96 selected rows (32 block rows + k = 64), full steps at L
+    mm = cfg.model
+    L_, hd = cfg.L, mm.n_q_heads * mm.head_dim
+    nqkv = (mm.n_q_heads + 2 * mm.n_kv_heads) * mm.head_dim
+    kv_bytes = 2 * mm.n_kv_heads * L_ * mm.head_dim * 2
+    def ideal_us(nbytes, flops):
+        return max(nbytes / (HBM_PEAK_GBS * 1e3), flops / (BF16_PEAK_TFLOPS * 1e6))
+    n_p = cfg.block_len + cfg.k
+    ideal = {
+        "partial": {"qkv": ideal_us(nqkv * d * 2, 2.0 * n_p * d * nqkv),
+                    "attn": ideal_us(kv_bytes, 4.0 * n_p * L_ * hd),
+                    "oproj": ideal_us(d * hd * 2, 2.0 * n_p * hd * d),
+                    "lmhead": ideal_us(lm_bytes, 2.0 * m * d * V)},
+        "full": {"qkv": ideal_us(nqkv * d * 2 + L_ * d * 2, 2.0 * L_ * d * nqkv),
+                 "attn": ideal_us(kv_bytes, 4.0 * L_ * L_ * hd),
+                 "oproj": ideal_us(d * hd * 2, 2.0 * L_ * hd * d),
+                 "lmhead": ideal_us(lm_bytes, 2.0 * m * d * V)},
+    }
+    phase_roofline = {
+        mode: {name: {"us": round(by_mode[mode][name] * 1e3, 2), "ideal_us": round(iu, 2),
+                      "frac": round(iu / (by_mode[mode][name] * 1e3), 3)}
+               for name, iu in ideal[mode].items() if name in by_mode[mode]}
+        for mode in ideal}
     out = {
         "value": steps / wall,
         "ms_per_step": wall * 1e3 / steps,
         "partial_fraction": float(1.0 - fl.mean()),
         "phases_us": {k: round(v * 1e3, 2) for k, v in phase_ms.items()},
         "decision_overhead_frac": decide_ms / sum(phase_ms.values()),
+        "phase_roofline": phase_roofline,
         "roofline": {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("gemm_skinny_kernel<bf16,lmhead>", "gemm.hip", 1),
@@ -585,9 +616,62 @@ def stack_leg(n_steps: int = 66) -> dict:
         out[key] = rec
         _log(f"{cfg.name} tau={tau}: {rec}")
     out["speedup_vs_vanilla"] = round(out["entropycache"]["steps_per_s"] / out["vanilla"]["steps_per_s"], 3)
+    # the per-step roofline: the sum of every kernel's ideal (HBM bytes at 8 TB/s
+    # on partial steps, bf16 MFMA flops at 2.5 PFLOP/s on full steps)
+    d, hd, ff, L_ = m.d, m.n_q_heads * m.head_dim, m.d_ffn, cfg.L
+    nqkv = (m.n_q_heads + 2 * m.n_kv_heads) * m.head_dim
+    layer_w = (nqkv * d + hd * d + 3 * ff * d) * 2
+    kv = 2 * m.n_kv_heads * L_ * m.head_dim * 2
+    lm_w = m.vocab * d * 2
+    part_ms = (m.n_layers * (layer_w + kv) + lm_w) / (HBM_PEAK_GBS * 1e6)
+    full_fl = m.n_layers * (2.0 * L_ * d * (nqkv + hd + 3 * ff) + 4.0 * L_ * L_ * hd)
+    full_ms = full_fl / (BF16_PEAK_TFLOPS * 1e9) + lm_w / (HBM_PEAK_GBS * 1e6)
+    ec = out["entropycache"]
+    out["roofline"] = {"partial_step_ideal_ms": round(part_ms, 3), "full_step_ideal_ms": round(full_ms, 3),
+                       "partial_frac": round(part_ms / ec["partial_step_ms"], 3) if "partial_step_ms" in ec else None,
+                       "full_frac": round(full_ms / ec["full_step_ms"], 3) if "full_step_ms" in ec else None}
+    _log(f"{cfg.name} roofline: {out['roofline']}")
     del ds, dm
     torch.cuda.empty_cache()
     return out
+
+
+def stack_cpu_baseline(budget_s: float = 20.0) -> dict:
+    """The float64 oracle on a bounded sample of the 32-layer stack: one layer's
+    partial step (96 selected rows against an L = 2048 cache; the vocabulary,
+    which a layer does not touch beyond one embedding row per token, cut to
+    1024) and the LM head over the block's 32 rows on 1/16 of W_lm.  The step
+    time is extrapolated as 32 x layer + 16 x head slice (labelled so)."""
+    import numpy as np
+
+    import oracle as O
+    from synth import configs as C
+    from synth import generators as G
+
+    cfg = C.scaled(C.LLADA_STACK, name="stack_one_layer", model_n_layers=1, model_vocab=1024)
+    w = G.model_weights(cfg)
+    model = O.Model.from_arrays(cfg.model, cfg.dtype, w)
+    toks, masked = G.initial_sequence(cfg)
+    st = O.init_state(model, toks, masked)       # empty cache: the timing does not depend on it
+    rows = np.arange(cfg.prompt_len - cfg.k, cfg.prompt_len + cfg.block_len)   # 96 rows
+    n, t_layer = 0, 0.0
+    t0 = time.perf_counter()
+    while n < 3 and (n == 0 or time.perf_counter() - t0 < budget_s):
+        t1 = time.perf_counter()
+        x = O.forward_rows(model, st, rows)
+        t_layer += time.perf_counter() - t1
+        n += 1
+    V, d = C.LLADA_STACK.model.vocab, cfg.model.d
+    w_slice = np.random.default_rng(0).standard_normal((V // 16, d))
+    t1 = time.perf_counter()
+    O.linear(x[-cfg.block_len:], w_slice)
+    t_head = 16 * (time.perf_counter() - t1)
+    step_s = C.LLADA_STACK.model.n_layers * t_layer / n + t_head
+    return {"value": round(1.0 / step_s, 4), "unit": "partial steps/s (extrapolated)",
+            "cores": _cpu_cores(), "kind": "oracle",
+            "sample": f"one layer's partial step (96 rows, L = {cfg.L}) x {n} and the LM head over "
+                      f"{cfg.block_len} rows on 1/16 of W_lm, NumPy float64; step = 32 x layer + "
+                      f"16 x head slice"}
 
 
 # --------------------------------------------------------------------------- profiling
@@ -686,6 +770,7 @@ def main() -> int:
             "partial_fraction": round(res["partial_fraction"], 3),
             "phases_us": res["phases_us"],
             "decision_overhead_frac": round(res["decision_overhead_frac"], 4),
+            "phase_roofline": res["phase_roofline"],
             "tau_sweep": res["tau_sweep"],
             "speedup_vs_vanilla_at_tau_1": res["speedup_vs_vanilla_at_tau_1"],
             "k_ablation_tau_1": res["k_ablation_tau_1"],
@@ -696,6 +781,8 @@ def main() -> int:
             line["cpu_baseline"] = res["cpu_baseline"]
     if not args.skip_stack:
         line["stack32"] = stack_leg()
+        if not args.no_cpu_baseline:
+            line["stack32"]["cpu_baseline"] = stack_cpu_baseline()
     if not args.skip_long:
         from synth import configs as C
         from synth import generators as G
@@ -709,7 +796,7 @@ def main() -> int:
         del tok
     if not args.skip_entropy:
         ent = entropy_leg(200, 30, not args.no_cpu_baseline)   # ~40 ms timed, clocks settled
-        line["entropy_pass"] = {"GB_per_s": round(ent["GB_per_s"], 1), "us_per_pass": round(ent["kernel_ms"] * 1e3, 2),
+        line["entropy_pass"] = {"GB_per_s": round(ent["GB_per_s"], 1), "us_per_pass": round(ent["kernel_ms"] * 1e3, 2), "rows_per_s": round(ent["rows_per_s"], 1),
                                 "roofline": ent["roofline"], "workload": "entropy_4096x126464_bf16",
                                 "cpu_baseline": ent.get("cpu_baseline")}
     print(json.dumps(line), flush=True)

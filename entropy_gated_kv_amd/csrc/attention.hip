@@ -1010,11 +1010,18 @@ hipError_t launch_bf16(const AttnArgs& a, void* ws, hipStream_t s) {
                      b.sp.nw * 32 * b.sp.qb, b.grid_p);
   e = hipGetLastError();
   if (e != hipSuccess || a.max_rows <= kPartialMaxRows) return e;
-  // unsplit variant (n > 128)
+  // unsplit variant (n > 128); when the eight-wave query tiles would leave CUs
+  // idle (e.g. MHA at L = 1024: 32 heads x 4 tiles), four-wave tiles of 128
+  // rows double the workgroups
   p.partial = 0;
-  const BShape sh = full_shape(DH);
-  const int qt = sh.nw * 32 * sh.qb;
-  const int64_t groups = (int64_t(a.max_rows) * p.G + qt - 1) / qt * a.Hkv;
+  BShape sh = full_shape(DH);
+  int qt = sh.nw * 32 * sh.qb;
+  int64_t groups = (int64_t(a.max_rows) * p.G + qt - 1) / qt * a.Hkv;
+  if (DH >= 64 && groups < device_cu_count()) {
+    sh = BShape{4, 1, 3, 1, 0};
+    qt = sh.nw * 32 * sh.qb;
+    groups = (int64_t(a.max_rows) * p.G + qt - 1) / qt * a.Hkv;
+  }
   return launch_bf16_shape<DH>(p, sh, unsigned((groups + 7) / 8 * 8), s);
 }
 
