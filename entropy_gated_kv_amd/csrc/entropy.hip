@@ -106,20 +106,10 @@ constexpr int kVPT = 8;   // 16-byte vectors per lane in a full segment
 
 constexpr int64_t seg_elems(int per_vec) { return int64_t(kVPT) * kWave * per_vec; }
 
-// Maximum of the elements of one vector, NaN-propagating (IEEE 754-2019
+// Maximum of the elements of one fp32 vector, NaN-propagating (IEEE 754-2019
 // maximum, v_maximum3_f32: no input canonicalisation, two elements per
-// instruction).  For bf16 the upper element of each 32-bit word is compared as
-// the raw word read as fp32: the low 16 bits only move it within the gap to the
-// next bf16 value, which keeps the order, and masking them off afterwards
-// restores the exact element.  A raw word is NaN only when its upper element
-// is infinite or NaN; the NaN maximum then sends the segment to the exact path.
+// instruction); a NaN maximum sends the segment to the exact path.
 __device__ __forceinline__ float max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-__device__ __forceinline__ float vec_max(const u32x4& v) {
-  const float h = max2(max2(__uint_as_float(v.x), __uint_as_float(v.y)),
-                       max2(__uint_as_float(v.z), __uint_as_float(v.w)));
-  const float hm = __uint_as_float(__float_as_uint(h) & 0xffff0000u);
-  return max2(max2(max2(hm, bf16_lo(v.x)), max2(bf16_lo(v.y), bf16_lo(v.z))), bf16_lo(v.w));
-}
 __device__ __forceinline__ float vec_max(const f32x4& v) {
   return max2(max2(v.x, v.y), max2(v.z, v.w));
 }

@@ -223,10 +223,10 @@ int32_t ec_bidir_attention(const void* q, const int32_t* n_rows, int32_t max_row
  * skipping the final norm (nothing reads it).  This is the steady-state
  * long-context step, where the decoded rows come from outside the layer.
  * The first step of a sequence must run with *full_flag = 1 (no cache yet).
- * ws (ec_step_workspace_bytes(model, max_block) bytes) must be zero-filled
- * before its first use; steps leave its counters zeroed.
+ * ws (ec_step_workspace_bytes(model, max_block) bytes) is scratch: every
+ * region is written before it is read, so no initial contents are required.
  * Norms and FFN are present iff d_ffn > 0.  d, Hq*dh and d_ffn must be
- * multiples of 256 (bf16) or 128 (fp32) (EC_E_UNSUPPORTED otherwise); block_len
+ * multiples of 128 (bf16) or 64 (fp32) (EC_E_UNSUPPORTED otherwise); block_len
  * is at most 1024.  The block (block_start,
  * block_len) and n_unmask are host values: the schedule is fixed on the host.
  * ------------------------------------------------------------------------ */

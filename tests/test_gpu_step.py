@@ -202,3 +202,22 @@ def test_llada_layer_full_size_two_steps():
     # logits reach a few hundred here (scale up to 100), where one bf16 unit is
     # 2.0, so near-equal maxima are common; each tie was checked against its zone
     assert n_partial == 1 and ties <= 8
+
+
+def test_workspace_contents_do_not_matter():
+    """ec_step's workspace is scratch: a trajectory run on a workspace full of
+    0xFF bytes (NaN patterns) equals the one on a zero-filled workspace."""
+    cfg = C.TINY
+    out = []
+    for fill in (0, 255):
+        model, st, dm, ds = setup(cfg)
+        ds.ws.fill_(fill)
+        trace = []
+        for bs, bl, n in C.unmask_schedule(cfg)[:6]:
+            ds.step(1.5, cfg.k, bs, bl, n)
+            g = read(ds, bl)
+            trace.append((g["rows"], g["chosen"], g["tokens"], g["logits"], g["E"], g["flag"]))
+        out.append(trace)
+    for a, b in zip(*out):
+        for x, y in zip(a, b):
+            assert np.array_equal(np.asarray(x), np.asarray(y))
