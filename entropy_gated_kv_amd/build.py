@@ -26,10 +26,12 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC]
-# Per-source device options.  attention.hip: MFMA results in ordinary VGPRs
-# (the accumulator-register form makes the compiler copy the output tile
-# between register files on every kv tile).
-EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source device options: MFMA results in ordinary VGPRs.  attention.hip:
+# the accumulator-register form makes the compiler copy the output tile between
+# register files on every kv tile.  gemm.hip: it lowers the skinny kernels'
+# register count (the 96-row instance fits three waves per SIMD instead of two).
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+EXTRA = {"attention.hip": _VGPR_FORM, "gemm.hip": _VGPR_FORM}
 
 
 def _hipcc() -> str:

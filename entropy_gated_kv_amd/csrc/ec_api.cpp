@@ -298,6 +298,11 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   const int dt = m->dtype;
   const int L = st->L;
   const int hd = m->Hq * m->dh;
+  // A partial step selects at most block_len + k rows (the block's masked
+  // positions and the last k decoded ones); a full step selects all L, which
+  // the skinny kernels see only when L <= 128.
+  const int64_t part_rows = int64_t(c->block_len) + c->k;
+  const int sk_rows = (L <= 128 || part_rows >= L) ? L : int(part_rows);
   const PhaseTimer tm{phase_events, stream};
 
   EC_TRY(tm.begin(EC_PHASE_SELECT));
@@ -321,7 +326,7 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
     }
     ec::GemmArgs g;
     g.dtype = dt; g.epi = ec::Epi::kQKV; g.A = a_in; g.lda = m->d; g.n_rows_dev = st->n_rows;
-    g.max_rows = L; g.W = ly.w_qkv; g.N = (m->Hq + 2 * m->Hkv) * m->dh; g.K = m->d;
+    g.max_rows = L; g.skinny_rows = sk_rows; g.W = ly.w_qkv; g.N = (m->Hq + 2 * m->Hkv) * m->dh; g.K = m->d;
     g.rows = st->rows; g.q_out = s.q; g.k_cache = st->k_cache[l]; g.v_cache = st->v_cache[l];
     g.Hq = m->Hq; g.Hkv = m->Hkv; g.dh = m->dh; g.L_cap = m->L_cap;
     const int vrows = m->Hkv * m->dh;
@@ -343,7 +348,7 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
 
     ec::GemmArgs go;
     go.dtype = dt; go.epi = ec::Epi::kResidual; go.A = s.o; go.lda = hd; go.n_rows_dev = st->n_rows;
-    go.max_rows = L; go.W = ly.w_o; go.N = m->d; go.K = hd; go.C = s.x; go.ldc = m->d;
+    go.max_rows = L; go.skinny_rows = sk_rows; go.W = ly.w_o; go.N = m->d; go.K = hd; go.C = s.x; go.ldc = m->d;
     EC_TRY(ec::launch_gemm_rows(go, s.gemm_ws, stream));
     if (first) EC_TRY(tm.end(EC_PHASE_OPROJ));
 
@@ -352,12 +357,12 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
       EC_TRY(ec::launch_rmsnorm(dt, s.x, st->n_rows, L, m->d, ly.norm_ffn, m->rms_eps, s.a, stream));
       ec::GemmArgs gu;
       gu.dtype = dt; gu.epi = ec::Epi::kSwiGLU; gu.A = s.a; gu.lda = m->d;
-      gu.n_rows_dev = st->n_rows; gu.max_rows = L; gu.W = ly.w_gate; gu.W2 = ly.w_up;
+      gu.n_rows_dev = st->n_rows; gu.max_rows = L; gu.skinny_rows = sk_rows; gu.W = ly.w_gate; gu.W2 = ly.w_up;
       gu.N = m->d_ffn; gu.K = m->d; gu.C = s.h; gu.ldc = m->d_ffn;
       EC_TRY(ec::launch_gemm_rows(gu, s.gemm_ws, stream));
       ec::GemmArgs gd;
       gd.dtype = dt; gd.epi = ec::Epi::kResidual; gd.A = s.h; gd.lda = m->d_ffn;
-      gd.n_rows_dev = st->n_rows; gd.max_rows = L; gd.W = ly.w_down; gd.N = m->d; gd.K = m->d_ffn;
+      gd.n_rows_dev = st->n_rows; gd.max_rows = L; gd.skinny_rows = sk_rows; gd.W = ly.w_down; gd.N = m->d; gd.K = m->d_ffn;
       gd.C = s.x; gd.ldc = m->d;
       EC_TRY(ec::launch_gemm_rows(gd, s.gemm_ws, stream));
       if (first) EC_TRY(tm.end(EC_PHASE_FFN));

@@ -70,6 +70,10 @@ struct GemmArgs {
   const int32_t* a_idx = nullptr;
   const int32_t* n_rows_dev = nullptr;
   int max_rows = 0;
+  // Optional tighter bound on the device row count whenever that count is at
+  // most 128 (the rows the skinny kernel takes); 0 = max_rows.  The caller
+  // guarantees it: rows past the bound would be left unwritten.
+  int skinny_rows = 0;
   const void* W = nullptr;
   const void* W2 = nullptr;
   int N = 0, K = 0;

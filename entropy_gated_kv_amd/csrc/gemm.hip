@@ -280,8 +280,11 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
   }
 }
 
-// MBX: largest count of 16-row blocks this launch can see (2 when max_rows <= 32,
-// else 8); the kernel picks the body for the device row count.
+// MBX: largest count of 16-row blocks this launch can see (2, 4, 6 or 8, from
+// the host's bound on the row count); the kernel picks the body for the device
+// row count.  Each instance holds only the bodies up to MBX, so its register
+// footprint (and with it the waves per SIMD) follows the bound: at 96 rows the
+// six-block instance keeps three waves per SIMD where the eight-block one has two.
 template <typename T, int MBX, bool DUAL, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(GP p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -289,10 +292,12 @@ __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(GP p) {
   if (n_rows <= 0 || n_rows > kSkinnyMaxRows) return;
   const int mb = (n_rows + 15) / 16;
   if (MBX == 2 || mb <= 2) skinny_body<T, 2, DUAL, EPI>(p, n_rows, smem);
-  else if constexpr (MBX == 8) {
-    if (mb <= 4) skinny_body<T, 4, DUAL, EPI>(p, n_rows, smem);
-    else if (mb <= 6) skinny_body<T, 6, DUAL, EPI>(p, n_rows, smem);
-    else skinny_body<T, 8, DUAL, EPI>(p, n_rows, smem);
+  else if constexpr (MBX >= 4) {
+    if (MBX == 4 || mb <= 4) skinny_body<T, 4, DUAL, EPI>(p, n_rows, smem);
+    else if constexpr (MBX >= 6) {
+      if (MBX == 6 || mb <= 6) skinny_body<T, 6, DUAL, EPI>(p, n_rows, smem);
+      else if constexpr (MBX == 8) skinny_body<T, 8, DUAL, EPI>(p, n_rows, smem);
+    }
   }
 }
 
@@ -696,7 +701,7 @@ void tiled_by_cfg(int c, const GP& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------- planning
-int mbx_of(int max_rows) { return max_rows <= 32 ? 2 : 8; }
+int mbx_of(int rows) { return rows <= 32 ? 2 : rows <= 64 ? 4 : rows <= 96 ? 6 : 8; }
 
 struct Plan {
   int MBX, S, KS, tiles;
@@ -707,7 +712,7 @@ template <typename T>
 Plan plan_skinny(const GemmArgs& a) {
   Plan pl;
   const bool dual = (a.epi == Epi::kSwiGLU);
-  pl.MBX = mbx_of(a.max_rows);
+  pl.MBX = mbx_of(a.skinny_rows > 0 && a.skinny_rows < a.max_rows ? a.skinny_rows : a.max_rows);
   pl.tiles = (a.N + kSkinnyNT - 1) / kSkinnyNT;
   const int KIT = skit<T>();
   const int iters = (a.K + KIT - 1) / KIT;
@@ -731,6 +736,8 @@ void go_skinny(dim3 g, size_t lds, hipStream_t s, const GP& p) {
 template <typename T, int EPI, bool DUAL = false>
 void skinny_by_shape(const Plan& pl, dim3 g, size_t lds, hipStream_t s, const GP& p) {
   if (pl.MBX == 2) go_skinny<T, 2, DUAL, EPI>(g, lds, s, p);
+  else if (pl.MBX == 4) go_skinny<T, 4, DUAL, EPI>(g, lds, s, p);
+  else if (pl.MBX == 6) go_skinny<T, 6, DUAL, EPI>(g, lds, s, p);
   else go_skinny<T, 8, DUAL, EPI>(g, lds, s, p);
 }
 
