@@ -2,7 +2,8 @@
 
 Q and the refreshed cache rows within 2e-3 (fp32) / 2e-2 (bf16) abs and rel;
 cache rows not selected must be bitwise unchanged (sentinel-filled caches).
-Row counts cover 1..4 row blocks of the skinny kernel, the 128-row boundary,
+Row counts cover 1..4 row blocks of the skinny kernel (each row-bound
+instance), the 128-row boundary, split-K over a non-power-of-two count,
 the tiled kernel with a ragged last tile (in each of its tile
 configurations), and the LLaDA-shaped full size.
 """
@@ -77,3 +78,12 @@ def test_llada_full_size_sampled(n):
     Lc = 1024
     rows = np.arange(Lc) if n == Lc else np.sort(np.random.default_rng(3).choice(Lc, n, replace=False))
     run_case("bf16", 4096, 32, 32, 128, Lc, rows, seed=5, sample=[0, 1, n // 2, n - 1])
+
+
+@pytest.mark.parametrize("n", [40, 96])
+def test_dream_shape_split_k_sampled(n):
+    """Dream-shaped refresh (d = 3584, 28/4 heads of 128): 28 k-iterations
+    split seven ways, with the four- and six-block row instances."""
+    Lc = 1024
+    rows = np.sort(np.random.default_rng(11 + n).choice(Lc, n, replace=False))
+    run_case("bf16", 3584, 28, 4, 128, Lc, rows, seed=60 + n, sample=[0, 1, n // 2, n - 1])
