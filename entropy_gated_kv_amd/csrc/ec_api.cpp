@@ -289,8 +289,15 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
       (int64_t(m->V) * int64_t(esize(m->dtype))) % 16 != 0 ||
       (int64_t(m->L_cap) * int64_t(esize(m->dtype))) % 16 != 0)
     return EC_E_ALIGN;
-  for (int l = 0; l < m->n_layers; ++l)
-    if (!al16(st->k_cache[l]) || !al16(st->v_cache[l])) return EC_E_ALIGN;
+  if (m->d_ffn && !external && !al16(m->norm_final)) return EC_E_ALIGN;
+  for (int l = 0; l < m->n_layers; ++l) {
+    const ec_layer& ly = m->layers[l];
+    if (!al16(st->k_cache[l]) || !al16(st->v_cache[l]) || !al16(ly.w_qkv) || !al16(ly.w_o))
+      return EC_E_ALIGN;
+    if (m->d_ffn && (!al16(ly.norm_attn) || !al16(ly.norm_ffn) || !al16(ly.w_gate) ||
+                     !al16(ly.w_up) || !al16(ly.w_down)))
+      return EC_E_ALIGN;
+  }
   const int32_t max_block = c->block_len;
   const StepLayout s = step_layout(m, max_block, ws);
   if (ws_bytes < s.total) return EC_E_WORKSPACE;

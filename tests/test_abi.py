@@ -97,3 +97,26 @@ def test_step_argument_checks(lib):
     st, cfg = L.ec_state(), L.ec_step_cfg()
     assert lib.ec_step(C.byref(m), C.byref(st), C.byref(cfg), FAKE, 0, None, None) == -2
     assert lib.ec_step(None, C.byref(st), C.byref(cfg), FAKE, 0, None, None) == -1
+
+
+def test_step_rejects_misaligned_weights(lib):
+    """Every weight and gain is read in 16-byte vectors: a misaligned one is
+    EC_E_ALIGN (checked on the host; the workspace check comes after)."""
+    def call(**bad):
+        ly = L.ec_layer(**{f: bad.get(f, FAKE) for f in ("w_qkv", "w_o", "norm_attn", "norm_ffn",
+                                                          "w_gate", "w_up", "w_down")})
+        layers = (L.ec_layer * 1)(ly)
+        m = L.ec_model(n_layers=1, d=256, Hq=4, Hkv=4, dh=64, d_ffn=512, V=1024, L_cap=256, dtype=1,
+                       rms_eps=1e-5, tok_emb=FAKE, pos_emb=FAKE, layers=layers,
+                       norm_final=bad.get("norm_final", FAKE), w_lm=FAKE, logit_scale=None)
+        caches = (C.c_void_p * 1)(FAKE)
+        st = L.ec_state(L=256, tokens=FAKE, is_masked=FAKE, history=FAKE, history_len=FAKE,
+                        history_cap=64, full_flag=FAKE, k_cache=caches, v_cache=caches, rows=FAKE,
+                        n_rows=FAKE, logits=FAKE, row_entropy=FAKE, row_argmax=FAKE, row_top1=FAKE,
+                        chosen=FAKE, n_chosen=FAKE, e_max=FAKE, kv_drift=None)
+        cfg = L.ec_step_cfg(tau=1.0, k=16, n_unmask=2, block_start=192, block_len=32)
+        return lib.ec_step(C.byref(m), C.byref(st), C.byref(cfg), FAKE, 0, None, None)
+
+    assert call() == -4                                            # only the workspace is short
+    for f in ("w_qkv", "w_o", "norm_attn", "norm_ffn", "w_gate", "w_up", "w_down", "norm_final"):
+        assert call(**{f: ODD}) == -5, f
