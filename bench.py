@@ -591,6 +591,11 @@ def stack_leg(n_steps: int = 66) -> dict:
             if events is not None:
                 events[i][1].record()
 
+    def run_host_mode(tau):
+        # the host reads each step's mode (a 4-byte copy that waits for the
+        # previous step) and launches only that mode's kernels
+        return [ds.step_host_mode(tau, cfg.k, bs, bl, nn) for bs, bl, nn in sched]
+
     reset()
     for bs, bl, nn in sched[:3]:                 # warm-up (one full, two partial steps)
         ds.step(1.0, cfg.k, bs, bl, nn)
@@ -616,6 +621,17 @@ def stack_leg(n_steps: int = 66) -> dict:
         out[key] = rec
         _log(f"{cfg.name} tau={tau}: {rec}")
     out["speedup_vs_vanilla"] = round(out["entropycache"]["steps_per_s"] / out["vanilla"]["steps_per_s"], 3)
+    reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    modes = run_host_mode(1.0)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    out["entropycache_host_mode"] = {
+        "steps_per_s": round(len(sched) / wall, 3), "ms_per_step": round(wall * 1e3 / len(sched), 3),
+        "partial_fraction": round(1.0 - float(np.mean(modes)), 3),
+        "note": "mode read by the host before each step; only that mode's kernels launched"}
+    _log(f"{cfg.name} host-read mode: {out['entropycache_host_mode']}")
     # the per-step roofline: the sum of every kernel's ideal (HBM bytes at 8 TB/s
     # on partial steps, bf16 MFMA flops at 2.5 PFLOP/s on full steps)
     d, hd, ff, L_ = m.d, m.n_q_heads * m.head_dim, m.d_ffn, cfg.L

@@ -51,7 +51,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kKV = 64;              // kv rows per tile
 constexpr int kQT = 128;             // packed query rows per workgroup
-constexpr int kPartialMaxRows = 128; // rows handled by the split-KV variant
+constexpr int kPartialMaxRows = kSmallMaxRows; // rows handled by the split-KV variant
 
 template <typename T, int DH>
 struct Geo {
@@ -381,7 +381,7 @@ hipError_t launch_typed(const AttnArgs& a, void* ws, hipStream_t s) {
   p.opart = static_cast<float*>(ws);
   p.mlpart = p.opart + size_t(sp.S) * a.Hkv * sp.mcap * DH;
   if (sp.S > 1 && ws == nullptr) return hipErrorInvalidValue;
-  {
+  if (a.paths & kPathSmall) {
     const int qtiles = (kPartialMaxRows * p.G + kQT - 1) / kQT;
     hipLaunchKernelGGL((attn_kernel<T, DH>), dim3(unsigned(a.Hkv * qtiles * sp.S)), dim3(kThreads),
                        lds, s, p);
@@ -395,7 +395,7 @@ hipError_t launch_typed(const AttnArgs& a, void* ws, hipStream_t s) {
       if (e != hipSuccess) return e;
     }
   }
-  if (a.max_rows <= kPartialMaxRows) return hipSuccess;
+  if (a.max_rows <= kPartialMaxRows || !(a.paths & kPathLarge)) return hipSuccess;
   // unsplit variant (n > 128)
   p.S = 1; p.kv_per_split = (a.L + kKV - 1) / kKV * kKV; p.partial = 0;
   const int qtiles = (a.max_rows * p.G + kQT - 1) / kQT;
@@ -1002,14 +1002,17 @@ hipError_t launch_bf16(const AttnArgs& a, void* ws, hipStream_t s) {
   p.opart = static_cast<float*>(ws);
   p.mlpart = p.opart + size_t(b.smax) * a.Hkv * b.mcap * DH;
   // split-KV variant (n <= 128): one workgroup per CU, then the merge
-  p.partial = 1;
-  hipError_t e = launch_bf16_shape<DH>(p, b.sp, unsigned(b.grid_p), s);
-  if (e != hipSuccess) return e;
-  const int64_t rows = int64_t(a.Hkv) * kPartialMaxRows * p.G;   // (g, rho) rows, upper bound
-  hipLaunchKernelGGL((attn_bf16_merge_kernel<DH>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s, p,
-                     b.sp.nw * 32 * b.sp.qb, b.grid_p);
-  e = hipGetLastError();
-  if (e != hipSuccess || a.max_rows <= kPartialMaxRows) return e;
+  hipError_t e = hipSuccess;
+  if (a.paths & kPathSmall) {
+    p.partial = 1;
+    e = launch_bf16_shape<DH>(p, b.sp, unsigned(b.grid_p), s);
+    if (e != hipSuccess) return e;
+    const int64_t rows = int64_t(a.Hkv) * kPartialMaxRows * p.G;   // (g, rho) rows, upper bound
+    hipLaunchKernelGGL((attn_bf16_merge_kernel<DH>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
+                       p, b.sp.nw * 32 * b.sp.qb, b.grid_p);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess || a.max_rows <= kPartialMaxRows || !(a.paths & kPathLarge)) return e;
   // unsplit variant (n > 128); when the eight-wave query tiles would leave CUs
   // idle (e.g. MHA at L = 1024: 32 heads x 4 tiles), four-wave tiles of 128
   // rows double the workgroups

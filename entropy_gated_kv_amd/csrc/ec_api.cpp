@@ -276,7 +276,8 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   if (st->L < 1 || st->L > m->L_cap || c->block_start < -1 || c->block_len < 1 ||
       c->block_len > st->L || (c->block_start >= 0 && c->block_start + c->block_len > st->L) ||
       c->k < 0 || c->k > st->history_cap ||
-      c->n_unmask < 0 || st->history_cap < 1)
+      c->n_unmask < 0 || st->history_cap < 1 ||
+      (c->mode != EC_MODE_DEVICE && c->mode != EC_MODE_FULL && c->mode != EC_MODE_PARTIAL))
     return EC_E_SHAPE;
   if (external && (c->n_unmask < 1 || c->n_unmask > c->block_len)) return EC_E_SHAPE;
   const int km = ec::gemm_k_multiple(m->dtype);
@@ -307,9 +308,17 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   const int hd = m->Hq * m->dh;
   // A partial step selects at most block_len + k rows (the block's masked
   // positions and the last k decoded ones); a full step selects all L, which
-  // the skinny kernels see only when L <= 128.
+  // the small-row kernels see only when L <= kSmallMaxRows.
   const int64_t part_rows = int64_t(c->block_len) + c->k;
-  const int sk_rows = (L <= 128 || part_rows >= L) ? L : int(part_rows);
+  const int part_hi = part_rows >= L ? L : int(part_rows);
+  const int sk_rows = L <= ec::kSmallMaxRows ? L : part_hi;
+  // The most rows this step can select, and the row-count paths it can reach
+  // (a caller-stated mode leaves out the other mode's kernels).
+  const int hi = c->mode == EC_MODE_PARTIAL ? part_hi : L;
+  unsigned paths = 0;
+  if (c->mode != EC_MODE_FULL || L <= ec::kSmallMaxRows) paths |= ec::kPathSmall;
+  if (hi > ec::kSmallMaxRows) paths |= ec::kPathLarge;
+  const bool maybe_full = c->mode != EC_MODE_PARTIAL;
   const PhaseTimer tm{phase_events, stream};
 
   EC_TRY(tm.begin(EC_PHASE_SELECT));
@@ -318,7 +327,7 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
                                 st->n_rows, s.cand_pos, s.cand_idx, s.n_cand, stream));
   EC_TRY(tm.end(EC_PHASE_SELECT));
   EC_TRY(tm.begin(EC_PHASE_EMBED));
-  EC_TRY(ec::launch_embed(dt, m->tok_emb, m->pos_emb, st->tokens, st->rows, st->n_rows, L, m->d,
+  EC_TRY(ec::launch_embed(dt, m->tok_emb, m->pos_emb, st->tokens, st->rows, st->n_rows, hi, m->d,
                           s.x, stream));
   EC_TRY(tm.end(EC_PHASE_EMBED));
 
@@ -328,48 +337,48 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
     const void* a_in = s.x;
     if (first) EC_TRY(tm.begin(EC_PHASE_QKV));
     if (m->d_ffn) {
-      EC_TRY(ec::launch_rmsnorm(dt, s.x, st->n_rows, L, m->d, ly.norm_attn, m->rms_eps, s.a, stream));
+      EC_TRY(ec::launch_rmsnorm(dt, s.x, st->n_rows, hi, m->d, ly.norm_attn, m->rms_eps, s.a, stream));
       a_in = s.a;
     }
     ec::GemmArgs g;
     g.dtype = dt; g.epi = ec::Epi::kQKV; g.A = a_in; g.lda = m->d; g.n_rows_dev = st->n_rows;
-    g.max_rows = L; g.skinny_rows = sk_rows; g.W = ly.w_qkv; g.N = (m->Hq + 2 * m->Hkv) * m->dh; g.K = m->d;
+    g.max_rows = hi; g.skinny_rows = sk_rows; g.paths = paths; g.W = ly.w_qkv; g.N = (m->Hq + 2 * m->Hkv) * m->dh; g.K = m->d;
     g.rows = st->rows; g.q_out = s.q; g.k_cache = st->k_cache[l]; g.v_cache = st->v_cache[l];
     g.Hq = m->Hq; g.Hkv = m->Hkv; g.dh = m->dh; g.L_cap = m->L_cap;
     const int vrows = m->Hkv * m->dh;
-    if (st->kv_drift)   // full steps only (the kernels read the flag): the stale Value cache
+    if (st->kv_drift && maybe_full)   // full steps only (the kernels read the flag): the stale Value cache
       EC_TRY(ec::launch_value_drift_snapshot(dt, st->full_flag, st->v_cache[l], vrows, L, m->L_cap,
                                              s.drift_ws, stream));
     EC_TRY(ec::launch_gemm_rows(g, s.gemm_ws, stream));
-    if (st->kv_drift)
+    if (st->kv_drift && maybe_full)
       EC_TRY(ec::launch_value_drift(dt, st->full_flag, st->v_cache[l], vrows, L, m->L_cap, s.drift_ws,
                                     st->kv_drift + 2 * l, stream));
     if (first) { EC_TRY(tm.end(EC_PHASE_QKV)); EC_TRY(tm.begin(EC_PHASE_ATTN)); }
 
     ec::AttnArgs a;
-    a.dtype = dt; a.q = s.q; a.n_rows_dev = st->n_rows; a.max_rows = L; a.k_cache = st->k_cache[l];
+    a.dtype = dt; a.q = s.q; a.n_rows_dev = st->n_rows; a.max_rows = hi; a.k_cache = st->k_cache[l];
     a.v_cache = st->v_cache[l]; a.L = L; a.L_cap = m->L_cap; a.Hq = m->Hq; a.Hkv = m->Hkv;
-    a.dh = m->dh; a.scale = 1.0f / sqrtf(float(m->dh)); a.out = s.o;
+    a.dh = m->dh; a.scale = 1.0f / sqrtf(float(m->dh)); a.out = s.o; a.paths = paths;
     EC_TRY(ec::launch_attention(a, s.attn_ws, stream));
     if (first) { EC_TRY(tm.end(EC_PHASE_ATTN)); EC_TRY(tm.begin(EC_PHASE_OPROJ)); }
 
     ec::GemmArgs go;
     go.dtype = dt; go.epi = ec::Epi::kResidual; go.A = s.o; go.lda = hd; go.n_rows_dev = st->n_rows;
-    go.max_rows = L; go.skinny_rows = sk_rows; go.W = ly.w_o; go.N = m->d; go.K = hd; go.C = s.x; go.ldc = m->d;
+    go.max_rows = hi; go.skinny_rows = sk_rows; go.paths = paths; go.W = ly.w_o; go.N = m->d; go.K = hd; go.C = s.x; go.ldc = m->d;
     EC_TRY(ec::launch_gemm_rows(go, s.gemm_ws, stream));
     if (first) EC_TRY(tm.end(EC_PHASE_OPROJ));
 
     if (m->d_ffn) {
       if (first) EC_TRY(tm.begin(EC_PHASE_FFN));
-      EC_TRY(ec::launch_rmsnorm(dt, s.x, st->n_rows, L, m->d, ly.norm_ffn, m->rms_eps, s.a, stream));
+      EC_TRY(ec::launch_rmsnorm(dt, s.x, st->n_rows, hi, m->d, ly.norm_ffn, m->rms_eps, s.a, stream));
       ec::GemmArgs gu;
       gu.dtype = dt; gu.epi = ec::Epi::kSwiGLU; gu.A = s.a; gu.lda = m->d;
-      gu.n_rows_dev = st->n_rows; gu.max_rows = L; gu.skinny_rows = sk_rows; gu.W = ly.w_gate; gu.W2 = ly.w_up;
+      gu.n_rows_dev = st->n_rows; gu.max_rows = hi; gu.skinny_rows = sk_rows; gu.paths = paths; gu.W = ly.w_gate; gu.W2 = ly.w_up;
       gu.N = m->d_ffn; gu.K = m->d; gu.C = s.h; gu.ldc = m->d_ffn;
       EC_TRY(ec::launch_gemm_rows(gu, s.gemm_ws, stream));
       ec::GemmArgs gd;
       gd.dtype = dt; gd.epi = ec::Epi::kResidual; gd.A = s.h; gd.lda = m->d_ffn;
-      gd.n_rows_dev = st->n_rows; gd.max_rows = L; gd.skinny_rows = sk_rows; gd.W = ly.w_down; gd.N = m->d; gd.K = m->d_ffn;
+      gd.n_rows_dev = st->n_rows; gd.max_rows = hi; gd.skinny_rows = sk_rows; gd.paths = paths; gd.W = ly.w_down; gd.N = m->d; gd.K = m->d_ffn;
       gd.C = s.x; gd.ldc = m->d;
       EC_TRY(ec::launch_gemm_rows(gd, s.gemm_ws, stream));
       if (first) EC_TRY(tm.end(EC_PHASE_FFN));
@@ -395,7 +404,7 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   EC_TRY(tm.begin(EC_PHASE_LMHEAD));
   const void* xf = s.x;
   if (m->d_ffn) {
-    EC_TRY(ec::launch_rmsnorm(dt, s.x, st->n_rows, L, m->d, m->norm_final, m->rms_eps, s.a, stream));
+    EC_TRY(ec::launch_rmsnorm(dt, s.x, st->n_rows, hi, m->d, m->norm_final, m->rms_eps, s.a, stream));
     xf = s.a;
   }
   ec::GemmArgs gl;

@@ -62,6 +62,12 @@ enum class Epi : int {
   kSwiGLU = 3,    // C[r, n] = silu(acc) * acc2, acc2 from W2
   kLogits = 4,    // C[r, n] = acc * scale[scale_pos[r]]  (scale may be NULL)
 };
+// Launch paths of the row-count-dependent operations: device row counts up
+// to kSmallMaxRows (skinny GEMM, split-KV attention) or above (tiled GEMM,
+// unsplit attention).
+constexpr int kSmallMaxRows = 128;
+constexpr unsigned kPathSmall = 1u, kPathLarge = 2u;
+
 struct GemmArgs {
   int dtype = 0;
   Epi epi = Epi::kStore;
@@ -74,6 +80,11 @@ struct GemmArgs {
   // most 128 (the rows the skinny kernel takes); 0 = max_rows.  The caller
   // guarantees it: rows past the bound would be left unwritten.
   int skinny_rows = 0;
+  // Kernels to launch: kPathSmall (skinny kernel and its split-K reduction,
+  // device row counts <= 128) and/or kPathLarge (tiled kernel, counts > 128).
+  // Each exits at once on a count outside its range; a caller that knows the
+  // count's range may leave the other out.
+  unsigned paths = kPathSmall | kPathLarge;
   const void* W = nullptr;
   const void* W2 = nullptr;
   int N = 0, K = 0;
@@ -116,6 +127,9 @@ struct AttnArgs {
   int L = 0, L_cap = 0, Hq = 0, Hkv = 0, dh = 0;
   float scale = 1.f;
   void* out = nullptr;                // [max_rows, Hq, dh]
+  // kPathSmall: split-KV kernel and merge (<= 128 rows); kPathLarge: unsplit
+  // kernel (> 128 rows), as for GemmArgs.
+  unsigned paths = kPathSmall | kPathLarge;
 };
 size_t attn_ws_bytes(int max_rows, int L, int Hq, int Hkv, int dh);
 hipError_t launch_attention(const AttnArgs& a, void* ws, hipStream_t s);

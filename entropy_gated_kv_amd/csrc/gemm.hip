@@ -36,7 +36,7 @@ namespace ec {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSkinnyMaxRows = 128;
+constexpr int kSkinnyMaxRows = kSmallMaxRows;
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16_t> {
@@ -792,16 +792,18 @@ hipError_t launch_typed(const GemmArgs& a, void* ws, hipStream_t s, bool allow_s
   if (!allow_split || ws == nullptr) { pl.S = 1; pl.KS = a.K; }
   p.S = pl.S; p.KS = pl.KS;
   p.part = static_cast<float*>(ws);
-  const size_t lds_sk = size_t(pl.MBX) * 16 * (skit<T>() * sizeof(T) + 16);
-  const dim3 g_sk(unsigned(pl.tiles * pl.S));
-  hipError_t e = dispatch_skinny<T>(a.epi, pl, g_sk, lds_sk, s, p);
-  if (e != hipSuccess) return e;
-  if (pl.S > 1) {
-    const int64_t outs = int64_t(min(a.max_rows, kSkinnyMaxRows)) * a.N;
-    e = dispatch_split_epi<T>(a.epi, dim3(unsigned((outs + kThreads - 1) / kThreads)), s, p);
+  if (a.paths & kPathSmall) {
+    const size_t lds_sk = size_t(pl.MBX) * 16 * (skit<T>() * sizeof(T) + 16);
+    const dim3 g_sk(unsigned(pl.tiles * pl.S));
+    hipError_t e = dispatch_skinny<T>(a.epi, pl, g_sk, lds_sk, s, p);
     if (e != hipSuccess) return e;
+    if (pl.S > 1) {
+      const int64_t outs = int64_t(min(a.max_rows, kSkinnyMaxRows)) * a.N;
+      e = dispatch_split_epi<T>(a.epi, dim3(unsigned((outs + kThreads - 1) / kThreads)), s, p);
+      if (e != hipSuccess) return e;
+    }
   }
-  if (a.max_rows <= kSkinnyMaxRows) return hipSuccess;
+  if (a.max_rows <= kSkinnyMaxRows || !(a.paths & kPathLarge)) return hipSuccess;
 
   if constexpr (sizeof(T) == 2) {
     // the direct-to-LDS kernel takes 32-bit copy offsets and no row gather

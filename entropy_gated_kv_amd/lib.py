@@ -16,10 +16,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libec.so")
 
 EC_F32, EC_BF16 = 0, 1
+EC_MODE_DEVICE, EC_MODE_FULL, EC_MODE_PARTIAL = 0, 1, 2
 PHASES = ("select", "embed", "qkv", "attn", "oproj", "ffn", "lmhead", "entropy", "decide")
 
 _lib: Optional[C.CDLL] = None
-ABI_VERSION = 2                  # EC_ABI_VERSION of include/ec.h
+ABI_VERSION = 3                  # EC_ABI_VERSION of include/ec.h
 
 
 class EcError(RuntimeError):
@@ -55,7 +56,7 @@ class ec_state(C.Structure):
 
 class ec_step_cfg(C.Structure):
     _fields_ = [("tau", C.c_float), ("k", C.c_int32), ("n_unmask", C.c_int32),
-                ("block_start", C.c_int32), ("block_len", C.c_int32)]
+                ("block_start", C.c_int32), ("block_len", C.c_int32), ("mode", C.c_int32)]
 
 
 _P, _I32, _I64, _F32, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t

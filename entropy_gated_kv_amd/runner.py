@@ -125,9 +125,22 @@ class DeviceSequence:
         self.struct.kv_drift = self.kv_drift.data_ptr()
 
     def step(self, tau: float, k: int, block_start: int, block_len: int, n_unmask: int,
-             phase_events=None) -> None:
-        cfg = L.ec_step_cfg(float(tau), int(k), int(n_unmask), int(block_start), int(block_len))
+             phase_events=None, mode: int = L.EC_MODE_DEVICE) -> None:
+        """One ec_step.  mode: EC_MODE_DEVICE (the flag stays on the device), or
+        EC_MODE_FULL / EC_MODE_PARTIAL when the caller has read full_flag."""
+        cfg = L.ec_step_cfg(float(tau), int(k), int(n_unmask), int(block_start), int(block_len),
+                            int(mode))
         L.ec_step(self.model.struct, self.struct, cfg, self.ws, phase_events)
+
+    def step_host_mode(self, tau: float, k: int, block_start: int, block_len: int, n_unmask: int,
+                       phase_events=None) -> int:
+        """One step whose mode the host reads first (a 4-byte copy that waits
+        for the previous step), so only that mode's kernels are launched.
+        Returns the mode used (1 full, 0 partial)."""
+        full = int(self.full_flag.item())
+        self.step(tau, k, block_start, block_len, n_unmask, phase_events,
+                  L.EC_MODE_FULL if full else L.EC_MODE_PARTIAL)
+        return full
 
     def step_external(self, tau: float, k: int, block_start: int, block_len: int, decoded_logits,
                       phase_events=None) -> None:

@@ -54,7 +54,7 @@ const char* ec_status_string(int32_t status);
 
 /* ABI revision of this header; bumped on any signature or struct change. */
 int32_t ec_abi_version(void);
-#define EC_ABI_VERSION 2
+#define EC_ABI_VERSION 3
 
 /* --------------------------------------------------------------------------
  * Entropy pass (a1) and decision (a2).
@@ -283,12 +283,23 @@ typedef struct ec_state {
   float* kv_drift;
 } ec_state;
 
+/* Step modes (ec_step_cfg.mode).  EC_MODE_DEVICE: the mode is read from
+ * *full_flag on the device and the kernels of both modes are launched (those
+ * of the other mode exit at once), so the host never waits.  EC_MODE_FULL /
+ * EC_MODE_PARTIAL: the caller states what *full_flag holds (having read it
+ * after the previous step) and only that mode's kernels are launched, which
+ * saves one launch per GEMM and per attention call.  A statement that differs
+ * from *full_flag leaves the step's results undefined (every access stays in
+ * bounds). */
+enum { EC_MODE_DEVICE = 0, EC_MODE_FULL = 1, EC_MODE_PARTIAL = 2 };
+
 typedef struct ec_step_cfg {
   float tau;
   int32_t k;
   int32_t n_unmask;
   int32_t block_start;        /* or -1: sliding window (see ec_select_rows) */
   int32_t block_len;          /* <= max_block of the workspace             */
+  int32_t mode;               /* EC_MODE_* (EC_E_SHAPE otherwise)          */
 } ec_step_cfg;
 
 /* Optional per-phase timing: when non-NULL, phase_events holds 2*EC_PHASE_COUNT

@@ -221,3 +221,38 @@ def test_workspace_contents_do_not_matter():
     for a, b in zip(*out):
         for x, y in zip(a, b):
             assert np.array_equal(np.asarray(x), np.asarray(y))
+
+
+@pytest.mark.parametrize("case", ["tiny_fp32", "tiny_fp32_k100", "stack_bf16"])
+def test_host_stated_mode_matches_device_mode(case):
+    """A step whose mode the host read from full_flag (only that mode's kernels
+    launched) equals the device-decided step bit for bit, step by step.  k = 100
+    makes the partial-row bound exceed 128, so partial steps launch both paths."""
+    cfg = C.TINY if case.startswith("tiny") else gpu_stack_cfg()
+    k = 100 if case.endswith("k100") else cfg.k
+    tau = math.inf if case.startswith("tiny") else 1.0
+    runs = []
+    for host in (False, True):
+        w = G.model_weights(cfg)
+        toks, masked = G.initial_sequence(cfg)
+        dm = DeviceModel(cfg.model, cfg.dtype, cfg.L, w)
+        ds = DeviceSequence(dm, toks, masked, history_cap=max(cfg.gen_len, k), max_block=cfg.block_len)
+        trace = []
+        for bs, bl, n in C.unmask_schedule(cfg)[:12]:
+            if host:
+                mode = ds.step_host_mode(tau, k, bs, bl, n)
+            else:
+                mode = int(ds.full_flag.item())
+                ds.step(tau, k, bs, bl, n)
+            g = read(ds, bl)
+            caches = [np.concatenate([a.ravel() for a in ds.caches(l)]) for l in range(cfg.model.n_layers)]
+            trace.append((mode, g["rows"], g["chosen"], g["tokens"], g["logits"], g["E"], g["flag"], caches))
+        runs.append(trace)
+    modes = [t[0] for t in runs[0]]
+    assert 1 in modes and 0 in modes, modes
+    for i, (a, b) in enumerate(zip(*runs)):
+        assert a[0] == b[0], i
+        for x, y in zip(a[1:7], b[1:7]):
+            assert np.array_equal(np.asarray(x), np.asarray(y)), i
+        for x, y in zip(a[7], b[7]):
+            assert np.array_equal(x, y), i
