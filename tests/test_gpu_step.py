@@ -195,6 +195,17 @@ def test_bf16_two_layer_stack_teacher_forced(tile, monkeypatch):
     assert n_partial > 3 and ties <= 2
 
 
+def test_bf16_stack_split_k_teacher_forced():
+    """Two layers at d = 1024 (8 x 128 heads, SwiGLU 2048): on partial steps
+    every GEMM of the stack splits K (QKV, O-projection and SwiGLU two ways,
+    the down-projection four), so the residual reductions run inside a stack."""
+    cfg = C.scaled(C.LLADA_STACK, name="stack_split", model_n_layers=2, model_d=1024,
+                   model_n_q_heads=8, model_n_kv_heads=8, model_head_dim=128, model_vocab=2048,
+                   model_d_ffn=2048, prompt_len=96, gen_len=64, block_len=32, k=16)
+    ties, n_partial = check_teacher_forced(cfg, 12, 1.0)
+    assert n_partial > 3 and ties <= 2
+
+
 def test_llada_layer_full_size_two_steps():
     """LLaDA-shaped layer at full size (L = 1024, V = 126464): one full step and
     one partial step, teacher forced, every candidate's logits compared."""
