@@ -123,6 +123,35 @@ def test_tiny_fp32_sliding_window_free_running(tau):
     assert not st.masked.any(), n_steps         # the window reached the end of the sequence
 
 
+def short_cfg(dtype="f32"):
+    # L = 96 <= 128: a full step's rows all go through the small-row kernels
+    # (skinny GEMM, split-KV attention)
+    return C.scaled(C.TINY, name=f"short_{dtype}", dtype=dtype, prompt_len=64, gen_len=32, block_len=32)
+
+
+@pytest.mark.parametrize("tau", [1.5, math.inf])
+def test_short_sequence_fp32_free_running(tau):
+    cfg = short_cfg()
+    model, st, dm, ds = setup(cfg)
+    for i, (bs, bl, n) in enumerate(C.unmask_schedule(cfg)):
+        tr = O.step(model, st, tau, cfg.k, bs, bl, n)
+        ds.step(tau, cfg.k, bs, bl, n)
+        g = read(ds, len(tr.cand))
+        np.testing.assert_array_equal(g["rows"], tr.rows, err_msg=f"step {i} rows")
+        np.testing.assert_array_equal(g["chosen"], tr.chosen, err_msg=f"step {i} chosen")
+        np.testing.assert_array_equal(g["tokens"], st.tokens, err_msg=f"step {i} tokens")
+        assert g["flag"] == tr.flag_next, i
+        assert_close(g["logits"], tr.logits, "f32", f"step {i} logits")
+    k, v = ds.caches(0)
+    assert_close(k, st.K[0], "f32", "final K cache")
+    assert_close(v, st.V[0], "f32", "final V cache")
+
+
+def test_short_sequence_bf16_teacher_forced():
+    ties, n_partial = check_teacher_forced(short_cfg("bf16"), 8, math.inf)
+    assert n_partial == 7 and ties <= 2
+
+
 def logit_tol(model, tr):
     sp = np.ones(len(tr.cand)) if model.logit_scale is None else model.logit_scale[tr.cand]
     prop = sp[:, None] * (np.abs(tr.x_cand) @ np.abs(model.w_lm).T) * 2.0 ** -7
@@ -234,14 +263,14 @@ def test_workspace_contents_do_not_matter():
             assert np.array_equal(np.asarray(x), np.asarray(y))
 
 
-@pytest.mark.parametrize("case", ["tiny_fp32", "tiny_fp32_k100", "stack_bf16"])
+@pytest.mark.parametrize("case", ["tiny_fp32", "tiny_fp32_k100", "short_fp32", "stack_bf16"])
 def test_host_stated_mode_matches_device_mode(case):
     """A step whose mode the host read from full_flag (only that mode's kernels
     launched) equals the device-decided step bit for bit, step by step.  k = 100
     makes the partial-row bound exceed 128, so partial steps launch both paths."""
-    cfg = C.TINY if case.startswith("tiny") else gpu_stack_cfg()
+    cfg = {"tiny": C.TINY, "short": short_cfg(), "stack": gpu_stack_cfg()}[case.split("_")[0]]
     k = 100 if case.endswith("k100") else cfg.k
-    tau = math.inf if case.startswith("tiny") else 1.0
+    tau = 1.0 if case.startswith("stack") else math.inf
     runs = []
     for host in (False, True):
         w = G.model_weights(cfg)
