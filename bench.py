@@ -286,7 +286,7 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         "roofline": {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("gemm_skinny_kernel<bf16,lmhead>", "gemm.hip", 1),
-                     "kernel": "LM-head skinny GEMM (gemm_skinny_kernel<bf16, 2, false, 4>)",
+                     "kernel": "LM-head skinny GEMM (gemm_skinny_kernel<bf16, 2, false, 4, 8>)",
                      "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)},
     }
     _log(f"step: {out['value']:.1f} steps/s, {out['ms_per_step'] * 1e3:.1f} us/step, "

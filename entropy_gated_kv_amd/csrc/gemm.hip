@@ -149,12 +149,17 @@ template <> struct Mma16<float> {
 
 constexpr int kNV = 4;                       // 16-B vectors per lane per iteration
 constexpr int kSkinnyNT = 64;                // output columns per workgroup
-template <typename T> constexpr int skit() { return kNV * 4 * (16 / int(sizeof(T))); }  // k per iteration
+// k per iteration with NV vectors per lane
+template <typename T, int NV = kNV> constexpr int skit() { return NV * 4 * (16 / int(sizeof(T))); }
 
-template <typename T, int MB, bool DUAL, int EPI>
+// NV: 16-B vectors per lane per iteration.  Four everywhere but the LM head,
+// which streams its weights 3-4% faster with eight (512 contiguous bytes of
+// each of a wave's 16 rows per iteration, half the barriers per byte); at
+// four the smaller ring leaves registers for the larger row bounds.
+template <typename T, int MB, bool DUAL, int EPI, int NV>
 __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem) {
   constexpr int VPL = 16 / int(sizeof(T));
-  constexpr int KIT = skit<T>();
+  constexpr int KIT = skit<T, NV>();
   constexpr int ROWB = KIT * int(sizeof(T)) + 16;           // LDS row pitch (bytes), padded
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
   const int b = blockIdx.x;
@@ -197,10 +202,10 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
       *reinterpret_cast<u32x4*>(smem + r * ROWB + c * 16) = areg[i];
     }
   };
-  typedef u32x4 WBuf[kNV];
+  typedef u32x4 WBuf[NV];
   auto w_load = [&](WBuf& dst, const T* src, int it) {
 #pragma unroll
-    for (int v = 0; v < kNV; ++v)
+    for (int v = 0; v < NV; ++v)
       dst[v] = *reinterpret_cast<const u32x4*>(src + it * KIT + v * 4 * VPL);
   };
 
@@ -219,7 +224,7 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
     w_load(nxt, Wp, min(it + 2, last));
     if constexpr (DUAL) w_load(nxt2, W2p, min(it + 2, last));
 #pragma unroll
-    for (int v = 0; v < kNV; ++v) {
+    for (int v = 0; v < NV; ++v) {
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(smem + (rb * 16 + (lane & 15)) * ROWB +
@@ -285,18 +290,18 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
 // row count.  Each instance holds only the bodies up to MBX, so its register
 // footprint (and with it the waves per SIMD) follows the bound: at 96 rows the
 // six-block instance keeps three waves per SIMD where the eight-block one has two.
-template <typename T, int MBX, bool DUAL, int EPI>
+template <typename T, int MBX, bool DUAL, int EPI, int NV = kNV>
 __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(GP p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int n_rows = min(*p.n_rows, p.max_rows);
   if (n_rows <= 0 || n_rows > kSkinnyMaxRows) return;
   const int mb = (n_rows + 15) / 16;
-  if (MBX == 2 || mb <= 2) skinny_body<T, 2, DUAL, EPI>(p, n_rows, smem);
+  if (MBX == 2 || mb <= 2) skinny_body<T, 2, DUAL, EPI, NV>(p, n_rows, smem);
   else if constexpr (MBX >= 4) {
-    if (MBX == 4 || mb <= 4) skinny_body<T, 4, DUAL, EPI>(p, n_rows, smem);
+    if (MBX == 4 || mb <= 4) skinny_body<T, 4, DUAL, EPI, NV>(p, n_rows, smem);
     else if constexpr (MBX >= 6) {
-      if (MBX == 6 || mb <= 6) skinny_body<T, 6, DUAL, EPI>(p, n_rows, smem);
-      else if constexpr (MBX == 8) skinny_body<T, 8, DUAL, EPI>(p, n_rows, smem);
+      if (MBX == 6 || mb <= 6) skinny_body<T, 6, DUAL, EPI, NV>(p, n_rows, smem);
+      else if constexpr (MBX == 8) skinny_body<T, 8, DUAL, EPI, NV>(p, n_rows, smem);
     }
   }
 }
@@ -704,7 +709,7 @@ void tiled_by_cfg(int c, const GP& p, hipStream_t s) {
 int mbx_of(int rows) { return rows <= 32 ? 2 : rows <= 64 ? 4 : rows <= 96 ? 6 : 8; }
 
 struct Plan {
-  int MBX, S, KS, tiles;
+  int MBX, NV, S, KS, tiles;
   size_t part_floats;
 };
 
@@ -714,7 +719,11 @@ Plan plan_skinny(const GemmArgs& a) {
   const bool dual = (a.epi == Epi::kSwiGLU);
   pl.MBX = mbx_of(a.skinny_rows > 0 && a.skinny_rows < a.max_rows ? a.skinny_rows : a.max_rows);
   pl.tiles = (a.N + kSkinnyNT - 1) / kSkinnyNT;
-  const int KIT = skit<T>();
+  // eight vectors per lane for the LM head (<= 32 rows, enough tiles that K
+  // is never split, K a multiple of the longer iteration)
+  pl.NV = (a.epi == Epi::kLogits && pl.MBX == 2 && pl.tiles >= 512 && a.K % skit<T, 2 * kNV>() == 0)
+              ? 2 * kNV : kNV;
+  const int KIT = pl.NV == kNV ? skit<T>() : skit<T, 2 * kNV>();
   const int iters = (a.K + KIT - 1) / KIT;
   // Split K into equal whole iterations only when the column tiles alone
   // leave most CUs idle: the smallest split count (any divisor of the
@@ -740,9 +749,9 @@ Plan plan_skinny(const GemmArgs& a) {
 
 size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
 
-template <typename T, int MBX, bool DUAL, int EPI>
+template <typename T, int MBX, bool DUAL, int EPI, int NV = kNV>
 void go_skinny(dim3 g, size_t lds, hipStream_t s, const GP& p) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, MBX, DUAL, EPI>), g, dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, MBX, DUAL, EPI, NV>), g, dim3(kThreads), lds, s, p);
 }
 
 template <typename T, int EPI, bool DUAL = false>
@@ -760,7 +769,10 @@ hipError_t dispatch_skinny(Epi epi, const Plan& pl, dim3 g, size_t lds, hipStrea
     case Epi::kQKV: skinny_by_shape<T, 1>(pl, g, lds, s, p); break;
     case Epi::kResidual: skinny_by_shape<T, 2>(pl, g, lds, s, p); break;
     case Epi::kSwiGLU: skinny_by_shape<T, 3, true>(pl, g, lds, s, p); break;
-    case Epi::kLogits: skinny_by_shape<T, 4>(pl, g, lds, s, p); break;
+    case Epi::kLogits:
+      if (pl.NV == 2 * kNV) go_skinny<T, 2, false, 4, 2 * kNV>(g, lds, s, p);
+      else skinny_by_shape<T, 4>(pl, g, lds, s, p);
+      break;
   }
   return hipGetLastError();
 }
@@ -793,7 +805,8 @@ hipError_t launch_typed(const GemmArgs& a, void* ws, hipStream_t s, bool allow_s
   p.S = pl.S; p.KS = pl.KS;
   p.part = static_cast<float*>(ws);
   if (a.paths & kPathSmall) {
-    const size_t lds_sk = size_t(pl.MBX) * 16 * (skit<T>() * sizeof(T) + 16);
+    const int kit_sk = pl.NV == kNV ? skit<T>() : skit<T, 2 * kNV>();
+    const size_t lds_sk = size_t(pl.MBX) * 16 * (kit_sk * sizeof(T) + 16);
     const dim3 g_sk(unsigned(pl.tiles * pl.S));
     hipError_t e = dispatch_skinny<T>(a.epi, pl, g_sk, lds_sk, s, p);
     if (e != hipSuccess) return e;
