@@ -123,6 +123,44 @@ def test_tiny_fp32_sliding_window_free_running(tau):
     assert not st.masked.any(), n_steps         # the window reached the end of the sequence
 
 
+@pytest.mark.parametrize("case", ["k0", "steps_unmasking_nothing", "k_equals_ring_capacity"])
+def test_tiny_fp32_edge_schedules(case):
+    """k = 0 (partial steps refresh the block's masked rows only); steps that
+    unmask nothing (E = -inf, so the next step is partial whatever tau); k equal
+    to a 16-entry history ring that wraps four times.  Free-running against the
+    oracle, which keeps the whole history as a list."""
+    cfg = C.TINY
+    w = G.model_weights(cfg)
+    model = O.Model.from_arrays(cfg.model, cfg.dtype, w)
+    toks, masked = G.initial_sequence(cfg)
+    st = O.init_state(model, toks, masked)
+    dm = DeviceModel(cfg.model, cfg.dtype, cfg.L, w)
+    cap = 16 if case == "k_equals_ring_capacity" else cfg.gen_len
+    ds = DeviceSequence(dm, toks, masked, history_cap=cap, max_block=cfg.block_len)
+    k = 0 if case == "k0" else 16
+    sched = C.unmask_schedule(cfg)
+    if case == "steps_unmasking_nothing":
+        sched = [(bs, bl, n if i % 2 == 0 else 0) for i, (bs, bl, n) in enumerate(sched + sched)][:24]
+    # tau = 1.5: every step that decodes sends the next to a full recompute
+    # (E is about 6.9 nats), so partial steps follow only the empty ones;
+    # tau = +inf: every step after the first is partial
+    tau = 1.5 if case == "steps_unmasking_nothing" else math.inf
+    modes = []
+    for i, (bs, bl, n) in enumerate(sched):
+        modes.append(int(ds.full_flag.item()))
+        tr = O.step(model, st, tau, k, bs, bl, n)
+        ds.step(tau, k, bs, bl, n)
+        g = read(ds, len(tr.cand))
+        np.testing.assert_array_equal(g["rows"], tr.rows, err_msg=f"step {i} rows")
+        np.testing.assert_array_equal(g["chosen"], tr.chosen, err_msg=f"step {i} chosen")
+        np.testing.assert_array_equal(g["tokens"], st.tokens, err_msg=f"step {i} tokens")
+        assert g["flag"] == tr.flag_next, i
+        if n == 0:
+            assert g["E"] == -math.inf and g["flag"] == 0, i
+        assert_close(g["logits"], tr.logits, "f32", f"step {i} logits")
+    assert 0 in modes and 1 in modes, modes
+
+
 def short_cfg(dtype="f32"):
     # L = 96 <= 128: a full step's rows all go through the small-row kernels
     # (skinny GEMM, split-KV attention)
