@@ -42,11 +42,66 @@ def _log(msg: str) -> None:
 
 
 def _src_hash(*names: str) -> str:
+    """Hash of the code of kernel sources: comments and blank space are left
+    out, so only a change to the code itself voids recorded counters."""
+    import re
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "entropy_gated_kv_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "entropy_gated_kv_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
+
+
+# kernels whose HBM traffic is recorded: the name fragment the counter rows
+# carry, the source file, and which launches count (all, or the largest grid)
+TRAFFIC_KERNELS = {
+    "entropy_partials_kernel<bf16>": ("entropy_partials_kernel<ec::bf16_t>", "entropy.hip", "largest"),
+    "gemm_skinny_kernel<bf16,lmhead>": ("gemm_skinny_kernel<ec::bf16_t, 2, false, 4, 8>", "gemm.hip", "all"),
+}
+
+
+def record_traffic(fetch_dir: str, write_dir: str) -> dict:
+    """Turn two `rocprofv3 --pmc` runs of `bench.py --profile-mode` (FETCH_SIZE,
+    then WRITE_SIZE; CSV output directories) into profiles/traffic.json.  Each
+    counter is scaled by what it reads for the profile mode's 1 GiB copies."""
+    import csv
+    import glob
+
+    def rows(d):
+        (path,) = glob.glob(os.path.join(d, "*counter_collection.csv"))
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    f_rows, w_rows = rows(fetch_dir), rows(write_dir)
+    gib_kib = float(1 << 20)
+    copy_grid = str(1 << 17)       # the 1 GiB copies' grid (threads)
+
+    def mean(rs, frag, grid=None):
+        v = [float(r["Counter_Value"]) for r in rs
+             if frag in r["Kernel_Name"] and (grid is None or r["Grid_Size"] == grid)]
+        if not v:
+            raise RuntimeError(f"no counter rows for {frag}")
+        return sum(v) / len(v), len(v)
+
+    cal_f, _ = mean(f_rows, "copyBuffer", copy_grid)
+    cal_w, _ = mean(w_rows, "copyBuffer", copy_grid)
+    sf, sw = gib_kib / cal_f, gib_kib / cal_w
+    rec = {"_calibration": {"copy_bytes": 1 << 30, "fetch_kib": cal_f, "write_kib": cal_w,
+                            "fetch_scale": sf, "write_scale": sw}}
+    for key, (frag, src, which) in TRAFFIC_KERNELS.items():
+        grid = None
+        if which == "largest":
+            grid = str(max(int(r["Grid_Size"]) for r in f_rows if frag in r["Kernel_Name"]))
+        fk, n = mean(f_rows, frag, grid)
+        wk, _ = mean(w_rows, frag, grid)
+        rec[key] = {"src_hash": _src_hash(src), "fetch_kib": fk, "write_kib": wk,
+                    "bytes_per_launch": round((fk * sf + wk * sw) * 1024), "launches": n}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
 
 
 def _traffic(kernel: str, src: str, per_launch_units: float):
@@ -750,7 +805,12 @@ def main() -> int:
                     help="skip the step leg (diagnostics only: no headline value)")
     ap.add_argument("--profile-mode", action="store_true",
                     help="run the fixed short sequence used for hardware-counter runs")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two counter runs of --profile-mode")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(*args.record_traffic), indent=1))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the design notes describe how the step would shard)", file=sys.stderr)

@@ -7,17 +7,19 @@
 // output projection and FFN with residual adds, and the LM head over the
 // block's masked rows.
 //
-// Two tilings, both launched; each reads the row count from device memory and
-// the one that does not apply exits at once, so no row count crosses to the
-// host:
+// Two tilings.  By default both are launched; each reads the row count from
+// device memory and the one that does not apply exits at once, so no row
+// count crosses to the host (a caller that knows the count's range launches
+// only its tiling, GemmArgs::paths):
 //  * skinny (n <= 128, partial steps and the LM head): weights are streamed
 //    from HBM exactly once across the grid.  A workgroup owns 64 output
 //    columns (16 per wave) and a K range; the selected rows' A slice is staged
 //    in LDS per iteration and shared by the four waves; W fragments go
-//    global -> registers two iterations ahead (16x16x32 MFMA).  When the
-//    column tiles alone cannot fill the chip the K range is split over
-//    workgroups and a second kernel sums the partials in split order
-//    (deterministic) and runs the epilogue.
+//    global -> registers two iterations ahead (16x16x32 MFMA).  One instance
+//    per bound on the row count (32 / 64 / 96 / 128).  When the column tiles
+//    alone cannot fill the chip the K range is split over workgroups and a
+//    second kernel sums the partials in split order (deterministic) and runs
+//    the epilogue.
 //  * tiled (n > 128, full steps): BM x BN output tiles (128 x 128 up to
 //    256 x 256, chosen per shape), A and W tiles copied global -> LDS
 //    directly, 64 k per stage (32x32x16 MFMA); an fp32 variant stages
@@ -120,12 +122,13 @@ __device__ __forceinline__ int acc_row(int j, int lane) { return 8 * (j >> 2) + 
 // MFMA 16x16x32 bf16 / 16x16x4 fp32.  A wave owns 16 weight rows (output
 // columns).  Lane (n = l%16, g = l/16) loads, per iteration, NV vectors of
 // 16 B at k-offset (v*4 + g)*VPL, v = 0..NV-1: the four lanes of a row read
-// 64 contiguous bytes per instruction and the wave walks 256 B of each of its
-// 16 rows per iteration -- the access pattern that keeps HBM streaming at
-// ~5.5 TB/s on this part, where 32 rows x 32 B per instruction reach ~3 TB/s.
-// Four vectors per iteration rather than eight: the smaller W ring and A
-// stage leave registers for two waves per SIMD at up to 128 rows (one wave
-// with eight), which measured 25% faster at 96 rows.
+// 64 contiguous bytes per instruction and the wave walks NV * 64 B of each of
+// its 16 rows per iteration -- the access pattern that keeps HBM streaming at
+// ~5-5.5 TB/s on this part, where 32 rows x 32 B per instruction reach ~3 TB/s.
+// NV = 4 (256 B per row per iteration) for every shape but the LM head, which
+// takes 8: the smaller W ring and A stage leave registers for more waves per
+// SIMD at up to 128 rows (25% faster at 96 rows than eight), while the LM
+// head's long unsplit stream gains 3-4% from 512 B per row per iteration.
 // For bf16 that is exactly the MFMA's own operand layout (k = 32v + 8g + i);
 // for fp32 each 16-B vector feeds four 16x16x4 MFMAs.  W fragments sit in a
 // ring of three register buffers (loads run two iterations ahead); the
