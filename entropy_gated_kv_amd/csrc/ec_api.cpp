@@ -423,7 +423,7 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   EC_TRY(ec::launch_choose_decide(s.cand_pos, s.n_cand, st->row_entropy, st->row_argmax,
                                   st->row_top1, c->n_unmask, c->tau, st->chosen, st->n_chosen,
                                   st->tokens, st->is_masked, st->history, st->history_len,
-                                  st->history_cap, st->e_max, st->full_flag, stream));
+                                  st->history_cap, st->e_max, st->full_flag, max_block, stream));
   EC_TRY(tm.end(EC_PHASE_DECIDE));
   return EC_OK;
 }

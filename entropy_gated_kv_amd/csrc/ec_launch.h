@@ -50,7 +50,8 @@ hipError_t launch_choose_decide(const int32_t* cand_pos, const int32_t* n_cand, 
                                 const int32_t* argmax, const float* p1, int32_t n_unmask,
                                 float tau, int32_t* chosen, int32_t* n_chosen, int32_t* tokens,
                                 uint8_t* is_masked, int32_t* history, int32_t* history_len,
-                                int32_t history_cap, float* e_max, int32_t* flag, hipStream_t s);
+                                int32_t history_cap, float* e_max, int32_t* flag, int32_t max_cand,
+                                hipStream_t s);
 
 // ---- row GEMM with fused epilogues ---------------------------------------------
 // C[r, n] = sum_k A[row(r), k] * W[n, k] for r < *n_rows_dev (<= max_rows), n < N,

@@ -146,22 +146,26 @@ __global__ __launch_bounds__(kChooseThreads) void choose_decide_kernel(
     const float* __restrict__ p1, int32_t n_unmask, float tau, int32_t* __restrict__ chosen,
     int32_t* __restrict__ n_chosen, int32_t* __restrict__ tokens, uint8_t* __restrict__ is_masked,
     int32_t* __restrict__ history, int32_t* __restrict__ history_len, int32_t history_cap,
-    float* __restrict__ e_max, int32_t* __restrict__ flag) {
+    float* __restrict__ e_max, int32_t* __restrict__ flag, int32_t max_cand) {
   __shared__ float s_p1[kChooseThreads];
   __shared__ int s_pos[kChooseThreads];
   __shared__ int s_cnt[kChooseThreads / kWave + 1];
   __shared__ float s_max[kChooseThreads / kWave];
   __shared__ int s_nan[kChooseThreads / kWave];
   const int tid = threadIdx.x;
-  const int nc = min(*n_cand, kChooseThreads);
+  const int nwv = int(blockDim.x) / kWave;               // the launch covers max_cand threads
+  // every per-candidate load goes out at once: the arrays hold max_cand
+  // entries, whatever the device count says
+  float pi = 0.f, h = 0.f;
+  int posi = 0, am = 0;
+  if (tid < max_cand) { pi = p1[tid]; posi = cand_pos[tid]; h = H[tid]; am = argmax[tid]; }
+  const int nc = min(*n_cand, max_cand);
   const int ns = min(n_unmask, nc);
   const int hl = *history_len;
-  if (tid < nc) { s_p1[tid] = p1[tid]; s_pos[tid] = cand_pos[tid]; }
+  if (tid < nc) { s_p1[tid] = pi; s_pos[tid] = posi; }
   __syncthreads();
   bool pick = false;
   if (tid < nc) {
-    const float pi = s_p1[tid];
-    const int posi = s_pos[tid];
     int rank = 0;
     for (int j = 0; j < nc; ++j) rank += better(s_p1[j], s_pos[j], pi, posi) ? 1 : 0;
     pick = rank < ns;
@@ -179,20 +183,18 @@ __global__ __launch_bounds__(kChooseThreads) void choose_decide_kernel(
   __syncthreads();
   if (tid == 0) {
     int acc = 0;
-    for (int k = 0; k < kChooseThreads / kWave; ++k) { const int t = s_cnt[k]; s_cnt[k] = acc; acc += t; }
-    s_cnt[kChooseThreads / kWave] = acc;
+    for (int k = 0; k < nwv; ++k) { const int t = s_cnt[k]; s_cnt[k] = acc; acc += t; }
+    s_cnt[nwv] = acc;
   }
   __syncthreads();
   float hmax = -INFINITY;
   int hnan = 0;
   if (pick) {
     const int slot = s_cnt[w] + incl - v;
-    const int pos = s_pos[tid];
-    chosen[slot] = pos;
-    tokens[pos] = argmax[tid];
-    is_masked[pos] = 0;
-    history[(hl + slot) % history_cap] = pos;
-    const float h = H[tid];
+    chosen[slot] = posi;
+    tokens[posi] = am;
+    is_masked[posi] = 0;
+    history[(hl + slot) % history_cap] = posi;
     if (h != h) hnan = 1; else hmax = h;
   }
   hmax = wave_max(hmax);
@@ -202,8 +204,8 @@ __global__ __launch_bounds__(kChooseThreads) void choose_decide_kernel(
   if (tid == 0) {
     float b = -INFINITY;
     int n = 0;
-    for (int k = 0; k < kChooseThreads / kWave; ++k) { b = fmaxf(b, s_max[k]); n += s_nan[k]; }
-    const int total = s_cnt[kChooseThreads / kWave];
+    for (int k = 0; k < nwv; ++k) { b = fmaxf(b, s_max[k]); n += s_nan[k]; }
+    const int total = s_cnt[nwv];
     const float E = n ? NAN : b;
     *n_chosen = total;
     *history_len = hl + total;
@@ -247,10 +249,13 @@ hipError_t launch_choose_decide(const int32_t* cand_pos, const int32_t* n_cand, 
                                 const int32_t* argmax, const float* p1, int32_t n_unmask,
                                 float tau, int32_t* chosen, int32_t* n_chosen, int32_t* tokens,
                                 uint8_t* is_masked, int32_t* history, int32_t* history_len,
-                                int32_t history_cap, float* e_max, int32_t* flag, hipStream_t s) {
-  hipLaunchKernelGGL(choose_decide_kernel, dim3(1), dim3(kChooseThreads), 0, s, cand_pos, n_cand, H,
+                                int32_t history_cap, float* e_max, int32_t* flag, int32_t max_cand,
+                                hipStream_t s) {
+  if (max_cand < 1 || max_cand > kChooseThreads) return hipErrorInvalidValue;
+  const unsigned threads = unsigned((max_cand + kWave - 1) / kWave * kWave);
+  hipLaunchKernelGGL(choose_decide_kernel, dim3(1), dim3(threads), 0, s, cand_pos, n_cand, H,
                      argmax, p1, n_unmask, tau, chosen, n_chosen, tokens, is_masked, history,
-                     history_len, history_cap, e_max, flag);
+                     history_len, history_cap, e_max, flag, max_cand);
   return hipGetLastError();
 }
 
