@@ -661,7 +661,7 @@ constexpr TileCfg kTileCfgs[] = {
     {128, 128, 2, 0.23f, 0.36f},    // 2 x 2 waves of 64 x 64, two workgroups per CU
     {256, 128, 1, 0.38f, 0.38f},    // 4 x 2 waves of 64 x 64
     {256, 192, 1, 0.47f, 0.47f},    // 4 x 2 waves of 64 x 96
-    {256, 256, 1, 0.50f, 0.50f},    // 2 x 4 waves of 128 x 64
+    {256, 256, 1, 0.52f, 0.52f},    // 2 x 4 waves of 128 x 64
 };
 constexpr int kDualCfgs[] = {1, 3};   // SwiGLU pair: columns of both matrices per tile
 
