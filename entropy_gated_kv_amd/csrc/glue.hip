@@ -19,6 +19,8 @@ namespace ec {
 
 namespace {
 
+constexpr int kEmbedWgPerCu = 8;
+
 // 16-byte vectors of a storage type, as floats
 template <typename T> struct Vec16;
 template <> struct Vec16<float> {
@@ -43,8 +45,9 @@ template <> struct Vec16<bf16_t> {
 };
 
 // x[r, :] = tok_emb[tokens[rows[r]], :] + pos_emb[rows[r], :] (fp32 add, one
-// rounding): one workgroup per row, 16-byte vectors (d is a multiple of the
-// vector width)
+// rounding): a workgroup per row, 16-byte vectors (d is a multiple of the
+// vector width).  The grid is at most kEmbedWgPerCu per CU, so a partial step
+// of a long sequence does not dispatch a workgroup per cache row.
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ tok_emb,
                                                    const T* __restrict__ pos_emb,
@@ -53,20 +56,21 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ tok_em
                                                    const int32_t* __restrict__ n_rows, int d,
                                                    T* __restrict__ x) {
   using V = Vec16<T>;
-  const int r = blockIdx.x;
-  if (r >= *n_rows) return;
-  const int p = rows[r];
-  const int t = tokens[p];
-  const u32x4* te = reinterpret_cast<const u32x4*>(tok_emb + int64_t(t) * d);
-  const u32x4* pe = reinterpret_cast<const u32x4*>(pos_emb + int64_t(p) * d);
-  u32x4* xr = reinterpret_cast<u32x4*>(x + int64_t(r) * d);
-  for (int v = threadIdx.x; v < d / V::N; v += 256) {
-    float a[V::N], b[V::N];
-    V::unpack(te[v], a);
-    V::unpack(pe[v], b);
+  const int n = *n_rows;
+  for (int r = blockIdx.x; r < n; r += gridDim.x) {     // the grid is capped; rows stride over it
+    const int p = rows[r];
+    const int t = tokens[p];
+    const u32x4* te = reinterpret_cast<const u32x4*>(tok_emb + int64_t(t) * d);
+    const u32x4* pe = reinterpret_cast<const u32x4*>(pos_emb + int64_t(p) * d);
+    u32x4* xr = reinterpret_cast<u32x4*>(x + int64_t(r) * d);
+    for (int v = threadIdx.x; v < d / V::N; v += 256) {
+      float a[V::N], b[V::N];
+      V::unpack(te[v], a);
+      V::unpack(pe[v], b);
 #pragma unroll
-    for (int i = 0; i < V::N; ++i) a[i] += b[i];
-    xr[v] = V::pack(a);
+      for (int i = 0; i < V::N; ++i) a[i] += b[i];
+      xr[v] = V::pack(a);
+    }
   }
 }
 
@@ -219,6 +223,8 @@ __global__ __launch_bounds__(kChooseThreads) void choose_decide_kernel(
 hipError_t launch_embed(int dtype, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
                         const int32_t* rows, const int32_t* n_rows, int max_rows, int d, void* x,
                         hipStream_t s) {
+  const int cap = kEmbedWgPerCu * device_cu_count();
+  max_rows = max_rows < cap ? max_rows : cap;
   if (dtype == 1)
     hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(max_rows), dim3(256), 0, s,
                        static_cast<const bf16_t*>(tok_emb), static_cast<const bf16_t*>(pos_emb),
