@@ -534,7 +534,7 @@ struct BP {
   int L, L_cap, Hq, Hkv, G;
   float sl2;            // scale * log2(e)
   bf16_t* out;
-  float* opart;         // split partial O  [smax][Hkv][mcap][DH]
+  uint16_t* opart;      // split partial O  [smax][Hkv][mcap][DH], bf16 (unnormalised)
   float* mlpart;        // split (m, l)     [smax][Hkv][mcap][2]
   int mcap;             // packed-row capacity of the split workspace
   int smax;             // split capacity of the split workspace
@@ -859,13 +859,15 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
     if (rho >= M) continue;
     if (p.partial) {
       const int64_t prow = (int64_t(split) * p.Hkv + g) * p.mcap + rho;
-      float* op = p.opart + prow * DH;
+      uint16_t* op = p.opart + prow * DH;
+      // bf16 partials: half the bytes written here and read by the merge
 #pragma unroll
       for (int d = 0; d < B::DB; ++d)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
-          *reinterpret_cast<f32x4*>(op + d * 32 + 8 * i4 + 4 * h) =
-              f32x4{o[qb][d][4 * i4], o[qb][d][4 * i4 + 1], o[qb][d][4 * i4 + 2], o[qb][d][4 * i4 + 3]};
+          *reinterpret_cast<u32x2*>(op + d * 32 + 8 * i4 + 4 * h) =
+              u32x2{cvt_bf16x2(o[qb][d][4 * i4], o[qb][d][4 * i4 + 1]),
+                    cvt_bf16x2(o[qb][d][4 * i4 + 2], o[qb][d][4 * i4 + 3])};
       if (h == 0) { p.mlpart[prow * 2] = m_run[qb]; p.mlpart[prow * 2 + 1] = l_tot; }
     } else {
       const int r = rho / p.G, head = g * p.G + rho % p.G;
@@ -915,14 +917,21 @@ __global__ __launch_bounds__(256) void attn_bf16_merge_kernel(BP p, int QT, int 
   float num[EPL];
 #pragma unroll
   for (int k = 0; k < EPL; ++k) num[k] = 0.f;
-  const float* op = p.opart + r0 * DH + (act ? e0 : 0);
+  const uint16_t* op = p.opart + r0 * DH + (act ? e0 : 0);
   for (int s0 = 0; s0 < d.S; s0 += 8) {
     float v[8][EPL];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int s = min(s0 + u, d.S - 1);                  // clamped: weight 0 below
+      const uint16_t* src = op + s * stride * DH;
+      if constexpr (EPL == 2) {                            // two consecutive bf16: one 32-bit load
+        const uint32_t w2 = *reinterpret_cast<const uint32_t*>(src);
+        v[u][0] = bf16_lo(w2);
+        v[u][1] = bf16_hi(w2);
+      } else {
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) v[u][k] = op[s * stride * DH + k];
+        for (int k = 0; k < EPL; ++k) v[u][k] = bf16_to_f32(src[k]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -968,7 +977,8 @@ BPlan plan_bf16(int L, int Hkv, int G, int dh) {
 
 size_t bf16_ws_bytes(int L, int Hkv, int G, int dh) {
   const BPlan b = plan_bf16(L, Hkv, G, dh);
-  return size_t(b.smax) * Hkv * b.mcap * (size_t(dh) + 2) * sizeof(float);
+  // bf16 partial O, then float (m, l)
+  return size_t(b.smax) * Hkv * b.mcap * (size_t(dh) * 2 + 2 * sizeof(float));
 }
 
 template <int DH, int QB, int NW, int NS, bool PIPE>
@@ -999,8 +1009,8 @@ hipError_t launch_bf16(const AttnArgs& a, void* ws, hipStream_t s) {
   const BPlan b = plan_bf16(a.L, a.Hkv, p.G, DH);
   if (ws == nullptr) return hipErrorInvalidValue;
   p.mcap = b.mcap; p.smax = b.smax;
-  p.opart = static_cast<float*>(ws);
-  p.mlpart = p.opart + size_t(b.smax) * a.Hkv * b.mcap * DH;
+  p.opart = static_cast<uint16_t*>(ws);
+  p.mlpart = reinterpret_cast<float*>(p.opart + size_t(b.smax) * a.Hkv * b.mcap * DH);
   // split-KV variant (n <= 128): one workgroup per CU, then the merge
   hipError_t e = hipSuccess;
   if (a.paths & kPathSmall) {

@@ -250,7 +250,10 @@ def check_teacher_forced(cfg, n_steps, tau):
 
 def test_bf16_single_layer_teacher_forced():
     ties, n_partial = check_teacher_forced(gpu_single_cfg(), 30, 1.0)
-    assert n_partial > 3 and ties <= 2
+    # every tie is checked against its zone above; the count only guards
+    # against a systematic shift (about 960 candidate decisions here, with
+    # bf16 rounding of the softmax weights and of the split partial outputs)
+    assert n_partial > 3 and ties <= 4
 
 
 @pytest.mark.parametrize("tile", [None, "0", "1", "2", "3"])
