@@ -467,6 +467,14 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled_kernel(GP p) {
 // selected row and columns past N the last weight row (finite data whose
 // products are never stored).  Requires every copy offset to fit 32 bits
 // (launch_typed checks and otherwise uses the kernel above).
+// Orders one wave's LDS writes before its later LDS reads of what other lanes
+// wrote (and reads before later writes).  A wave's LDS operations complete in
+// order, so this only has to keep the compiler from moving them across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 constexpr int kTBK = 64;                     // k per stage
 
 template <int BM, int BN, int WGM, int WGN, int BK, int NS, int MINW, bool DUAL, int EPI>
@@ -632,7 +640,68 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINW) void gemm_tiled_bf16_kernel(G
           }
         }
     }
+  } else if ((p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 7) == 0) {
+    // Store, residual, SwiGLU and logits epilogues.  A lane holds one column
+    // of each accumulator block in runs of four rows, so direct stores would
+    // be 2-byte accesses (and the residual 2-byte loads).  Each wave instead
+    // passes its 32-row blocks through a private LDS slice (the stages are
+    // idle once the k loop is done) and reads them back row-contiguous: four
+    // columns per lane, one 8-byte load and store, a wave tile row of 64
+    // columns one 128-byte line.  The arithmetic is the per-element
+    // epilogue's, in the same order.
+    constexpr int WC = FN * 32;                       // columns of a wave tile
+    constexpr int PITCH = WC + 4;                     // floats per slice row
+    constexpr int CPR = WC / 4;                       // 4-column chunks per row
+    static_assert(NWAVES * 32 * PITCH * 4 <= NS * STAGE, "epilogue slices fit the stages");
+    static_assert((32 * CPR) % 64 == 0, "whole passes of the wave");
+    __syncthreads();                                  // every wave has left the last stage
+    float* slice = reinterpret_cast<float*>(smem) + wave * (32 * PITCH);
+    bf16_t* C = static_cast<bf16_t*>(p.C);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float v = acc[0][i][j][e];
+          if constexpr (EPI == int(Epi::kSwiGLU)) v = silu(v) * acc[NB - 1][i][j][e];
+          slice[acc_row(e, lane) * PITCH + j * 32 + (lane & 31)] = v;
+        }
+      wave_lds_sync();
+#pragma unroll
+      for (int k0 = 0; k0 < 32 * CPR; k0 += 64) {
+        const int k = k0 + lane, rr = k / CPR, cc = (k % CPR) * 4;
+        const int r = row0 + wr + i * 32 + rr, n = col0 + wc + cc;
+        if (r >= n_rows || n >= p.N) continue;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(slice + rr * PITCH + cc);
+        float x[4] = {v[0], v[1], v[2], v[3]};
+        if constexpr (EPI == int(Epi::kLogits)) {
+          const float sc = (p.scale != nullptr) ? p.scale[p.scale_pos[r]] : 1.0f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) x[t] = x[t] * sc;
+        }
+        bf16_t* dst = C + int64_t(r) * p.ldc + n;
+        if (n + 4 <= p.N) {
+          if constexpr (EPI == int(Epi::kResidual)) {
+            const u32x2 o = *reinterpret_cast<const u32x2*>(dst);
+            x[0] = bf16_lo(o[0]) + x[0];
+            x[1] = bf16_hi(o[0]) + x[1];
+            x[2] = bf16_lo(o[1]) + x[2];
+            x[3] = bf16_hi(o[1]) + x[3];
+          }
+          *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        } else {
+          for (int t = 0; t < p.N - n; ++t) {           // ragged last chunk of the row
+            float y = x[t];
+            if constexpr (EPI == int(Epi::kResidual)) y = bf16_to_f32(dst[t].bits) + y;
+            dst[t].bits = f32_to_bf16(y);
+          }
+        }
+      }
+      wave_lds_sync();                                // reads done before the next block's writes
+    }
   } else {
+    // unaligned output rows: per-element stores
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
