@@ -276,6 +276,27 @@ def test_bf16_stack_split_k_teacher_forced():
     assert n_partial > 3 and ties <= 2
 
 
+@pytest.mark.parametrize("tile", [None, "0", "1", "2", "3"])
+def test_bf16_long_blocks_teacher_forced(tile, monkeypatch):
+    """Two 160-position blocks, 16 tokens a step: the LM head takes up to 160
+    candidate rows, so it runs the tiled GEMM with the logits epilogue, and
+    partial steps refresh more than 128 rows, contiguous (the whole block) and
+    scattered (the block's masked rows and history behind them).  Every tiled
+    configuration runs once forced; SwiGLU keeps its own two."""
+    if tile is not None:
+        monkeypatch.setenv("EC_GEMM_TILE", tile)
+    cfg = C.scaled(C.LLADA_STACK, name="long_blocks", model_n_layers=2, model_d=256,
+                   model_n_q_heads=4, model_n_kv_heads=2, model_head_dim=64, model_vocab=2048,
+                   model_d_ffn=512, prompt_len=96, gen_len=320, block_len=160, k=16,
+                   schedule="fixed:16")
+    ties, n_partial = check_teacher_forced(cfg, 14, 1.0)
+    # each tie is checked against its zone; the count guards against a
+    # systematic shift.  Every step here picks 16 of up to 160 candidates by
+    # top-1 probability, so near-equal boundary choices are far more frequent
+    # than in the two-token schedules above.
+    assert n_partial >= 4 and ties <= 8
+
+
 def test_llada_layer_full_size_two_steps():
     """LLaDA-shaped layer at full size (L = 1024, V = 126464): one full step and
     one partial step, teacher forced, every candidate's logits compared."""
