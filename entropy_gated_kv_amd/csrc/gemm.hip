@@ -641,9 +641,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINW) void gemm_tiled_bf16_kernel(G
         }
     }
   } else if ((p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 7) == 0) {
-    // Store, residual, SwiGLU and logits epilogues.  A lane holds one column
-    // of each accumulator block in runs of four rows, so direct stores would
-    // be 2-byte accesses (and the residual 2-byte loads).  Each wave instead
+    // Residual and SwiGLU epilogues (the instantiated ones besides QKV).  A
+    // lane holds one column of each accumulator block in runs of four rows,
+    // so direct stores would be 2-byte accesses (and the residual's 2-byte
+    // loads).  Each wave instead
     // passes its 32-row blocks through a private LDS slice (the stages are
     // idle once the k loop is done) and reads them back row-contiguous: four
     // columns per lane, one 8-byte load and store, a wave tile row of 64
@@ -654,6 +655,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINW) void gemm_tiled_bf16_kernel(G
     constexpr int CPR = WC / 4;                       // 4-column chunks per row
     static_assert(NWAVES * 32 * PITCH * 4 <= NS * STAGE, "epilogue slices fit the stages");
     static_assert((32 * CPR) % 64 == 0, "whole passes of the wave");
+    static_assert(EPI == int(Epi::kResidual) || EPI == int(Epi::kSwiGLU), "epilogues handled here");
     __syncthreads();                                  // every wave has left the last stage
     float* slice = reinterpret_cast<float*>(smem) + wave * (32 * PITCH);
     bf16_t* C = static_cast<bf16_t*>(p.C);
@@ -675,11 +677,6 @@ __global__ __launch_bounds__(64 * WGM * WGN, MINW) void gemm_tiled_bf16_kernel(G
         if (r >= n_rows || n >= p.N) continue;
         const f32x4 v = *reinterpret_cast<const f32x4*>(slice + rr * PITCH + cc);
         float x[4] = {v[0], v[1], v[2], v[3]};
-        if constexpr (EPI == int(Epi::kLogits)) {
-          const float sc = (p.scale != nullptr) ? p.scale[p.scale_pos[r]] : 1.0f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) x[t] = x[t] * sc;
-        }
         bf16_t* dst = C + int64_t(r) * p.ldc + n;
         if (n + 4 <= p.N) {
           if constexpr (EPI == int(Epi::kResidual)) {

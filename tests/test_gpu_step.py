@@ -279,7 +279,7 @@ def test_bf16_stack_split_k_teacher_forced():
 @pytest.mark.parametrize("tile", [None, "0", "1", "2", "3"])
 def test_bf16_long_blocks_teacher_forced(tile, monkeypatch):
     """Two 160-position blocks, 16 tokens a step: the LM head takes up to 160
-    candidate rows, so it runs the tiled GEMM with the logits epilogue, and
+    candidate rows, so it runs the tiled (row-gathering) GEMM, and
     partial steps refresh more than 128 rows, contiguous (the whole block) and
     scattered (the block's masked rows and history behind them).  Every tiled
     configuration runs once forced; SwiGLU keeps its own two."""
