@@ -320,10 +320,24 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_epilogue(GP p) {
   if (r >= n_rows) return;
   const int64_t plane = int64_t(kSkinnyMaxRows) * p.N;
   const float* src = p.part + int64_t(r) * p.N + n;
+  const int64_t step = plane * (DUAL ? 2 : 1);              // floats between splits
+  // eight splits' loads in flight at a time, summed in split order
   float v = 0.f, v2 = 0.f;
-  for (int s = 0; s < p.S; ++s) {
-    v += src[int64_t(s) * plane * (DUAL ? 2 : 1)];
-    if constexpr (DUAL) v2 += src[int64_t(s) * plane * 2 + plane];
+  for (int s0 = 0; s0 < p.S; s0 += 8) {
+    float a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = min(s0 + u, p.S - 1);                    // clamped: not added below
+      a[u] = src[int64_t(s) * step];
+      if constexpr (DUAL) b[u] = src[int64_t(s) * step + plane];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u < p.S) {
+        v += a[u];
+        if constexpr (DUAL) v2 += b[u];
+      }
+    }
   }
   epilogue<T, EPI>(p, r, n, v, v2);
 }
