@@ -277,6 +277,44 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
     }
     return;
   }
+  if constexpr (EPI == int(Epi::kLogits) && sizeof(T) == 2) {
+    if ((p.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0) {
+      // Logits through LDS: a lane holds one column in runs of four rows, so
+      // direct stores are 2-byte accesses 32 bytes apart per row.  Each wave
+      // rounds its scaled 16-column tile into the activation stage (idle: the
+      // last step ended on a barrier after every wave's reads), and each
+      // thread then stores one 16-byte chunk of a row, a row of the
+      // workgroup's 64 columns being one 128-byte line.  The values are the
+      // per-element epilogue's (acc x scale, rounded once).
+      constexpr int OP = kSkinnyNT * 2 + 16;                 // bytes per staged row
+      static_assert(MB * 16 * OP <= MB * 16 * ROWB, "staged logits fit the activation stage");
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = rb * 16 + 4 * g + j;
+          const float sc = (r < n_rows && p.scale != nullptr) ? p.scale[p.scale_pos[r]] : 1.0f;
+          *reinterpret_cast<uint16_t*>(smem + r * OP + (wave * 16 + (lane & 15)) * 2) = f32_to_bf16(acc[rb][j] * sc);
+        }
+      __syncthreads();
+      bf16_t* C = static_cast<bf16_t*>(p.C);
+      const int c0 = tile * kSkinnyNT;
+#pragma unroll
+      for (int k = tid; k < MB * 16 * (kSkinnyNT / 8); k += kThreads) {
+        const int r = k / (kSkinnyNT / 8), n = c0 + (k % (kSkinnyNT / 8)) * 8;
+        if (r >= n_rows || n >= p.N) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * OP + (n - c0) * 2);
+        if (n + 8 <= p.N) {
+          *reinterpret_cast<u32x4*>(C + int64_t(r) * p.ldc + n) = v;
+        } else {                                              // ragged last chunk of the row
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if (n + t < p.N) C[int64_t(r) * p.ldc + n + t].bits = uint16_t(v[t >> 1] >> ((t & 1) * 16));
+        }
+      }
+      return;
+    }
+  }
   if (col < p.N) {
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
