@@ -15,8 +15,7 @@ rule (strict ">" for the full pass).  Readings where the pages are silent:
   * an empty decoded set gives E = -inf (so a partial step);
   * the decode rule: each candidate decodes to its argmax (lowest vocabulary
     id among equal maxima), and the n candidates with the largest top-1
-    probability are unmasked (ties to the lower position); the step ranks
-    float32-rounded probabilities, the precision the GPU kernel decides in.
+    probability are unmasked (ties to the lower position), ranked in float64.
 """
 from __future__ import annotations
 

@@ -108,12 +108,14 @@ def init_state(model: Model, tokens, masked) -> State:
 
 
 def forward_rows(model: Model, state: State, rows: np.ndarray,
-                 drift: Optional[list] = None) -> np.ndarray:
+                 drift: Optional[list] = None, attn: Optional[list] = None) -> np.ndarray:
     """Run every layer over the selected rows, refreshing their K/V in each cache.
 
     Returns the final activations of those rows (after the final norm, if any).
     When `drift` is a list, each layer's (mean, max) Value drift between the
     cache before and after its refresh is appended to it (oracle.drift).
+    When `attn` is a list, each layer's attention output of the selected rows
+    ([n, Hq, dh], storage precision) is appended to it.
     """
     dt = model.dtype
     n = len(rows)
@@ -127,6 +129,8 @@ def forward_rows(model: Model, state: State, rows: np.ndarray,
         if drift is not None:
             drift.append(value_drift(stale, state.V[l]))
         o = to_storage(bidir_attention(q, state.K[l], state.V[l], scale), dt)
+        if attn is not None:
+            attn.append(o)
         x = to_storage(x + linear(o.reshape(n, model.n_q * model.dh), lw["w_o"]), dt)
         if model.d_ffn:
             a2 = to_storage(rmsnorm(x, lw["norm_ffn"], model.eps), dt)
@@ -157,10 +161,8 @@ def step(model: Model, state: State, tau: float, k: int, block_start: int, block
         z = z * model.logit_scale[cand][:, None]
     z = to_storage(z, model.dtype)
     H, A, P = row_stats(z)
-    # The unmask choice ranks candidates by top-1 probability in float32, the
-    # precision of the kernel that produces it: peaked rows round to exactly
-    # 1.0 there, and such ties go to the lower position.
-    chosen = choose(cand, P.astype(np.float32).astype(np.float64), n_unmask)
+    # The unmask choice ranks candidates by their float64 top-1 probability.
+    chosen = choose(cand, P, n_unmask)
     pick = np.searchsorted(cand, chosen)
     state.tokens[chosen] = A[pick]
     state.masked[chosen] = False
