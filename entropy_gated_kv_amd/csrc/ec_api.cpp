@@ -291,6 +291,7 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
       (int64_t(m->L_cap) * int64_t(esize(m->dtype))) % 16 != 0)
     return EC_E_ALIGN;
   if (m->d_ffn && !external && !al16(m->norm_final)) return EC_E_ALIGN;
+  if (st->attn_out && !al16(st->attn_out)) return EC_E_ALIGN;
   for (int l = 0; l < m->n_layers; ++l) {
     const ec_layer& ly = m->layers[l];
     if (!al16(st->k_cache[l]) || !al16(st->v_cache[l]) || !al16(ly.w_qkv) || !al16(ly.w_o))
@@ -384,6 +385,10 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
       if (first) EC_TRY(tm.end(EC_PHASE_FFN));
     }
   }
+
+  if (st->attn_out)   // rows past *n_rows carry whatever the workspace held
+    EC_TRY(hipMemcpyAsync(st->attn_out, s.o, size_t(hi) * size_t(hd) * esize(dt),
+                          hipMemcpyDeviceToDevice, stream));
 
   if (external) {
     // The caller decoded c->n_unmask rows itself and left their logits in

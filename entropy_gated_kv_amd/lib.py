@@ -20,7 +20,7 @@ EC_MODE_DEVICE, EC_MODE_FULL, EC_MODE_PARTIAL = 0, 1, 2
 PHASES = ("select", "embed", "qkv", "attn", "oproj", "ffn", "lmhead", "entropy", "decide")
 
 _lib: Optional[C.CDLL] = None
-ABI_VERSION = 3                  # EC_ABI_VERSION of include/ec.h
+ABI_VERSION = 4                  # EC_ABI_VERSION of include/ec.h
 
 
 class EcError(RuntimeError):
@@ -51,7 +51,7 @@ class ec_state(C.Structure):
                 ("v_cache", C.POINTER(C.c_void_p)), ("rows", C.c_void_p), ("n_rows", C.c_void_p),
                 ("logits", C.c_void_p), ("row_entropy", C.c_void_p), ("row_argmax", C.c_void_p),
                 ("row_top1", C.c_void_p), ("chosen", C.c_void_p), ("n_chosen", C.c_void_p),
-                ("e_max", C.c_void_p), ("kv_drift", C.c_void_p)]
+                ("e_max", C.c_void_p), ("kv_drift", C.c_void_p), ("attn_out", C.c_void_p)]
 
 
 class ec_step_cfg(C.Structure):

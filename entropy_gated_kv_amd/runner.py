@@ -115,7 +115,18 @@ class DeviceSequence:
         s.row_top1, s.chosen = self.row_top1.data_ptr(), self.chosen.data_ptr()
         s.n_chosen, s.e_max = self.n_chosen.data_ptr(), self.e_max.data_ptr()
         s.kv_drift = None
+        s.attn_out = None
+        self.attn_out = None                      # enable_attn_out(): last layer's attention output
         self.struct = s
+
+    def enable_attn_out(self):
+        """Have every step copy the last layer's attention output of its
+        selected rows into self.attn_out ([L_cap, Hq, dh], rows [0, n_rows))."""
+        import torch
+        sh = self.model.shape
+        self.attn_out = torch.zeros((self.model.L_cap, sh.n_q_heads, sh.head_dim),
+                                    dtype=_torch_dtype(self.model.dtype), device="cuda")
+        self.struct.attn_out = self.attn_out.data_ptr()
 
     def enable_drift(self):
         """Have full steps report each layer's Value drift (mean, max of 1 - cos)."""

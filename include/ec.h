@@ -54,7 +54,7 @@ const char* ec_status_string(int32_t status);
 
 /* ABI revision of this header; bumped on any signature or struct change. */
 int32_t ec_abi_version(void);
-#define EC_ABI_VERSION 3
+#define EC_ABI_VERSION 4
 
 /* --------------------------------------------------------------------------
  * Entropy pass (a1) and decision (a2).
@@ -281,6 +281,12 @@ typedef struct ec_state {
    * summary page §2.1 and Portuguese page §2: the entropy of decoded tokens
    * tracks this drift of the Value vectors.  Needs 16-byte aligned caches. */
   float* kv_drift;
+  /* Optional observation point, or NULL: [L_cap, Hq, dh] device, the model's
+   * dtype, 16-byte aligned.  After the step, rows [0, *n_rows) hold the last
+   * layer's attention output for the selected rows, in selection order (the
+   * bidirectional attention of Portuguese page §1 / Chinese page §1, before
+   * the output projection).  One extra device-to-device copy per step. */
+  void* attn_out;
 } ec_state;
 
 /* Step modes (ec_step_cfg.mode).  EC_MODE_DEVICE: the mode is read from

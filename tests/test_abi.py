@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ec_abi_version() == 3
+    assert lib.ec_abi_version() == 4
     for s in range(-7, 1):
         assert lib.ec_status_string(s)
     assert lib.ec_status_string(99) == b"unknown status"
@@ -113,7 +113,8 @@ def test_step_rejects_misaligned_weights(lib):
         st = L.ec_state(L=256, tokens=FAKE, is_masked=FAKE, history=FAKE, history_len=FAKE,
                         history_cap=64, full_flag=FAKE, k_cache=caches, v_cache=caches, rows=FAKE,
                         n_rows=FAKE, logits=FAKE, row_entropy=FAKE, row_argmax=FAKE, row_top1=FAKE,
-                        chosen=FAKE, n_chosen=FAKE, e_max=FAKE, kv_drift=None)
+                        chosen=FAKE, n_chosen=FAKE, e_max=FAKE, kv_drift=None,
+                        attn_out=bad.get("attn_out"))
         cfg = L.ec_step_cfg(tau=1.0, k=16, n_unmask=2, block_start=192, block_len=32,
                             mode=bad.get("mode", 0))
         return lib.ec_step(C.byref(m), C.byref(st), C.byref(cfg), FAKE, 0, None, None)
@@ -122,5 +123,7 @@ def test_step_rejects_misaligned_weights(lib):
     for mode in (1, 2):
         assert call(mode=mode) == -4
     assert call(mode=3) == -2                                      # not an EC_MODE_*
-    for f in ("w_qkv", "w_o", "norm_attn", "norm_ffn", "w_gate", "w_up", "w_down", "norm_final"):
+    for f in ("w_qkv", "w_o", "norm_attn", "norm_ffn", "w_gate", "w_up", "w_down", "norm_final",
+              "attn_out"):
         assert call(**{f: ODD}) == -5, f
+    assert call(attn_out=FAKE) == -4                               # aligned: accepted

@@ -11,9 +11,13 @@ masked block of 32 plus the 64 history positions before it).
   1e-4 relative (both sides read the same bf16 logits), caches within 2e-2.
 * Full size (L = 8224 and 32800): one partial step, teacher forced from a
   seeded cache, against the oracle (rows exact, refreshed rows within 2e-2,
-  every other cache row bitwise unchanged, E and flag); and one full step,
-  whose refreshed cache rows are checked on a sample the oracle computes one
-  by one (a row's K/V depend only on its own input).
+  every other cache row bitwise unchanged, every one of the step's 96 x 28 x
+  128 attention outputs within 2e-2, E and flag); and one full step, whose
+  refreshed cache rows are checked on a sample the oracle computes one by one
+  (a row's K/V depend only on its own input).  The seeded K cache has
+  standard deviation 2, so with the model's queries (standard deviation about
+  1.7) the scores spread by about 3.4 and the attention outputs are of order
+  0.1-1, well above the tolerance floor: a wrong split merge shows.
 """
 import numpy as np
 import pytest
@@ -23,7 +27,7 @@ import oracle as O
 from entropy_gated_kv_amd.runner import DeviceModel, DeviceSequence, to_device
 from synth import configs as C
 from synth import generators as G
-from tests.gpu_helpers import assert_close
+from tests.gpu_helpers import assert_close, host
 
 pytestmark = pytest.mark.gpu
 
@@ -80,9 +84,9 @@ def test_short_prefix_trajectory_free_running():
     assert_close(v, st.V[0], "bf16", "V cache")
 
 
-def seeded_caches(cfg):
+def seeded_caches(cfg, k_std=1.0):
     m = cfg.model
-    K = G.random_matrix(cfg.seed, (21,), (m.n_kv_heads, cfg.L, m.head_dim), 1.0, cfg.dtype)
+    K = G.random_matrix(cfg.seed, (21,), (m.n_kv_heads, cfg.L, m.head_dim), k_std, cfg.dtype)
     V = G.random_matrix(cfg.seed, (22,), (m.n_kv_heads, cfg.L, m.head_dim), 1.0, cfg.dtype)
     return K.astype(np.float64), V.astype(np.float64)
 
@@ -90,16 +94,23 @@ def seeded_caches(cfg):
 @pytest.mark.parametrize("cfg", [C.DREAM_8K, C.DREAM_32K], ids=["L8224", "L32800"])
 def test_full_size_partial_step(cfg):
     model, st, ds = setup(cfg)
-    K, V = seeded_caches(cfg)
+    K, V = seeded_caches(cfg, k_std=2.0)
     st.K, st.V, st.flag = [K.copy()], [V.copy()], 0
     ds.load_state(st.tokens, st.masked, st.history, 0, [K], [V])
+    ds.enable_attn_out()
     z, zd = decision(cfg, 3)
+    before = st.copy()
     tr = O.step_external(model, st, cfg.tau, cfg.k, cfg.prefix_len, cfg.block_len, z)
     ds.step_external(cfg.tau, cfg.k, cfg.prefix_len, cfg.block_len, zd)
     torch.cuda.synchronize()
     n = int(ds.n_rows.item())
     assert n == cfg.block_len + cfg.k
     np.testing.assert_array_equal(ds.rows[:n].cpu().numpy(), tr.rows)
+    attn = []
+    O.forward_rows(model, before, tr.rows, attn=attn)
+    want = attn[-1]
+    assert np.abs(want).mean() > 0.1
+    assert_close(host(ds.attn_out[:n]), want, "bf16", "step attention output")
     k, v = ds.caches(0)
     assert_close(k[:, tr.rows], st.K[0][:, tr.rows], "bf16", "refreshed K rows")
     assert_close(v[:, tr.rows], st.V[0][:, tr.rows], "bf16", "refreshed V rows")
