@@ -198,7 +198,9 @@ __global__ __launch_bounds__(kChooseThreads) void choose_decide_kernel(
     chosen[slot] = posi;
     tokens[posi] = am;
     is_masked[posi] = 0;
-    history[(hl + slot) % history_cap] = posi;
+    // Slots that differ by history_cap share a ring entry; only the newest
+    // history_cap of this step's slots are written, so each entry has one writer.
+    if (slot >= s_cnt[nwv] - history_cap) history[(hl + slot) % history_cap] = posi;
     if (h != h) hnan = 1; else hmax = h;
   }
   hmax = wave_max(hmax);
