@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "libec.so")
 
 EC_F32, EC_BF16 = 0, 1
 EC_MODE_DEVICE, EC_MODE_FULL, EC_MODE_PARTIAL = 0, 1, 2
+EC_NOALLOC_SCRATCH_BYTES = 8 << 20     # of include/ec.h
 PHASES = ("select", "embed", "qkv", "attn", "oproj", "ffn", "lmhead", "entropy", "decide")
 
 _lib: Optional[C.CDLL] = None
@@ -67,6 +68,8 @@ _SIGS = {
     "ec_entropy_workspace_bytes": (_SZ, [_I64, _I64]),
     "ec_entropy_max": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _I32, _F32, _P, _P, _P, _P, _P,
                               _P, _SZ, _P]),
+    "ec_entropy_max_noalloc": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _I32, _F32, _P, _P, _P,
+                                      _P, _P, _P]),
     "ec_select_rows": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
     "ec_kv_refresh_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "ec_kv_refresh": (_I32, [_P, _I64, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
@@ -143,6 +146,18 @@ def ec_entropy_max(logits, tau: float, row_entropy, e_max, full_flag, ws, *, V: 
         _ptr(n_decoded), max_decoded, float(tau), _ptr(row_entropy), _ptr(row_argmax),
         _ptr(row_top1), _ptr(e_max), _ptr(full_flag), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def ec_entropy_max_noalloc(logits, tau: float, row_entropy, e_max, full_flag, *,
+                           V: Optional[int] = None, decoded_rows=None, n_decoded=None,
+                           max_decoded: int = 0, row_argmax=None, row_top1=None,
+                           stream=None) -> None:
+    n_rows = logits.shape[0]
+    V = logits.shape[1] if V is None else V
+    _check("ec_entropy_max_noalloc", load().ec_entropy_max_noalloc(
+        _ptr(logits), dtype_code(logits), n_rows, V, logits.stride(0), _ptr(decoded_rows),
+        _ptr(n_decoded), max_decoded, float(tau), _ptr(row_entropy), _ptr(row_argmax),
+        _ptr(row_top1), _ptr(e_max), _ptr(full_flag), _stream(stream)))
 
 
 def ec_select_rows(full_flag, is_masked, block_start: int, block_len: int, history, history_len,

@@ -103,6 +103,35 @@ int32_t ec_entropy_max(const void* logits, int32_t dtype, int64_t n_rows, int64_
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* --------------------------------------------------------------------------
+ * Entropy pass and decision with no workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).
+ *
+ * Same arguments (minus ws / ws_bytes), kernels and results, bit for bit, as
+ * ec_entropy_max above.  The per-segment partial statistics live in a static
+ * device array of EC_NOALLOC_SCRATCH_BYTES that each GPU the library runs on
+ * holds until the process ends; the call allocates nothing.  Its device
+ * address is looked up on the stream's device at that device's first call.
+ * Calls on one GPU share the array: two calls that overlap in time on the
+ * same GPU race (serialise them, for example on one stream).  Nothing in the
+ * array needs clearing between calls.
+ * Limit: the partial statistics, n_rows * ceil(V / 4096) * 16 bytes (bf16)
+ * or n_rows * ceil(V / 2048) * 16 bytes (fp32), must fit in
+ * EC_NOALLOC_SCRATCH_BYTES (8 MiB: e.g. 4096 rows of V = 126464 in bf16 use
+ * 2 MiB); a larger call returns EC_E_WORKSPACE before anything is enqueued.
+ * Errors: as ec_entropy_max; EC_E_LAUNCH also when the array's device address
+ * cannot be looked up on the stream's device.
+ * ------------------------------------------------------------------------ */
+#define EC_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+int32_t ec_entropy_max_noalloc(const void* logits, int32_t dtype, int64_t n_rows, int64_t V,
+                               int64_t row_stride,
+                               const int32_t* decoded_rows, const int32_t* n_decoded,
+                               int32_t max_decoded, float tau,
+                               float* row_entropy, int32_t* row_argmax, float* row_top1,
+                               float* e_max, int32_t* full_flag, hipStream_t stream);
+
+/* --------------------------------------------------------------------------
  * Row selection (a3).
  *
  * Source: EntropyCache Chinese page §2.2 and Portuguese page §2: a full step

@@ -69,6 +69,30 @@ def test_entropy_argument_checks(lib):
     assert call(a5=FAKE, a6=None) == -1      # decoded rows without a count
 
 
+def test_noalloc_entropy_argument_checks(lib):
+    """The workspace-free entropy pass refuses, on the host, a call whose
+    partial statistics exceed its static array (before any HIP call)."""
+    f = lib.ec_entropy_max_noalloc
+    base = [FAKE, 1, 4, 100, 104, None, None, 0, 1.0, FAKE, None, None, FAKE, FAKE, None]
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=None) == -1
+    assert call(a1=7) == -3
+    assert call(a4=99) == -2
+    assert call(a0=ODD) == -5
+    rows = L.EC_NOALLOC_SCRATCH_BYTES // 16 + 1          # one 16-byte partial per row
+    assert call(a2=rows, a3=16, a4=16) == -4
+    # V = 4096: one segment per row in bf16, two in fp32
+    half = L.EC_NOALLOC_SCRATCH_BYTES // 32 + 1
+    assert call(a1=0, a2=half, a3=4096, a4=4096) == -4
+    # within the array the host checks pass (without a GPU the device lookup then fails)
+    assert call(a1=1, a2=half, a3=4096, a4=4096) not in (-1, -2, -3, -4, -5)
+    assert call(a2=rows - 1, a3=16, a4=16) not in (-1, -2, -3, -4, -5)
+
+
 def test_select_and_refresh_and_attention_checks(lib):
     assert lib.ec_select_rows(FAKE, FAKE, 10, 8, 4, FAKE, FAKE, 16, 4, FAKE, FAKE, None) == -2
     assert lib.ec_select_rows(FAKE, FAKE, 10, 0, 4, FAKE, FAKE, 2, 4, FAKE, FAKE, None) == -2
