@@ -104,6 +104,43 @@ def record_traffic(fetch_dir: str, write_dir: str) -> dict:
     return rec
 
 
+def summarize_counters(dirs) -> str:
+    """Markdown table of `rocprofv3 --pmc` runs (CSV output directories): per
+    kernel and grid, the mean of each counter per dispatch, plus the MFMA
+    busy share (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs, as
+    the MfmaUtil metric computes it, when both are present) and the bf16
+    MFMA flops per dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)."""
+    import collections
+    import csv
+    import glob
+
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    key = (r["Kernel_Name"].split("(")[0].replace("ec::(anonymous namespace)::", ""),
+                           int(r["Grid_Size"]))
+                    per[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for v in per.values() for c in v})
+    lines = ["| kernel | grid (threads) | dispatches | " + " | ".join(names) +
+             " | MFMA busy | bf16 MFMA GFLOP / dispatch |",
+             "|---|---|---|" + "---|" * len(names) + "---|---|"]
+    for (k, grid), cs in sorted(per.items(), key=lambda kv: -sum(kv[1].get("SQ_VALU_MFMA_BUSY_CYCLES", [0]))):
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        n = max(len(v) for v in cs.values())
+        busy = ""
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("GRBM_GUI_ACTIVE"):
+            busy = f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (mean['GRBM_GUI_ACTIVE'] * 1024):.3f}"
+        gf = ""
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
+            gf = f"{mean['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.2f}"
+        lines.append(f"| `{k}` | {grid} | {n} | " +
+                     " | ".join(f"{mean[c]:.4g}" if c in mean else "" for c in names) +
+                     f" | {busy} | {gf} |")
+    return "\n".join(lines)
+
+
 def _traffic(kernel: str, src: str, per_launch_units: float):
     """HBM bytes per launch from the committed counter summary, or None if the
     kernel source changed since the counters were taken."""
@@ -246,8 +283,8 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
             else:
                 reset()
 
-    # warm-up, then the timed steps from a fresh sequence.  Inside the timed
-    # region only the dominant kernel (the LM head) is bracketed by events.
+    # Inside the timed region only the dominant kernel (the LM head) is
+    # bracketed by events.
     LM = PHASES.index("lmhead")
     n_ev = 2 * len(PHASES)
 
@@ -261,27 +298,75 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
             evs[k].record()                 # materialise the event handle
         return evs
 
-    reset()
-    run(warmup, tau)
-    reset()
+    # The timed steps are spread over the whole generation, so the headline
+    # does not depend on how many are timed: n_seq = min(steps, schedule
+    # length) sequences start at evenly spaced points of the schedule
+    # (snapshots of one untimed trajectory; every sequence then follows that
+    # same deterministic trajectory), and timed step i advances sequence
+    # i mod n_seq by one denoising step.  With the whole schedule timed, the
+    # timed steps are exactly the trajectory's steps, each once; fewer timed
+    # steps are an evenly spaced sample of it.  A sequence that finishes
+    # starts again from the prompt.  Sequences share one workspace (scratch).
+    # Each timed step then runs on a different sequence's state, as in
+    # serving several sequences, which measures about 1-2% slower than one
+    # sequence stepping alone (the tau sweep below).
+    n_seq = max(1, min(steps, len(sched)))
+    phases = [j * len(sched) // n_seq for j in range(n_seq)]
+    seqs = [DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len,
+                           ws=ds.ws) for _ in range(n_seq)]
+    sched_flags = torch.zeros(len(sched), dtype=torch.int32, device="cuda")
+
+    def stage():
+        """Put sequence j at schedule index phases[j]; record the flag each
+        schedule index runs with (the trajectory is deterministic)."""
+        reset()
+        j = 0
+        for s_idx, (bs, bl, nn) in enumerate(sched):
+            while j < n_seq and phases[j] == s_idx:
+                seqs[j].copy_state_from(ds)
+                j += 1
+            sched_flags[s_idx].copy_(ds.full_flag[0])
+            ds.step(tau, cfg.k, bs, bl, nn)
+        return list(phases)
+
+    def seq_step(pos, i, ev=None):
+        j = i % n_seq
+        if pos[j] == len(sched):                  # finished: a fresh sequence
+            sq = seqs[j]
+            sq.tokens.copy_(init[0])
+            sq.is_masked.copy_(init[1])
+            sq.history_len.zero_()
+            sq.full_flag.fill_(1)
+            pos[j] = 0
+        bs, bl, nn = sched[pos[j]]
+        seqs[j].step(tau, cfg.k, bs, bl, nn, phase_events=ev)
+        pos[j] += 1
+        return pos[j] - 1
+
+    pos = stage()
+    for i in range(warmup):
+        seq_step(pos, i)
     torch.cuda.synchronize()
     timed_events = [event_set(True) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run(steps, tau, timed_events)
+    idx = [seq_step(pos, warmup + i, timed_events[i]) for i in range(steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     lm_ms = float(np.mean([ev[2 * LM].elapsed_time(ev[2 * LM + 1]) for ev in timed_events]))
 
     # untimed replay of the same (deterministic) steps with every phase
-    # bracketed, for the breakdown and the step modes
-    reset()
+    # bracketed, for the breakdown; the step modes come from the trajectory
+    pos = stage()
+    for i in range(warmup):
+        seq_step(pos, i)
     torch.cuda.synchronize()
     bd_events = [event_set(False) for _ in range(steps)]
-    flags = torch.zeros(steps, dtype=torch.int32, device="cuda")
-    run(steps, tau, bd_events, flags)
+    for i in range(steps):
+        seq_step(pos, warmup + i, bd_events[i])
     torch.cuda.synchronize()
-    fl = flags.cpu().numpy()
+    fl = sched_flags.cpu().numpy()[idx]
+    del seqs
     phase_ms = {}
     by_mode = {"partial": {}, "full": {}}
     for k, name in enumerate(PHASES):
@@ -303,7 +388,7 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
             cur, left = bs, bl
         cand.append(left)
         left -= nn
-    m = float(np.mean([cand[i % len(sched)] for i in range(steps)]))
+    m = float(np.mean([cand[i] for i in idx]))
     lm_bytes = int(V * d * 2 + m * d * 2 + m * V * 2)
     lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
     decide_ms = phase_ms["select"] + phase_ms["entropy"] + phase_ms["decide"]
@@ -746,6 +831,57 @@ def stack_cpu_baseline(budget_s: float = 20.0) -> dict:
 
 
 # --------------------------------------------------------------------------- profiling
+def profile_mfma_mode() -> int:
+    """A short, fixed sequence of the MFMA kernels for counter runs: the
+    Dream-shaped layer at L = 8224 in steady state (a prefill, six partial
+    steps and the full step that follows a flat decision), one block (22
+    steps) of the LLaDA-shaped layer, and three steps of the 32-layer stack
+    (one full, two partial)."""
+    import torch
+
+    from entropy_gated_kv_amd.runner import DeviceModel, DeviceSequence, to_device
+    from synth import configs as C
+    from synth import generators as G
+
+    cfg = C.DREAM_8K
+    w = G.model_weights(cfg)
+    toks, masked = G.initial_sequence(cfg)
+    dm = DeviceModel(cfg.model, cfg.dtype, cfg.L, w)
+    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.k, max_block=cfg.block_len)
+    ds.load_state(toks, masked, [int(p) for p in G.long_context_history(cfg)], 1)
+    for t in range(9):                   # t = 0 full (prefill), 1..7 partial, 8 full
+        ds.step_external(cfg.tau, cfg.k, cfg.prefix_len, cfg.block_len,
+                         to_device(G.decision_logits(cfg, t), cfg.dtype))
+    torch.cuda.synchronize()
+    del ds, dm, w
+    _log("Dream-shaped steps done")
+    sc = C.LLADA_LAYER
+    w = G.model_weights(sc)
+    toks, masked = G.initial_sequence(sc)
+    dm = DeviceModel(sc.model, sc.dtype, sc.L, w)
+    ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len)
+    for bs, bl, nn in C.unmask_schedule(sc)[:22]:
+        ds.step(1.0, sc.k, bs, bl, nn)
+    torch.cuda.synchronize()
+    del ds, dm, w
+    _log("LLaDA-shaped block done")
+    sc = C.LLADA_STACK
+    dm = DeviceModel(sc.model, sc.dtype, sc.L, G.model_weights_streamed(sc))
+    toks, masked = G.initial_sequence(sc)
+    ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len)
+    for bs, bl, nn in C.unmask_schedule(sc)[:3]:
+        ds.step(1.0, sc.k, bs, bl, nn, mode=L_mode(ds))
+    torch.cuda.synchronize()
+    _log("stack steps done")
+    return 0
+
+
+def L_mode(ds) -> int:
+    """The step mode read from the flag (only that mode's kernels launch)."""
+    from entropy_gated_kv_amd import lib as L
+    return L.EC_MODE_FULL if int(ds.full_flag.item()) else L.EC_MODE_PARTIAL
+
+
 def profile_mode() -> int:
     """A short, fixed sequence for hardware-counter runs (rocprofv3 --pmc):
     a 1 GiB device copy (the calibration of FETCH_SIZE / WRITE_SIZE), five
@@ -805,11 +941,18 @@ def main() -> int:
                     help="skip the step leg (diagnostics only: no headline value)")
     ap.add_argument("--profile-mode", action="store_true",
                     help="run the fixed short sequence used for hardware-counter runs")
+    ap.add_argument("--profile-mfma", action="store_true",
+                    help="run the fixed short sequence of MFMA kernels used for counter runs")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="print a markdown table of rocprofv3 --pmc runs (CSV directories)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two counter runs of --profile-mode")
     args = ap.parse_args()
     if args.record_traffic:
         print(json.dumps(record_traffic(*args.record_traffic), indent=1))
+        return 0
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -821,6 +964,8 @@ def main() -> int:
         return 2
     if args.profile_mode:
         return profile_mode()
+    if args.profile_mfma:
+        return profile_mfma_mode()
     if args.skip_step:
         line = {"metric": METRIC, "value": None, "unit": "steps/s", "n_gpus": 1,
                 "note": "diagnostic run without the step leg (no headline value)"}

@@ -71,7 +71,7 @@ class DeviceSequence:
     """Per-sequence device state (tokens, mask, history, flag, KV caches, step outputs)."""
 
     def __init__(self, model: DeviceModel, tokens: np.ndarray, masked: np.ndarray,
-                 history_cap: int, max_block: int):
+                 history_cap: int, max_block: int, ws=None):
         import torch
         sh = model.shape
         self.model, self.L, self.max_block = model, len(tokens), max_block
@@ -100,7 +100,11 @@ class DeviceSequence:
         nbytes = L.ec_step_workspace_bytes(model.struct, max_block)
         if nbytes == 0:
             raise RuntimeError("ec_step_workspace_bytes rejected the model shape")
-        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        # the workspace is scratch: sequences whose steps run one after another
+        # on one stream may share it
+        if ws is not None and ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("shared workspace too small")
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev) if ws is None else ws
         self._k_arr = (C.c_void_p * sh.n_layers)(*[t.data_ptr() for t in self.k_cache])
         self._v_arr = (C.c_void_p * sh.n_layers)(*[t.data_ptr() for t in self.v_cache])
         s = L.ec_state()
@@ -167,6 +171,16 @@ class DeviceSequence:
             self.step(tau, k, block_start, block_len, decoded_logits.shape[0], phase_events)
         finally:
             self.struct.logits = saved
+
+    def copy_state_from(self, other: "DeviceSequence") -> None:
+        """Device-side copy of another sequence's state (same model and sizes):
+        tokens, mask, history, flag and every layer's caches."""
+        for a, b in ((self.tokens, other.tokens), (self.is_masked, other.is_masked),
+                     (self.history, other.history), (self.history_len, other.history_len),
+                     (self.full_flag, other.full_flag)):
+            a.copy_(b)
+        for a, b in zip(self.k_cache + self.v_cache, other.k_cache + other.v_cache):
+            a.copy_(b)
 
     # -- state transfer (tests: teacher forcing and read-back) -------------------
     def load_state(self, tokens, masked, history: Sequence[int], flag: int,
