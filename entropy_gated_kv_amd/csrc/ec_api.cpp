@@ -283,7 +283,7 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   const int km = ec::gemm_k_multiple(m->dtype);
   if (m->d % km != 0 || (m->Hq * m->dh) % km != 0 || m->d_ffn % km != 0 || m->d_ffn % 32 != 0 ||
       !head_dim_ok(m->dh) || m->Hq / m->Hkv > 16 ||
-      c->block_len > ec::choose_max_candidates() || st->L > ec::select_max_L())
+      c->block_len > ec::step_max_rows() || st->L > ec::select_max_L())
     return EC_E_UNSUPPORTED;
   if (!al16(ws) || !al16(m->tok_emb) || !al16(m->pos_emb) || (!external && !al16(m->w_lm)) ||
       !al16(st->logits) ||
@@ -322,14 +322,15 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   const bool maybe_full = c->mode != EC_MODE_PARTIAL;
   const PhaseTimer tm{phase_events, stream};
 
+  // Selection and embedding run in one kernel, timed as the select phase
+  // (the embed phase is empty).
   EC_TRY(tm.begin(EC_PHASE_SELECT));
-  EC_TRY(ec::launch_select_rows(st->full_flag, st->is_masked, L, c->block_start, c->block_len,
-                                st->history, st->history_len, st->history_cap, c->k, st->rows,
-                                st->n_rows, s.cand_pos, s.cand_idx, s.n_cand, stream));
+  EC_TRY(ec::launch_select_embed(dt, st->full_flag, st->is_masked, L, c->block_start,
+                                 c->block_len, st->history, st->history_len, st->history_cap,
+                                 c->k, st->rows, st->n_rows, s.cand_pos, s.cand_idx, s.n_cand,
+                                 m->tok_emb, m->pos_emb, st->tokens, hi, m->d, s.x, stream));
   EC_TRY(tm.end(EC_PHASE_SELECT));
   EC_TRY(tm.begin(EC_PHASE_EMBED));
-  EC_TRY(ec::launch_embed(dt, m->tok_emb, m->pos_emb, st->tokens, st->rows, st->n_rows, hi, m->d,
-                          s.x, stream));
   EC_TRY(tm.end(EC_PHASE_EMBED));
 
   for (int l = 0; l < m->n_layers; ++l) {
@@ -396,10 +397,12 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
     // history stay as they are.
     EC_TRY(tm.begin(EC_PHASE_LMHEAD));
     EC_TRY(tm.end(EC_PHASE_LMHEAD));
+    // One timed phase covers the entropy pass and the decision (one kernel).
     EC_TRY(tm.begin(EC_PHASE_ENTROPY));
-    EC_TRY(ec::launch_entropy(st->logits, dt, c->n_unmask, nullptr, m->V, m->V, st->row_entropy,
-                              st->row_argmax, st->row_top1, nullptr, nullptr, 0, c->tau, st->e_max,
-                              st->full_flag, s.ent_ws, stream));
+    EC_TRY(ec::launch_entropy_step(st->logits, dt, c->n_unmask, nullptr, m->V, m->V,
+                                   st->row_entropy, st->row_argmax, st->row_top1, nullptr, 0,
+                                   c->tau, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                                   st->e_max, st->full_flag, s.ent_ws, stream));
     EC_TRY(tm.end(EC_PHASE_ENTROPY));
     EC_TRY(tm.begin(EC_PHASE_DECIDE));
     EC_TRY(tm.end(EC_PHASE_DECIDE));
@@ -419,16 +422,16 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   EC_TRY(ec::launch_gemm_rows(gl, s.gemm_ws, stream));
   EC_TRY(tm.end(EC_PHASE_LMHEAD));
 
+  // The entropy phase now includes the unmask choice and the decision, which
+  // run in the same kernel as the per-row fold (the decide phase is empty).
   EC_TRY(tm.begin(EC_PHASE_ENTROPY));
-  EC_TRY(ec::launch_entropy(st->logits, dt, max_block, s.n_cand, m->V, m->V, st->row_entropy,
-                            st->row_argmax, st->row_top1, nullptr, nullptr, 0, 0.f, nullptr,
-                            nullptr, s.ent_ws, stream));
+  EC_TRY(ec::launch_entropy_step(st->logits, dt, max_block, s.n_cand, m->V, m->V,
+                                 st->row_entropy, st->row_argmax, st->row_top1, s.cand_pos,
+                                 c->n_unmask, c->tau, st->chosen, st->n_chosen, st->tokens,
+                                 st->is_masked, st->history, st->history_len, st->history_cap,
+                                 st->e_max, st->full_flag, s.ent_ws, stream));
   EC_TRY(tm.end(EC_PHASE_ENTROPY));
   EC_TRY(tm.begin(EC_PHASE_DECIDE));
-  EC_TRY(ec::launch_choose_decide(s.cand_pos, s.n_cand, st->row_entropy, st->row_argmax,
-                                  st->row_top1, c->n_unmask, c->tau, st->chosen, st->n_chosen,
-                                  st->tokens, st->is_masked, st->history, st->history_len,
-                                  st->history_cap, st->e_max, st->full_flag, max_block, stream));
   EC_TRY(tm.end(EC_PHASE_DECIDE));
   return EC_OK;
 }

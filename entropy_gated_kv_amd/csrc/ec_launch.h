@@ -22,6 +22,21 @@ size_t entropy_ws_bytes(int64_t n_rows, int64_t V, int dtype);
 // be NULL) and, when e_max != NULL, E = max over D of H and flag = E > tau
 // (NaN -> 1); D NULL means rows [0, n_rows).  ws holds the segment partials.
 int device_cu_count();
+// The entropy pass of a step's few rows (at most step_max_rows()) and its
+// decision: partials, then one workgroup that folds each row and decides.
+// cand_pos != NULL: rows are the block's candidates at positions cand_pos
+// (*n_rows_dev of them); the n_unmask of largest p1 are unmasked, decoded,
+// appended to the history, E = max H over them.  cand_pos == NULL: E = max H
+// over all max_rows rows (n_rows_dev NULL); nothing else is written.
+// Then *flag = (E > tau) || isnan(E).
+int32_t step_max_rows();
+hipError_t launch_entropy_step(const void* logits, int dtype, int32_t max_rows,
+                               const int32_t* n_rows_dev, int64_t V, int64_t stride, float* H,
+                               int32_t* argmax, float* p1, const int32_t* cand_pos,
+                               int32_t n_unmask, float tau, int32_t* chosen, int32_t* n_chosen,
+                               int32_t* tokens, uint8_t* is_masked, int32_t* history,
+                               int32_t* history_len, int32_t history_cap, float* e_max,
+                               int32_t* flag, void* ws, hipStream_t s);
 hipError_t launch_entropy(const void* logits, int dtype, int64_t n_rows, const int32_t* n_rows_dev,
                           int64_t V, int64_t stride, float* H, int32_t* argmax, float* p1,
                           const int32_t* D, const int32_t* nD, int32_t maxD, float tau,
@@ -39,19 +54,21 @@ hipError_t launch_select_rows(const int32_t* full_flag, const uint8_t* is_masked
                               int32_t* rows, int32_t* n_rows, int32_t* cand_pos,
                               int32_t* cand_idx, int32_t* n_cand, hipStream_t s);
 
+// The selection above and the embedding of the selected rows in one launch
+// (every workgroup derives the selection itself; max_rows bounds the count):
+//   x[r, :] = tok_emb[tokens[rows[r]], :] + pos_emb[rows[r], :]
+hipError_t launch_select_embed(int dtype, const int32_t* full_flag, const uint8_t* is_masked,
+                               int32_t L, int32_t block_start, int32_t block_len,
+                               const int32_t* history, const int32_t* history_len,
+                               int32_t history_cap, int32_t k, int32_t* rows, int32_t* n_rows,
+                               int32_t* cand_pos, int32_t* cand_idx, int32_t* n_cand,
+                               const void* tok_emb, const void* pos_emb, const int32_t* tokens,
+                               int max_rows, int d, void* x, hipStream_t s);
+
 // ---- glue --------------------------------------------------------------------
-hipError_t launch_embed(int dtype, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
-                        const int32_t* rows, const int32_t* n_rows, int max_rows, int d, void* x,
-                        hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const void* x, const int32_t* n_rows, int max_rows, int d,
                           const void* gain, float eps, void* out, hipStream_t s);
-int32_t choose_max_candidates();
-hipError_t launch_choose_decide(const int32_t* cand_pos, const int32_t* n_cand, const float* H,
-                                const int32_t* argmax, const float* p1, int32_t n_unmask,
-                                float tau, int32_t* chosen, int32_t* n_chosen, int32_t* tokens,
-                                uint8_t* is_masked, int32_t* history, int32_t* history_len,
-                                int32_t history_cap, float* e_max, int32_t* flag, int32_t max_cand,
-                                hipStream_t s);
+
 
 // ---- row GEMM with fused epilogues ---------------------------------------------
 // C[r, n] = sum_k A[row(r), k] * W[n, k] for r < *n_rows_dev (<= max_rows), n < N,

@@ -343,18 +343,14 @@ __device__ __forceinline__ void finish_row(const EntropyPartial& acc, int64_t ro
 
 // One wave per row: lane l folds segments l, l + 64, ... in order, then the
 // lanes merge in a fixed butterfly.  Segments marked kRedo are first replaced
-// by their exact statistics, computed by the whole wave.
+// by their exact statistics, computed by the whole wave.  Every lane returns
+// the row's merged statistics.
 template <typename T>
-__global__ __launch_bounds__(256) void entropy_combine_kernel(
-    const T* __restrict__ logits, int64_t stride, int64_t V,
-    const EntropyPartial* __restrict__ part, int64_t n_rows, const int32_t* __restrict__ n_rows_dev,
-    int P, float* __restrict__ H, int32_t* __restrict__ A, float* __restrict__ p1) {
+__device__ __forceinline__ EntropyPartial combine_row(const T* __restrict__ logits, int64_t stride,
+                                                      int64_t V,
+                                                      const EntropyPartial* __restrict__ part,
+                                                      int P, int64_t row, int lane) {
   constexpr int E = Elem<T>::kPerVec;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = int64_t(blockIdx.x) * (256 / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int64_t nr = n_rows;
-  if (n_rows_dev != nullptr) nr = min(nr, int64_t(max(0, *n_rows_dev)));
-  if (row >= nr) return;                                  // wave-uniform
   const T* rp = logits + row * stride;
   EntropyPartial acc = empty_partial();
   for (int b = 0; b < P; b += kWave) {                    // wave-uniform loop
@@ -371,7 +367,20 @@ __global__ __launch_bounds__(256) void entropy_combine_kernel(
     }
     acc = merge(acc, p);
   }
-  acc = wave_merge(acc, lane);
+  return wave_merge(acc, lane);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void entropy_combine_kernel(
+    const T* __restrict__ logits, int64_t stride, int64_t V,
+    const EntropyPartial* __restrict__ part, int64_t n_rows, const int32_t* __restrict__ n_rows_dev,
+    int P, float* __restrict__ H, int32_t* __restrict__ A, float* __restrict__ p1) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = int64_t(blockIdx.x) * (256 / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int64_t nr = n_rows;
+  if (n_rows_dev != nullptr) nr = min(nr, int64_t(max(0, *n_rows_dev)));
+  if (row >= nr) return;                                  // wave-uniform
+  const EntropyPartial acc = combine_row<T>(logits, stride, V, part, P, row, lane);
   if (lane == 0) finish_row(acc, row, H, A, p1);
 }
 
@@ -404,7 +413,165 @@ __global__ __launch_bounds__(kCombineThreads) void entropy_decide_kernel(
   }
 }
 
+// ---- the step's decode and decision, in one workgroup
+//
+// The few logit rows of a step (the block's candidates, or the rows a caller
+// decoded) are folded here, one wave per row as in entropy_combine_kernel,
+// and the decision follows in the same workgroup:
+//  * choose (cand_pos != nullptr): the n_unmask candidates of largest p1 are
+//    unmasked (ties to the lower position, NaN last), decode to their argmax
+//    and join the history in ascending position order; E = max H over them;
+//  * decide-all (cand_pos == nullptr): E = max H over every row.
+// Then flag = (E > tau) || isnan(E) (-inf when nothing was decoded).
+// EntropyCache, Chinese summary page §2.2 (decode, E_{t+1}, threshold rule)
+// and Portuguese page §2 (decode history).  The pages do not fix the decode
+// rule; the ranking by top-1 probability is this library's reading.
+constexpr int kStepThreads = 1024;
+
+__device__ __forceinline__ bool better(float pj, int posj, float pi, int posi) {
+  const bool nj = (pj != pj), ni = (pi != pi);
+  if (nj != ni) return ni;                 // a number beats NaN
+  if (!nj && pj != pi) return pj > pi;
+  return posj < posi;                      // equal (or both NaN): lower position first
+}
+
+template <typename T>
+__global__ __launch_bounds__(kStepThreads) void entropy_step_kernel(
+    const T* __restrict__ logits, int64_t stride, int64_t V,
+    const EntropyPartial* __restrict__ part, int P, int32_t max_rows,
+    const int32_t* __restrict__ n_rows_dev, float* __restrict__ H, int32_t* __restrict__ A,
+    float* __restrict__ p1, const int32_t* __restrict__ cand_pos, int32_t n_unmask, float tau,
+    int32_t* __restrict__ chosen, int32_t* __restrict__ n_chosen, int32_t* __restrict__ tokens,
+    uint8_t* __restrict__ is_masked, int32_t* __restrict__ history,
+    int32_t* __restrict__ history_len, int32_t history_cap, float* __restrict__ e_max,
+    int32_t* __restrict__ flag) {
+  __shared__ float s_h[kStepThreads];
+  __shared__ float s_p1[kStepThreads];
+  __shared__ int s_am[kStepThreads];
+  __shared__ int s_pos[kStepThreads];
+  __shared__ int s_cnt[kStepThreads / kWave + 1];
+  __shared__ float s_max[kStepThreads / kWave];
+  __shared__ int s_nan[kStepThreads / kWave];
+  constexpr int kWaves = kStepThreads / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool choose = (cand_pos != nullptr);
+  const int nc = n_rows_dev != nullptr ? min(max(0, *n_rows_dev), max_rows) : max_rows;
+  // every per-candidate load goes out at once (the arrays hold max_rows entries)
+  const int posi = (choose && tid < max_rows) ? cand_pos[tid] : 0;
+  const int hl = choose ? *history_len : 0;
+  for (int row = w; row < nc; row += kWaves) {             // wave-uniform
+    const EntropyPartial acc = combine_row<T>(logits, stride, V, part, P, row, lane);
+    if (lane == 0) {
+      finish_row(acc, row, H, A, p1);
+      finish_row(acc, row, s_h, s_am, s_p1);
+    }
+  }
+  if (tid < nc) s_pos[tid] = posi;
+  __syncthreads();
+  float hmax = -INFINITY;
+  int hnan = 0;
+  int total = nc;
+  if (choose) {
+    const int ns = min(n_unmask, nc);
+    bool pick = false;
+    float pi = 0.f;
+    if (tid < nc) {
+      pi = s_p1[tid];
+      int rank = 0;
+      for (int j = 0; j < nc; ++j) rank += better(s_p1[j], s_pos[j], pi, posi) ? 1 : 0;
+      pick = rank < ns;
+    }
+    // ascending-position slot of each chosen candidate (candidates are ascending)
+    const int v = pick ? 1 : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int t = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) s_cnt[w] = incl;
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int k = 0; k < kWaves; ++k) { const int t = s_cnt[k]; s_cnt[k] = acc; acc += t; }
+      s_cnt[kWaves] = acc;
+    }
+    __syncthreads();
+    total = s_cnt[kWaves];
+    if (pick) {
+      const int slot = s_cnt[w] + incl - v;
+      chosen[slot] = posi;
+      tokens[posi] = s_am[tid];
+      is_masked[posi] = 0;
+      // Slots that differ by history_cap share a ring entry; only the newest
+      // history_cap of this step's slots are written, so each entry has one writer.
+      if (slot >= total - history_cap) history[(hl + slot) % history_cap] = posi;
+      const float h = s_h[tid];
+      if (h != h) hnan = 1; else hmax = h;
+    }
+  } else if (tid < nc) {
+    const float h = s_h[tid];
+    if (h != h) hnan = 1; else hmax = h;
+  }
+  hmax = wave_max(hmax);
+  hnan = wave_sum_i(hnan);
+  if (lane == 0) { s_max[w] = hmax; s_nan[w] = hnan; }
+  __syncthreads();
+  if (tid == 0) {
+    float b = -INFINITY;
+    int n = 0;
+    for (int k = 0; k < kWaves; ++k) { b = fmaxf(b, s_max[k]); n += s_nan[k]; }
+    const float E = n ? NAN : b;
+    if (choose) {
+      *n_chosen = total;
+      *history_len = hl + total;
+    }
+    *e_max = E;
+    *flag = (n || E > tau) ? 1 : 0;
+  }
+}
+
 }  // namespace
+
+int32_t step_max_rows() { return kStepThreads; }
+
+hipError_t launch_entropy_step(const void* logits, int dtype, int32_t max_rows,
+                               const int32_t* n_rows_dev, int64_t V, int64_t stride, float* H,
+                               int32_t* argmax, float* p1, const int32_t* cand_pos,
+                               int32_t n_unmask, float tau, int32_t* chosen, int32_t* n_chosen,
+                               int32_t* tokens, uint8_t* is_masked, int32_t* history,
+                               int32_t* history_len, int32_t history_cap, float* e_max,
+                               int32_t* flag, void* ws, hipStream_t s) {
+  if (max_rows < 1 || max_rows > kStepThreads) return hipErrorInvalidValue;
+  const int P = entropy_segments(V, dtype);
+  EntropyPartial* part = static_cast<EntropyPartial*>(ws);
+  constexpr int kUnitsPerWG = 256 / kWave;
+  const unsigned grid = unsigned((int64_t(max_rows) * P + kUnitsPerWG - 1) / kUnitsPerWG);
+  constexpr size_t kResidencyLds = 32 * 1024;            // as in launch_entropy
+  if (dtype == 1) {
+    hipLaunchKernelGGL(entropy_partials_kernel<bf16_t>, dim3(grid), dim3(256), kResidencyLds, s,
+                       static_cast<const bf16_t*>(logits), stride, V, int64_t(max_rows), n_rows_dev,
+                       P, part);
+  } else {
+    hipLaunchKernelGGL(entropy_partials_kernel<float>, dim3(grid), dim3(256), kResidencyLds, s,
+                       static_cast<const float*>(logits), stride, V, int64_t(max_rows), n_rows_dev,
+                       P, part);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dtype == 1)
+    hipLaunchKernelGGL(entropy_step_kernel<bf16_t>, dim3(1), dim3(kStepThreads), 0, s,
+                       static_cast<const bf16_t*>(logits), stride, V, part, P, max_rows, n_rows_dev,
+                       H, argmax, p1, cand_pos, n_unmask, tau, chosen, n_chosen, tokens, is_masked,
+                       history, history_len, history_cap, e_max, flag);
+  else
+    hipLaunchKernelGGL(entropy_step_kernel<float>, dim3(1), dim3(kStepThreads), 0, s,
+                       static_cast<const float*>(logits), stride, V, part, P, max_rows, n_rows_dev,
+                       H, argmax, p1, cand_pos, n_unmask, tau, chosen, n_chosen, tokens, is_masked,
+                       history, history_len, history_cap, e_max, flag);
+  return hipGetLastError();
+}
 
 int device_cu_count() {
   static int cached = 0;

@@ -1,15 +1,7 @@
-// Step glue around the three graded phases: embedding gather of the selected
-// rows, RMSNorm, and the decode/decide kernel that unmasks tokens, appends to
-// the decode history and takes the threshold decision.
-//
-// EntropyCache, Chinese summary page §2.2: after the forward pass new tokens are
-// decoded from the logits and E_{t+1} is the maximum entropy over the newly
-// decoded tokens; E_{t+1} > tau makes the next step a full recompute.  The
-// Portuguese page §2 adds that a decode history is kept to pick the k most
-// recent tokens.  The pages do not fix the decode rule; this library decodes
-// each candidate to its argmax and unmasks the n candidates with the largest
-// top-1 probability (ties to the lower position, NaN last), appending them to
-// the history in ascending position order.
+// Step glue: RMSNorm of the selected rows.  (The embedding gather runs with
+// the row selection in select.hip; the decode and decision kernel, which
+// unmasks tokens, appends to the decode history and takes the threshold
+// decision, runs with the entropy pass in entropy.hip.)
 #include <math.h>
 
 #include "ec_device.h"
@@ -18,8 +10,6 @@
 namespace ec {
 
 namespace {
-
-constexpr int kEmbedWgPerCu = 8;
 
 // 16-byte vectors of a storage type, as floats
 template <typename T> struct Vec16;
@@ -43,36 +33,6 @@ template <> struct Vec16<bf16_t> {
     return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
   }
 };
-
-// x[r, :] = tok_emb[tokens[rows[r]], :] + pos_emb[rows[r], :] (fp32 add, one
-// rounding): a workgroup per row, 16-byte vectors (d is a multiple of the
-// vector width).  The grid is at most kEmbedWgPerCu per CU, so a partial step
-// of a long sequence does not dispatch a workgroup per cache row.
-template <typename T>
-__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ tok_emb,
-                                                   const T* __restrict__ pos_emb,
-                                                   const int32_t* __restrict__ tokens,
-                                                   const int32_t* __restrict__ rows,
-                                                   const int32_t* __restrict__ n_rows, int d,
-                                                   T* __restrict__ x) {
-  using V = Vec16<T>;
-  const int n = *n_rows;
-  for (int r = blockIdx.x; r < n; r += gridDim.x) {     // the grid is capped; rows stride over it
-    const int p = rows[r];
-    const int t = tokens[p];
-    const u32x4* te = reinterpret_cast<const u32x4*>(tok_emb + int64_t(t) * d);
-    const u32x4* pe = reinterpret_cast<const u32x4*>(pos_emb + int64_t(p) * d);
-    u32x4* xr = reinterpret_cast<u32x4*>(x + int64_t(r) * d);
-    for (int v = threadIdx.x; v < d / V::N; v += 256) {
-      float a[V::N], b[V::N];
-      V::unpack(te[v], a);
-      V::unpack(pe[v], b);
-#pragma unroll
-      for (int i = 0; i < V::N; ++i) a[i] += b[i];
-      xr[v] = V::pack(a);
-    }
-  }
-}
 
 // out[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * gain   (one workgroup per row)
 // The row and the gain are loaded once, as 16-byte vectors, and kept in
@@ -135,108 +95,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x,
   for (int v = threadIdx.x + kNormKeep * 256; v < nv; v += 256) orow[v] = scaled(xr[v], gr[v]);
 }
 
-constexpr int kChooseThreads = 1024;
-
-__device__ __forceinline__ bool better(float pj, int posj, float pi, int posi) {
-  const bool nj = (pj != pj), ni = (pi != pi);
-  if (nj != ni) return ni;                 // a number beats NaN
-  if (!nj && pj != pi) return pj > pi;
-  return posj < posi;                      // equal (or both NaN): lower position first
-}
-
-__global__ __launch_bounds__(kChooseThreads) void choose_decide_kernel(
-    const int32_t* __restrict__ cand_pos, const int32_t* __restrict__ n_cand,
-    const float* __restrict__ H, const int32_t* __restrict__ argmax,
-    const float* __restrict__ p1, int32_t n_unmask, float tau, int32_t* __restrict__ chosen,
-    int32_t* __restrict__ n_chosen, int32_t* __restrict__ tokens, uint8_t* __restrict__ is_masked,
-    int32_t* __restrict__ history, int32_t* __restrict__ history_len, int32_t history_cap,
-    float* __restrict__ e_max, int32_t* __restrict__ flag, int32_t max_cand) {
-  __shared__ float s_p1[kChooseThreads];
-  __shared__ int s_pos[kChooseThreads];
-  __shared__ int s_cnt[kChooseThreads / kWave + 1];
-  __shared__ float s_max[kChooseThreads / kWave];
-  __shared__ int s_nan[kChooseThreads / kWave];
-  const int tid = threadIdx.x;
-  const int nwv = int(blockDim.x) / kWave;               // the launch covers max_cand threads
-  // every per-candidate load goes out at once: the arrays hold max_cand
-  // entries, whatever the device count says
-  float pi = 0.f, h = 0.f;
-  int posi = 0, am = 0;
-  if (tid < max_cand) { pi = p1[tid]; posi = cand_pos[tid]; h = H[tid]; am = argmax[tid]; }
-  const int nc = min(*n_cand, max_cand);
-  const int ns = min(n_unmask, nc);
-  const int hl = *history_len;
-  if (tid < nc) { s_p1[tid] = pi; s_pos[tid] = posi; }
-  __syncthreads();
-  bool pick = false;
-  if (tid < nc) {
-    int rank = 0;
-    for (int j = 0; j < nc; ++j) rank += better(s_p1[j], s_pos[j], pi, posi) ? 1 : 0;
-    pick = rank < ns;
-  }
-  // ascending-position slot of each chosen candidate (candidates are ascending)
-  const int lane = tid & (kWave - 1), w = tid / kWave;
-  const int v = pick ? 1 : 0;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += t;
-  }
-  if (lane == kWave - 1) s_cnt[w] = incl;
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int k = 0; k < nwv; ++k) { const int t = s_cnt[k]; s_cnt[k] = acc; acc += t; }
-    s_cnt[nwv] = acc;
-  }
-  __syncthreads();
-  float hmax = -INFINITY;
-  int hnan = 0;
-  if (pick) {
-    const int slot = s_cnt[w] + incl - v;
-    chosen[slot] = posi;
-    tokens[posi] = am;
-    is_masked[posi] = 0;
-    // Slots that differ by history_cap share a ring entry; only the newest
-    // history_cap of this step's slots are written, so each entry has one writer.
-    if (slot >= s_cnt[nwv] - history_cap) history[(hl + slot) % history_cap] = posi;
-    if (h != h) hnan = 1; else hmax = h;
-  }
-  hmax = wave_max(hmax);
-  hnan = wave_sum_i(hnan);
-  if (lane == 0) { s_max[w] = hmax; s_nan[w] = hnan; }
-  __syncthreads();
-  if (tid == 0) {
-    float b = -INFINITY;
-    int n = 0;
-    for (int k = 0; k < nwv; ++k) { b = fmaxf(b, s_max[k]); n += s_nan[k]; }
-    const int total = s_cnt[nwv];
-    const float E = n ? NAN : b;
-    *n_chosen = total;
-    *history_len = hl + total;
-    *e_max = E;
-    *flag = (n || E > tau) ? 1 : 0;
-  }
-}
-
 }  // namespace
-
-hipError_t launch_embed(int dtype, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
-                        const int32_t* rows, const int32_t* n_rows, int max_rows, int d, void* x,
-                        hipStream_t s) {
-  const int cap = kEmbedWgPerCu * device_cu_count();
-  max_rows = max_rows < cap ? max_rows : cap;
-  if (dtype == 1)
-    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(max_rows), dim3(256), 0, s,
-                       static_cast<const bf16_t*>(tok_emb), static_cast<const bf16_t*>(pos_emb),
-                       tokens, rows, n_rows, d, static_cast<bf16_t*>(x));
-  else
-    hipLaunchKernelGGL(embed_kernel<float>, dim3(max_rows), dim3(256), 0, s,
-                       static_cast<const float*>(tok_emb), static_cast<const float*>(pos_emb),
-                       tokens, rows, n_rows, d, static_cast<float*>(x));
-  return hipGetLastError();
-}
 
 hipError_t launch_rmsnorm(int dtype, const void* x, const int32_t* n_rows, int max_rows, int d,
                           const void* gain, float eps, void* out, hipStream_t s) {
@@ -248,22 +107,6 @@ hipError_t launch_rmsnorm(int dtype, const void* x, const int32_t* n_rows, int m
     hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(max_rows), dim3(256), 0, s,
                        static_cast<const float*>(x), n_rows, d, static_cast<const float*>(gain), eps,
                        static_cast<float*>(out));
-  return hipGetLastError();
-}
-
-int32_t choose_max_candidates() { return kChooseThreads; }
-
-hipError_t launch_choose_decide(const int32_t* cand_pos, const int32_t* n_cand, const float* H,
-                                const int32_t* argmax, const float* p1, int32_t n_unmask,
-                                float tau, int32_t* chosen, int32_t* n_chosen, int32_t* tokens,
-                                uint8_t* is_masked, int32_t* history, int32_t* history_len,
-                                int32_t history_cap, float* e_max, int32_t* flag, int32_t max_cand,
-                                hipStream_t s) {
-  if (max_cand < 1 || max_cand > kChooseThreads) return hipErrorInvalidValue;
-  const unsigned threads = unsigned((max_cand + kWave - 1) / kWave * kWave);
-  hipLaunchKernelGGL(choose_decide_kernel, dim3(1), dim3(threads), 0, s, cand_pos, n_cand, H,
-                     argmax, p1, n_unmask, tau, chosen, n_chosen, tokens, is_masked, history,
-                     history_len, history_cap, e_max, flag, max_cand);
   return hipGetLastError();
 }
 
