@@ -105,40 +105,69 @@ def record_traffic(fetch_dir: str, write_dir: str) -> dict:
 
 
 def summarize_counters(dirs) -> str:
-    """Markdown table of `rocprofv3 --pmc` runs (CSV output directories): per
-    kernel and grid, the mean of each counter per dispatch, plus the MFMA
-    busy share (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x 1024 SIMDs, as
-    the MfmaUtil metric computes it, when both are present) and the bf16
-    MFMA flops per dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)."""
+    """Markdown table of `rocprofv3 --pmc` runs (CSV output directories), per
+    kernel and grid, over the dispatches that did work (device-gated launches
+    that exit at once are counted but left out of the means):
+      time           median dispatch duration (counter-run timestamps)
+      GFLOP          bf16 MFMA flops per dispatch, SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
+      TFLOP/s, frac  GFLOP / time, and that over the 2.5 PFLOP/s bf16 peak
+      MFMA busy      SQ_VALU_MFMA_BUSY_CYCLES / (time x 2.4 GHz x 1024 SIMDs)
+      clock          GRBM_GUI_ACTIVE / 8 XCDs / time (dispatches over 200 us;
+                     shorter windows carry the profiler's own cycles)
+      VALU, wait     SQ_ACTIVE_INST_VALU and SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES
+      LDS conflict   SQ_LDS_BANK_CONFLICT over SQ_ACTIVE_INST_LDS"""
     import collections
     import csv
     import glob
+    import re
+    import statistics
 
-    per = collections.defaultdict(lambda: collections.defaultdict(list))
-    for d in dirs:
+    disp = {}                                    # (run, dispatch) -> (key, us, counters)
+    for ri, d in enumerate(dirs):
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(path) as f:
                 for r in csv.DictReader(f):
-                    key = (r["Kernel_Name"].split("(")[0].replace("ec::(anonymous namespace)::", ""),
-                           int(r["Grid_Size"]))
-                    per[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
-    names = sorted({c for v in per.values() for c in v})
-    lines = ["| kernel | grid (threads) | dispatches | " + " | ".join(names) +
-             " | MFMA busy | bf16 MFMA GFLOP / dispatch |",
-             "|---|---|---|" + "---|" * len(names) + "---|---|"]
-    for (k, grid), cs in sorted(per.items(), key=lambda kv: -sum(kv[1].get("SQ_VALU_MFMA_BUSY_CYCLES", [0]))):
-        mean = {c: sum(v) / len(v) for c, v in cs.items()}
-        n = max(len(v) for v in cs.values())
-        busy = ""
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and mean.get("GRBM_GUI_ACTIVE"):
-            busy = f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (mean['GRBM_GUI_ACTIVE'] * 1024):.3f}"
-        gf = ""
-        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in mean:
-            gf = f"{mean['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.2f}"
-        lines.append(f"| `{k}` | {grid} | {n} | " +
-                     " | ".join(f"{mean[c]:.4g}" if c in mean else "" for c in names) +
-                     f" | {busy} | {gf} |")
-    return "\n".join(lines)
+                    name = re.sub(r"\(anonymous namespace\)::", "", r["Kernel_Name"])
+                    name = re.sub(r"^void ", "", name.split("(")[0]).replace("ec::", "")
+                    key = (name, int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+                    us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+                    rec = disp.setdefault((ri, r["Dispatch_Id"]), (key, us, {}))
+                    rec[2][r["Counter_Name"]] = float(r["Counter_Value"])
+    groups = collections.defaultdict(list)
+    for (ri, _), (key, us, c) in disp.items():
+        groups[key].append((us, c))
+    rows = []
+    for key, ds in groups.items():
+        if not key[0].startswith(("attn", "gemm", "entropy", "select", "rmsnorm", "value_drift")):
+            continue
+        big = max(c.get("SQ_WAVE_CYCLES", c.get("SQ_BUSY_CYCLES", 0.0)) for _, c in ds)
+        act = [(us, c) for us, c in ds
+               if c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) > 0
+               or c.get("SQ_WAVE_CYCLES", 0) > 0.05 * big > 0]
+        if not act:
+            continue
+        def med(f):
+            v = [f(us, c) for us, c in act if f(us, c) is not None]
+            return statistics.median(v) if v else None
+        us = med(lambda u, c: u)
+        gf = med(lambda u, c: c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9 if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c else None)
+        busy = med(lambda u, c: c["SQ_VALU_MFMA_BUSY_CYCLES"] / (u * 2400.0 * 1024) if "SQ_VALU_MFMA_BUSY_CYCLES" in c else None)
+        clk = med(lambda u, c: c["GRBM_GUI_ACTIVE"] / 8 / u / 1000 if "GRBM_GUI_ACTIVE" in c and u > 200 else None)
+        valu = med(lambda u, c: c["SQ_ACTIVE_INST_VALU"] / c["SQ_WAVE_CYCLES"] if c.get("SQ_WAVE_CYCLES") else None)
+        wait = med(lambda u, c: c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"] if c.get("SQ_WAVE_CYCLES") else None)
+        ldsc = med(lambda u, c: c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"] if c.get("SQ_ACTIVE_INST_LDS") else None)
+        rows.append((key, len(act), len(ds), us, gf, busy, clk, valu, wait, ldsc))
+    fmt = lambda v, f: "" if v is None else format(v, f)
+    out = ["| kernel | workgroups | dispatches (with work / all) | time us | bf16 MFMA GFLOP | TFLOP/s | "
+           "frac of 2.5 PF | MFMA busy | clock GHz | VALU / wave-cycles | wait / wave-cycles | "
+           "LDS conflict / LDS cycles |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for key, na, nd, us, gf, busy, clk, valu, wait, ldsc in sorted(rows, key=lambda r: -(r[4] or 0) * r[1]):
+        tf = gf / us * 1e3 if gf and us else None
+        out.append(f"| `{key[0]}` | {key[1]} | {na} / {nd} | {fmt(us, '.1f')} | {fmt(gf, '.2f')} | "
+                   f"{fmt(tf, '.0f')} | {fmt(tf / 2500 if tf else None, '.3f')} | {fmt(busy, '.3f')} | "
+                   f"{fmt(clk, '.2f')} | {fmt(valu, '.3f')} | {fmt(wait, '.3f')} | {fmt(ldsc, '.3f')} |")
+    return "\n".join(out)
 
 
 def _traffic(kernel: str, src: str, per_launch_units: float):
@@ -831,48 +860,49 @@ def stack_cpu_baseline(budget_s: float = 20.0) -> dict:
 
 
 # --------------------------------------------------------------------------- profiling
-def profile_mfma_mode() -> int:
-    """A short, fixed sequence of the MFMA kernels for counter runs: the
-    Dream-shaped layer at L = 8224 in steady state (a prefill, six partial
-    steps and the full step that follows a flat decision), one block (22
-    steps) of the LLaDA-shaped layer, and three steps of the 32-layer stack
-    (one full, two partial)."""
+def profile_mfma_mode(workload: str) -> int:
+    """A short, fixed sequence of one workload's kernels for counter runs:
+      dream8k  the Dream-shaped layer at L = 8224 in steady state: a prefill,
+               seven partial steps and the full step after a flat decision;
+      dream32k the same at L = 32800;
+      llada    one block (22 steps) of the LLaDA-shaped layer;
+      stack    three steps of the 32-layer stack (one full, two partial),
+               each launching only its mode's kernels."""
     import torch
 
     from entropy_gated_kv_amd.runner import DeviceModel, DeviceSequence, to_device
     from synth import configs as C
     from synth import generators as G
 
-    cfg = C.DREAM_8K
-    w = G.model_weights(cfg)
-    toks, masked = G.initial_sequence(cfg)
-    dm = DeviceModel(cfg.model, cfg.dtype, cfg.L, w)
-    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.k, max_block=cfg.block_len)
-    ds.load_state(toks, masked, [int(p) for p in G.long_context_history(cfg)], 1)
-    for t in range(9):                   # t = 0 full (prefill), 1..7 partial, 8 full
-        ds.step_external(cfg.tau, cfg.k, cfg.prefix_len, cfg.block_len,
-                         to_device(G.decision_logits(cfg, t), cfg.dtype))
+    if workload in ("dream8k", "dream32k"):
+        cfg = C.DREAM_8K if workload == "dream8k" else C.DREAM_32K
+        w = G.model_weights(cfg)
+        toks, masked = G.initial_sequence(cfg)
+        dm = DeviceModel(cfg.model, cfg.dtype, cfg.L, w)
+        ds = DeviceSequence(dm, toks, masked, history_cap=cfg.k, max_block=cfg.block_len)
+        ds.load_state(toks, masked, [int(p) for p in G.long_context_history(cfg)], 1)
+        for t in range(9):               # t = 0 full (prefill), 1..7 partial, 8 full
+            ds.step_external(cfg.tau, cfg.k, cfg.prefix_len, cfg.block_len,
+                             to_device(G.decision_logits(cfg, t), cfg.dtype))
+    elif workload == "llada":
+        sc = C.LLADA_LAYER
+        w = G.model_weights(sc)
+        toks, masked = G.initial_sequence(sc)
+        dm = DeviceModel(sc.model, sc.dtype, sc.L, w)
+        ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len)
+        for bs, bl, nn in C.unmask_schedule(sc)[:22]:
+            ds.step(1.0, sc.k, bs, bl, nn)
+    elif workload == "stack":
+        sc = C.LLADA_STACK
+        dm = DeviceModel(sc.model, sc.dtype, sc.L, G.model_weights_streamed(sc))
+        toks, masked = G.initial_sequence(sc)
+        ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len)
+        for bs, bl, nn in C.unmask_schedule(sc)[:3]:
+            ds.step(1.0, sc.k, bs, bl, nn, mode=L_mode(ds))
+    else:
+        raise SystemExit(f"unknown workload {workload}")
     torch.cuda.synchronize()
-    del ds, dm, w
-    _log("Dream-shaped steps done")
-    sc = C.LLADA_LAYER
-    w = G.model_weights(sc)
-    toks, masked = G.initial_sequence(sc)
-    dm = DeviceModel(sc.model, sc.dtype, sc.L, w)
-    ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len)
-    for bs, bl, nn in C.unmask_schedule(sc)[:22]:
-        ds.step(1.0, sc.k, bs, bl, nn)
-    torch.cuda.synchronize()
-    del ds, dm, w
-    _log("LLaDA-shaped block done")
-    sc = C.LLADA_STACK
-    dm = DeviceModel(sc.model, sc.dtype, sc.L, G.model_weights_streamed(sc))
-    toks, masked = G.initial_sequence(sc)
-    ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len)
-    for bs, bl, nn in C.unmask_schedule(sc)[:3]:
-        ds.step(1.0, sc.k, bs, bl, nn, mode=L_mode(ds))
-    torch.cuda.synchronize()
-    _log("stack steps done")
+    _log(f"{workload} steps done")
     return 0
 
 
@@ -941,8 +971,8 @@ def main() -> int:
                     help="skip the step leg (diagnostics only: no headline value)")
     ap.add_argument("--profile-mode", action="store_true",
                     help="run the fixed short sequence used for hardware-counter runs")
-    ap.add_argument("--profile-mfma", action="store_true",
-                    help="run the fixed short sequence of MFMA kernels used for counter runs")
+    ap.add_argument("--profile-mfma", choices=("dream8k", "dream32k", "llada", "stack"),
+                    help="run one workload's fixed short sequence, for counter runs")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                     help="print a markdown table of rocprofv3 --pmc runs (CSV directories)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -965,7 +995,7 @@ def main() -> int:
     if args.profile_mode:
         return profile_mode()
     if args.profile_mfma:
-        return profile_mfma_mode()
+        return profile_mfma_mode(args.profile_mfma)
     if args.skip_step:
         line = {"metric": METRIC, "value": None, "unit": "steps/s", "n_gpus": 1,
                 "note": "diagnostic run without the step leg (no headline value)"}
