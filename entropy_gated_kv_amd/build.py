@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libec.so")
 
 SOURCES = ["entropy.hip", "select.hip", "glue.hip", "gemm.hip", "attention.hip", "drift.hip",
-           "noalloc.hip", "ec_api.cpp"]
+           "noalloc.hip", "ec_validate.cpp", "ec_api.cpp"]
 ARCH = "gfx950"
 # Packed FP32 (v_pk_fma/mul/add_f32) is disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1,19 +1,21 @@
-// C-ABI entry points of libec.so: host-side argument checks, workspace
-// carving and kernel launches on the caller's stream.  No entry point
-// allocates device memory, synchronises, or reads device memory on the host.
+// C-ABI entry points of libec.so: argument checks (ec_validate.cpp), workspace
+// sizes and carving, and kernel launches on the caller's stream.  No entry
+// point allocates device memory, synchronises, or reads device memory on the
+// host.
 #include "ec.h"
 
 #include <math.h>
 #include <string.h>
 
 #include "ec_launch.h"
+#include "ec_validate.h"
 
 namespace {
 
-inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+using ec::dtype_ok;
+inline bool al16(const void* p) { return ec::aligned16(p); }
 inline size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
-inline size_t esize(int32_t dtype) { return dtype == EC_BF16 ? 2 : 4; }
-inline bool dtype_ok(int32_t dtype) { return dtype == EC_F32 || dtype == EC_BF16; }
+inline size_t esize(int32_t dtype) { return ec::elem_size(dtype); }
 inline int32_t launch_status(hipError_t e) {
   if (e == hipSuccess) return EC_OK;
   if (e == hipErrorNotSupported) return EC_E_UNSUPPORTED;
@@ -36,8 +38,6 @@ struct Carver {
     return p;
   }
 };
-
-bool head_dim_ok(int32_t dh) { return dh == 32 || dh == 64 || dh == 128; }
 
 }  // namespace
 
@@ -81,13 +81,11 @@ int32_t ec_entropy_max(const void* logits, int32_t dtype, int64_t n_rows, int64_
                        int32_t max_decoded, float tau, float* row_entropy, int32_t* row_argmax,
                        float* row_top1, float* e_max, int32_t* full_flag, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
-  if (!logits || !row_entropy || !e_max || !full_flag || !ws) return EC_E_NULL;
-  if (decoded_rows && !n_decoded) return EC_E_NULL;
-  if (!dtype_ok(dtype)) return EC_E_DTYPE;
-  if (n_rows < 1 || V < 1 || row_stride < V || max_decoded < 0) return EC_E_SHAPE;
-  if (n_rows > (int64_t(1) << 24) || V > (int64_t(1) << 30)) return EC_E_UNSUPPORTED;
-  if (!al16(logits) || !al16(ws) || (row_stride * int64_t(esize(dtype))) % 16 != 0)
-    return EC_E_ALIGN;
+  if (!ws) return EC_E_NULL;
+  const int32_t st = ec::check_entropy(logits, dtype, n_rows, V, row_stride, decoded_rows,
+                                       n_decoded, max_decoded, row_entropy, e_max, full_flag);
+  if (st != EC_OK) return st;
+  if (!al16(ws)) return EC_E_ALIGN;
   if (ws_bytes < ec_entropy_workspace_bytes(n_rows, V)) return EC_E_WORKSPACE;
   EC_TRY(ec::launch_entropy(logits, dtype, n_rows, nullptr, V, row_stride, row_entropy,
                             row_argmax, row_top1, decoded_rows, n_decoded, max_decoded, tau, e_max,
@@ -100,12 +98,9 @@ int32_t ec_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32
                        int32_t block_start, int32_t block_len, const int32_t* history,
                        const int32_t* history_len, int32_t history_cap, int32_t k, int32_t* rows,
                        int32_t* n_rows, hipStream_t stream) {
-  if (!full_flag || !is_masked || !history || !history_len || !rows || !n_rows) return EC_E_NULL;
-  if (L < 1 || block_start < -1 || block_len < 0 || block_len > L ||
-      (block_start >= 0 && block_start + block_len > L) || k < 0 ||
-      history_cap < 1 || k > history_cap)
-    return EC_E_SHAPE;
-  if (L > ec::select_max_L()) return EC_E_UNSUPPORTED;
+  const int32_t st = ec::check_select(full_flag, is_masked, L, block_start, block_len, history,
+                                      history_len, history_cap, k, rows, n_rows);
+  if (st != EC_OK) return st;
   EC_TRY(ec::launch_select_rows(full_flag, is_masked, L, block_start, block_len, history,
                                 history_len, history_cap, k, rows, n_rows, nullptr, nullptr,
                                 nullptr, stream));
@@ -124,15 +119,9 @@ int32_t ec_kv_refresh(const void* x, int64_t x_stride, const int32_t* rows, cons
                       int32_t max_rows, const void* w_qkv, int32_t d, int32_t Hq, int32_t Hkv,
                       int32_t dh, int32_t dtype, void* q_out, void* k_cache, void* v_cache,
                       int32_t L_cap, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!x || !rows || !n_rows || !w_qkv || !q_out || !k_cache || !v_cache) return EC_E_NULL;
-  if (!dtype_ok(dtype)) return EC_E_DTYPE;
-  if (max_rows < 1 || d < 1 || Hq < 1 || Hkv < 1 || dh < 1 || L_cap < 1 || x_stride < d ||
-      Hq % Hkv != 0)
-    return EC_E_SHAPE;
-  if (d % ec::gemm_k_multiple(dtype) != 0 || !head_dim_ok(dh)) return EC_E_UNSUPPORTED;
-  if (!al16(x) || !al16(w_qkv) || !al16(q_out) || !al16(k_cache) || !al16(v_cache) ||
-      (ws && !al16(ws)) || (x_stride * int64_t(esize(dtype))) % 16 != 0)
-    return EC_E_ALIGN;
+  const int32_t st = ec::check_refresh(x, x_stride, rows, n_rows, max_rows, w_qkv, d, Hq, Hkv, dh,
+                                       dtype, q_out, k_cache, v_cache, L_cap, ws);
+  if (st != EC_OK) return st;
   ec::GemmArgs g = qkv_args(max_rows, d, Hq, Hkv, dh, dtype);
   const size_t need = ec::gemm_ws_bytes(g);
   if (need > 0 && !ws) return EC_E_NULL;
@@ -154,17 +143,11 @@ int32_t ec_bidir_attention(const void* q, const int32_t* n_rows, int32_t max_row
                            const void* k_cache, const void* v_cache, int32_t L, int32_t L_cap,
                            int32_t Hq, int32_t Hkv, int32_t dh, float scale, int32_t dtype,
                            void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!q || !n_rows || !k_cache || !v_cache || !out) return EC_E_NULL;
-  if (!dtype_ok(dtype)) return EC_E_DTYPE;
-  if (max_rows < 1 || L < 1 || L > L_cap || Hq < 1 || Hkv < 1 || dh < 1 || Hq % Hkv != 0 ||
-      !(scale > 0.f) || !isfinite(scale))
-    return EC_E_SHAPE;
-  if (!head_dim_ok(dh) || Hq / Hkv > 16) return EC_E_UNSUPPORTED;
+  const int32_t st = ec::check_attention(q, n_rows, max_rows, k_cache, v_cache, L, L_cap, Hq, Hkv,
+                                         dh, scale, dtype, out, ws);
+  if (st != EC_OK) return st;
   const size_t need = ec_attention_workspace_bytes(max_rows, L, Hq, Hkv, dh);
   if (need > 0 && !ws) return EC_E_NULL;
-  if (!al16(q) || !al16(k_cache) || !al16(v_cache) || !al16(out) || (ws && !al16(ws)) ||
-      (int64_t(L_cap) * int64_t(esize(dtype))) % 16 != 0)
-    return EC_E_ALIGN;
   if (ws_bytes < need) return EC_E_WORKSPACE;
   ec::AttnArgs a;
   a.dtype = dtype; a.q = q; a.n_rows_dev = n_rows; a.max_rows = max_rows; a.k_cache = k_cache;
@@ -194,11 +177,6 @@ struct StepLayout {
   int32_t* cand_idx = nullptr;
   int32_t* n_cand = nullptr;
 };
-
-bool model_ok(const ec_model* m) {
-  return m->n_layers >= 1 && m->d >= 64 && m->Hq >= 1 && m->Hkv >= 1 && m->dh >= 1 &&
-         m->Hq % m->Hkv == 0 && m->V >= 1 && m->L_cap >= 1 && m->d_ffn >= 0;
-}
 
 StepLayout step_layout(const ec_model* m, int32_t max_block, void* ws) {
   const size_t es = esize(m->dtype);
@@ -248,58 +226,15 @@ struct PhaseTimer {
 extern "C" {
 
 size_t ec_step_workspace_bytes(const ec_model* m, int32_t max_block) {
-  if (!m || !model_ok(m) || !dtype_ok(m->dtype) || max_block < 1) return 0;
+  if (!m || !ec::model_ok(m) || !dtype_ok(m->dtype) || max_block < 1) return 0;
   return step_layout(m, max_block, nullptr).total;
 }
 
 int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, void* ws,
                 size_t ws_bytes, hipEvent_t* phase_events, hipStream_t stream) {
-  if (!m || !st || !c || !ws) return EC_E_NULL;
-  if (!dtype_ok(m->dtype)) return EC_E_DTYPE;
-  if (!model_ok(m)) return EC_E_SHAPE;
-  if (!m->tok_emb || !m->pos_emb || !m->layers) return EC_E_NULL;
+  const int32_t chk = ec::check_step(m, st, c, ws);
+  if (chk != EC_OK) return chk;
   const bool external = (m->w_lm == nullptr);   // no LM head: the caller decodes
-  if (m->d_ffn && !external && !m->norm_final) return EC_E_NULL;
-  for (int l = 0; l < m->n_layers; ++l) {
-    const ec_layer& ly = m->layers[l];
-    if (!ly.w_qkv || !ly.w_o) return EC_E_NULL;
-    if (m->d_ffn && (!ly.norm_attn || !ly.norm_ffn || !ly.w_gate || !ly.w_up || !ly.w_down))
-      return EC_E_NULL;
-  }
-  if (!st->tokens || !st->is_masked || !st->history || !st->history_len || !st->full_flag ||
-      !st->k_cache || !st->v_cache || !st->rows || !st->n_rows || !st->logits ||
-      !st->row_entropy || !st->row_argmax || !st->row_top1 || !st->chosen || !st->n_chosen ||
-      !st->e_max)
-    return EC_E_NULL;
-  for (int l = 0; l < m->n_layers; ++l)
-    if (!st->k_cache[l] || !st->v_cache[l]) return EC_E_NULL;
-  if (st->L < 1 || st->L > m->L_cap || c->block_start < -1 || c->block_len < 1 ||
-      c->block_len > st->L || (c->block_start >= 0 && c->block_start + c->block_len > st->L) ||
-      c->k < 0 || c->k > st->history_cap ||
-      c->n_unmask < 0 || st->history_cap < 1 ||
-      (c->mode != EC_MODE_DEVICE && c->mode != EC_MODE_FULL && c->mode != EC_MODE_PARTIAL))
-    return EC_E_SHAPE;
-  if (external && (c->n_unmask < 1 || c->n_unmask > c->block_len)) return EC_E_SHAPE;
-  const int km = ec::gemm_k_multiple(m->dtype);
-  if (m->d % km != 0 || (m->Hq * m->dh) % km != 0 || m->d_ffn % km != 0 || m->d_ffn % 32 != 0 ||
-      !head_dim_ok(m->dh) || m->Hq / m->Hkv > 16 ||
-      c->block_len > ec::step_max_rows() || st->L > ec::select_max_L())
-    return EC_E_UNSUPPORTED;
-  if (!al16(ws) || !al16(m->tok_emb) || !al16(m->pos_emb) || (!external && !al16(m->w_lm)) ||
-      !al16(st->logits) ||
-      (int64_t(m->V) * int64_t(esize(m->dtype))) % 16 != 0 ||
-      (int64_t(m->L_cap) * int64_t(esize(m->dtype))) % 16 != 0)
-    return EC_E_ALIGN;
-  if (m->d_ffn && !external && !al16(m->norm_final)) return EC_E_ALIGN;
-  if (st->attn_out && !al16(st->attn_out)) return EC_E_ALIGN;
-  for (int l = 0; l < m->n_layers; ++l) {
-    const ec_layer& ly = m->layers[l];
-    if (!al16(st->k_cache[l]) || !al16(st->v_cache[l]) || !al16(ly.w_qkv) || !al16(ly.w_o))
-      return EC_E_ALIGN;
-    if (m->d_ffn && (!al16(ly.norm_attn) || !al16(ly.norm_ffn) || !al16(ly.w_gate) ||
-                     !al16(ly.w_up) || !al16(ly.w_down)))
-      return EC_E_ALIGN;
-  }
   const int32_t max_block = c->block_len;
   const StepLayout s = step_layout(m, max_block, ws);
   if (ws_bytes < s.total) return EC_E_WORKSPACE;

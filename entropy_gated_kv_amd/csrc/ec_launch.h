@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ec_limits.h"
+
 namespace ec {
 
 // ---- entropy pass ----------------------------------------------------------
@@ -83,7 +85,6 @@ enum class Epi : int {
 // Launch paths of the row-count-dependent operations: device row counts up
 // to kSmallMaxRows (skinny GEMM, split-KV attention) or above (tiled GEMM,
 // unsplit attention).
-constexpr int kSmallMaxRows = 128;
 constexpr unsigned kPathSmall = 1u, kPathLarge = 2u;
 
 struct GemmArgs {

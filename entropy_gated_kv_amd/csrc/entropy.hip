@@ -534,6 +534,7 @@ __global__ __launch_bounds__(kStepThreads) void entropy_step_kernel(
 
 }  // namespace
 
+static_assert(kStepThreads == kStepMaxRows, "one thread per candidate row");
 int32_t step_max_rows() { return kStepThreads; }
 
 hipError_t launch_entropy_step(const void* logits, int dtype, int32_t max_rows,

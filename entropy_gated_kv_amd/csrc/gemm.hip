@@ -972,7 +972,9 @@ hipError_t launch_typed(const GemmArgs& a, void* ws, hipStream_t s, bool allow_s
 
 }  // namespace
 
-int gemm_k_multiple(int dtype) { return dtype == 1 ? skit<bf16_t>() : skit<float>(); }
+static_assert(skit<bf16_t>() == kKMultipleBf16 && skit<float>() == kKMultipleF32,
+              "the host checks' k multiple is one skinny iteration");
+int gemm_k_multiple(int dtype) { return k_multiple(dtype); }
 
 size_t gemm_ws_bytes(const GemmArgs& a) {
   if (a.epi == Epi::kQKV && a.N == 0) return 0;

@@ -17,6 +17,7 @@
 
 #include "ec.h"
 #include "ec_launch.h"
+#include "ec_validate.h"
 
 static __device__ __align__(256) unsigned char scratch[EC_NOALLOC_SCRATCH_BYTES];
 
@@ -52,8 +53,6 @@ hipError_t scratch_on(int dev, void** out) {
   return hipSuccess;
 }
 
-inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
 }  // namespace
 
 extern "C" int32_t ec_entropy_max_noalloc(const void* logits, int32_t dtype, int64_t n_rows,
@@ -62,13 +61,9 @@ extern "C" int32_t ec_entropy_max_noalloc(const void* logits, int32_t dtype, int
                                           int32_t max_decoded, float tau, float* row_entropy,
                                           int32_t* row_argmax, float* row_top1, float* e_max,
                                           int32_t* full_flag, hipStream_t stream) {
-  if (!logits || !row_entropy || !e_max || !full_flag) return EC_E_NULL;
-  if (decoded_rows && !n_decoded) return EC_E_NULL;
-  if (dtype != EC_F32 && dtype != EC_BF16) return EC_E_DTYPE;
-  if (n_rows < 1 || V < 1 || row_stride < V || max_decoded < 0) return EC_E_SHAPE;
-  if (n_rows > (int64_t(1) << 24) || V > (int64_t(1) << 30)) return EC_E_UNSUPPORTED;
-  const int64_t es = dtype == EC_BF16 ? 2 : 4;
-  if (!al16(logits) || (row_stride * es) % 16 != 0) return EC_E_ALIGN;
+  const int32_t st = ec::check_entropy(logits, dtype, n_rows, V, row_stride, decoded_rows,
+                                       n_decoded, max_decoded, row_entropy, e_max, full_flag);
+  if (st != EC_OK) return st;
   if (ec::entropy_ws_bytes(n_rows, V, dtype) > size_t(EC_NOALLOC_SCRATCH_BYTES))
     return EC_E_WORKSPACE;
   int dev = 0;

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void select_embed_kernel(
 
 }  // namespace
 
-int32_t select_max_L() { return 262144; }   // 32 KB LDS bitmap
+int32_t select_max_L() { return kSelectMaxL; }
 
 hipError_t launch_select_embed(int dtype, const int32_t* full_flag, const uint8_t* is_masked,
                                int32_t L, int32_t block_start, int32_t block_len,

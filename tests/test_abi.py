@@ -151,3 +151,29 @@ def test_step_rejects_misaligned_weights(lib):
               "attn_out"):
         assert call(**{f: ODD}) == -5, f
     assert call(attn_out=FAKE) == -4                               # aligned: accepted
+
+
+def test_validation_checks_under_host_sanitizers(tmp_path):
+    """The entry points' argument checks live in a HIP-free translation unit
+    (ec_validate.cpp).  Built with the host compiler's address and
+    undefined-behaviour sanitizers, a driver (tests/validate_driver.cpp)
+    checks hand-made cases and calls every check with 200000 rounds of seeded
+    random arguments, extreme integers included; any sanitizer report aborts
+    it."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = str(tmp_path / "validate_driver")
+    csrc = os.path.join(ROOT, "entropy_gated_kv_amd", "csrc")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-I", os.path.join(ROOT, "include"),
+           "-I", csrc, "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__",
+           os.path.join(csrc, "ec_validate.cpp"), os.path.join(ROOT, "tests", "validate_driver.cpp"),
+           "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
+    assert "all expectations held" in r.stdout
