@@ -539,13 +539,22 @@ struct BP {
   int mcap;             // packed-row capacity of the split workspace
   int smax;             // split capacity of the split workspace
   int partial;          // 1: split-KV variant (n <= 128), 0: unsplit
+  // split-KV variant: the plan, made on the host for a bound nb on the row
+  // count (min(max_rows, 128)): qa query tiles, S splits of `per` kv tiles,
+  // over the packed rows of nb rows (mb = nb * G)
+  int qa, S, per, mb;
+  // 1: the split variant is the only one launched (the row count is known to
+  // be <= 128), so it starts its loads before the count arrives; 0: it is
+  // the gated sibling of the unsplit variant and reads the count first, so
+  // that on a full step it exits without loading anything
+  int spec;
 };
 
-// Split plan of the partial variant, computed on the device from the actual
-// row count: qa query tiles, S splits of `per` kv tiles, for `grid` groups.
+// Split plan of the partial variant for a bound n on the row count: qa query
+// tiles, S splits of `per` kv tiles, for `grid` groups.  Made on the host, so
+// the kernels can start their loads before the device row count arrives.
 struct DPlan { int qa, S, per; };
-__device__ __forceinline__ DPlan device_plan(int n, int G, int QT, int Hkv, int tiles, int grid,
-                                             int smax) {
+inline DPlan split_plan(int n, int G, int QT, int Hkv, int tiles, int grid, int smax) {
   DPlan d;
   d.qa = (n * G + QT - 1) / QT;
   int S = grid / (Hkv * d.qa);
@@ -701,22 +710,35 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
   using B = BG<DH, NW>;
   constexpr int QT = NW * 32 * QB;                         // packed query rows per workgroup
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int n = min(*p.n_rows, p.max_rows);
-  if (n <= 0) return;
-  if (p.partial ? (n > kPartialMaxRows) : (n <= kPartialMaxRows)) return;
-  const int M = n * p.G;
-  const int tiles_all = (p.L + kKV - 1) / kKV;
+  // The split variant's work comes from the host plan.  When it is the only
+  // variant launched (p.spec), its tile copies and Q loads go out before the
+  // row count arrives (one memory latency less) and the count then decides
+  // whether the workgroup's rows exist; otherwise, and in the unsplit
+  // variant, the count is read first and a workgroup with nothing to do
+  // exits before loading anything.
+  const int n_dev = *p.n_rows;
   const int j = xcd_work_index(blockIdx.x, gridDim.x);
-  int g, qt, kv0, kv1, split = 0;
+  int n, M, g, qt, kv0, kv1, split = 0;
   if (p.partial) {
-    const DPlan d = device_plan(n, p.G, QT, p.Hkv, tiles_all, gridDim.x, p.smax);
-    if (j >= p.Hkv * d.S * d.qa) return;
-    qt = j % d.qa;
-    split = (j / d.qa) % d.S;
-    g = j / (d.qa * d.S);
-    kv0 = split * d.per * kKV;
-    kv1 = min(p.L, kv0 + d.per * kKV);
+    if (j >= p.Hkv * p.S * p.qa) return;
+    qt = j % p.qa;
+    split = (j / p.qa) % p.S;
+    g = j / (p.qa * p.S);
+    kv0 = split * p.per * kKV;
+    kv1 = min(p.L, kv0 + p.per * kKV);
+    if (kv0 >= kv1) return;
+    if (p.spec) {
+      M = p.mb;                                             // rows of the plan's bound, for now
+      n = 0;
+    } else {
+      n = min(n_dev, p.max_rows);
+      M = n * p.G;
+      if (n <= 0 || n > kPartialMaxRows || qt * QT >= M) return;
+    }
   } else {
+    n = min(n_dev, p.max_rows);
+    if (n <= kPartialMaxRows) return;
+    M = n * p.G;
     const int qtn = (M + QT - 1) / QT;
     if (j >= p.Hkv * qtn) return;
     qt = j % qtn;
@@ -724,7 +746,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
     kv0 = 0;
     kv1 = p.L;
   }
-  if (kv0 >= kv1) return;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -762,6 +783,21 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
       for (int v = 0; v < B::VH; ++v)
         qf[qb][it * B::VH + v] = ok ? *reinterpret_cast<const u32x4*>(qrow + it * 128 + (h * B::VH + v) * 16)
                                     : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (p.partial && p.spec) {
+    // the device row count: a query tile past the rows (or a count outside
+    // this variant's range) ends the workgroup once its copies have landed
+    n = min(n_dev, p.max_rows);
+    M = n * p.G;
+    if (n <= 0 || n > kPartialMaxRows || qt * QT >= M) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      return;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      if (rho0 + qb * 32 + (lane & 31) >= M)
+#pragma unroll
+        for (int k = 0; k < B::NK; ++k) qf[qb][k] = u32x4{0u, 0u, 0u, 0u};
   }
 
   f32x16 o[QB][B::DB];
@@ -894,13 +930,18 @@ constexpr int kMaxSplits = 64;
 template <int DH>
 __global__ __launch_bounds__(256) void attn_bf16_merge_kernel(BP p, int QT, int grid) {
   constexpr int EPL = DH >= 64 ? DH / 64 : 1;              // elements per lane
-  const int n = min(*p.n_rows, p.max_rows);
-  if (n <= 0 || n > kPartialMaxRows) return;
-  const int M = n * p.G;
-  const DPlan d = device_plan(n, p.G, QT, p.Hkv, (p.L + kKV - 1) / kKV, grid, p.smax);
-  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // (g, rho)
-  const int g = row / M, rho = row % M;
+  // (g, rho) over the plan's bound.  With p.spec the loads go out before the
+  // row count arrives and rows past the count are dropped after it; without,
+  // the count is read first (on a full step nothing is loaded).
+  const int n_dev = *p.n_rows;
+  const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = row / p.mb, rho = row % p.mb;
   if (g >= p.Hkv) return;
+  if (!p.spec) {
+    const int n0 = min(n_dev, p.max_rows);
+    if (n0 <= 0 || n0 > kPartialMaxRows || rho >= n0 * p.G) return;
+  }
+  const DPlan d{p.qa, p.S, p.per};
   const int lane = threadIdx.x & 63;
   const int64_t stride = int64_t(p.Hkv) * p.mcap;           // rows between consecutive splits
   const int64_t r0 = int64_t(g) * p.mcap + rho;
@@ -940,7 +981,8 @@ __global__ __launch_bounds__(256) void attn_bf16_merge_kernel(BP p, int QT, int 
       for (int k = 0; k < EPL; ++k) num[k] = fmaf(wu, v[u][k], num[k]);
     }
   }
-  if (!act) return;
+  const int n = min(n_dev, p.max_rows);
+  if (!act || n <= 0 || n > kPartialMaxRows || rho >= n * p.G) return;
   const int r = rho / p.G, head = g * p.G + rho % p.G;
   const float inv = 1.f / den;
 #pragma unroll
@@ -1011,13 +1053,19 @@ hipError_t launch_bf16(const AttnArgs& a, void* ws, hipStream_t s) {
   p.mcap = b.mcap; p.smax = b.smax;
   p.opart = static_cast<uint16_t*>(ws);
   p.mlpart = reinterpret_cast<float*>(p.opart + size_t(b.smax) * a.Hkv * b.mcap * DH);
-  // split-KV variant (n <= 128): one workgroup per CU, then the merge
+  // split-KV variant (n <= 128): one workgroup per CU, then the merge.  The
+  // plan is made here for the bound min(max_rows, 128) on the row count.
+  const int nb = a.max_rows < kPartialMaxRows ? a.max_rows : kPartialMaxRows;
+  const DPlan d = split_plan(nb, p.G, b.sp.nw * 32 * b.sp.qb, a.Hkv, (a.L + kKV - 1) / kKV,
+                             b.grid_p, b.smax);
+  p.qa = d.qa; p.S = d.S; p.per = d.per; p.mb = nb * p.G;
+  p.spec = (a.max_rows <= kPartialMaxRows || !(a.paths & kPathLarge)) ? 1 : 0;
   hipError_t e = hipSuccess;
   if (a.paths & kPathSmall) {
     p.partial = 1;
     e = launch_bf16_shape<DH>(p, b.sp, unsigned(b.grid_p), s);
     if (e != hipSuccess) return e;
-    const int64_t rows = int64_t(a.Hkv) * kPartialMaxRows * p.G;   // (g, rho) rows, upper bound
+    const int64_t rows = int64_t(a.Hkv) * p.mb;                     // (g, rho) rows of the bound
     hipLaunchKernelGGL((attn_bf16_merge_kernel<DH>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
                        p, b.sp.nw * 32 * b.sp.qb, b.grid_p);
     e = hipGetLastError();
