@@ -1055,7 +1055,8 @@ hipError_t launch_bf16(const AttnArgs& a, void* ws, hipStream_t s) {
   p.mlpart = reinterpret_cast<float*>(p.opart + size_t(b.smax) * a.Hkv * b.mcap * DH);
   // split-KV variant (n <= 128): one workgroup per CU, then the merge.  The
   // plan is made here for the bound min(max_rows, 128) on the row count.
-  const int nb = a.max_rows < kPartialMaxRows ? a.max_rows : kPartialMaxRows;
+  const int bound = (a.small_rows > 0 && a.small_rows < a.max_rows) ? a.small_rows : a.max_rows;
+  const int nb = bound < kPartialMaxRows ? bound : kPartialMaxRows;
   const DPlan d = split_plan(nb, p.G, b.sp.nw * 32 * b.sp.qb, a.Hkv, (a.L + kKV - 1) / kKV,
                              b.grid_p, b.smax);
   p.qa = d.qa; p.S = d.S; p.per = d.per; p.mb = nb * p.G;

@@ -257,15 +257,14 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   const bool maybe_full = c->mode != EC_MODE_PARTIAL;
   const PhaseTimer tm{phase_events, stream};
 
-  // Selection and embedding run in one kernel, timed as the select phase
-  // (the embed phase is empty).
   EC_TRY(tm.begin(EC_PHASE_SELECT));
-  EC_TRY(ec::launch_select_embed(dt, st->full_flag, st->is_masked, L, c->block_start,
-                                 c->block_len, st->history, st->history_len, st->history_cap,
-                                 c->k, st->rows, st->n_rows, s.cand_pos, s.cand_idx, s.n_cand,
-                                 m->tok_emb, m->pos_emb, st->tokens, hi, m->d, s.x, stream));
+  EC_TRY(ec::launch_select_rows(st->full_flag, st->is_masked, L, c->block_start, c->block_len,
+                                st->history, st->history_len, st->history_cap, c->k, st->rows,
+                                st->n_rows, s.cand_pos, s.cand_idx, s.n_cand, stream));
   EC_TRY(tm.end(EC_PHASE_SELECT));
   EC_TRY(tm.begin(EC_PHASE_EMBED));
+  EC_TRY(ec::launch_embed(dt, m->tok_emb, m->pos_emb, st->tokens, st->rows, st->n_rows, hi, m->d,
+                          s.x, stream));
   EC_TRY(tm.end(EC_PHASE_EMBED));
 
   for (int l = 0; l < m->n_layers; ++l) {
@@ -296,6 +295,7 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
     a.dtype = dt; a.q = s.q; a.n_rows_dev = st->n_rows; a.max_rows = hi; a.k_cache = st->k_cache[l];
     a.v_cache = st->v_cache[l]; a.L = L; a.L_cap = m->L_cap; a.Hq = m->Hq; a.Hkv = m->Hkv;
     a.dh = m->dh; a.scale = 1.0f / sqrtf(float(m->dh)); a.out = s.o; a.paths = paths;
+    a.small_rows = sk_rows;
     EC_TRY(ec::launch_attention(a, s.attn_ws, stream));
     if (first) { EC_TRY(tm.end(EC_PHASE_ATTN)); EC_TRY(tm.begin(EC_PHASE_OPROJ)); }
 

@@ -56,18 +56,10 @@ hipError_t launch_select_rows(const int32_t* full_flag, const uint8_t* is_masked
                               int32_t* rows, int32_t* n_rows, int32_t* cand_pos,
                               int32_t* cand_idx, int32_t* n_cand, hipStream_t s);
 
-// The selection above and the embedding of the selected rows in one launch
-// (every workgroup derives the selection itself; max_rows bounds the count):
-//   x[r, :] = tok_emb[tokens[rows[r]], :] + pos_emb[rows[r], :]
-hipError_t launch_select_embed(int dtype, const int32_t* full_flag, const uint8_t* is_masked,
-                               int32_t L, int32_t block_start, int32_t block_len,
-                               const int32_t* history, const int32_t* history_len,
-                               int32_t history_cap, int32_t k, int32_t* rows, int32_t* n_rows,
-                               int32_t* cand_pos, int32_t* cand_idx, int32_t* n_cand,
-                               const void* tok_emb, const void* pos_emb, const int32_t* tokens,
-                               int max_rows, int d, void* x, hipStream_t s);
-
 // ---- glue --------------------------------------------------------------------
+hipError_t launch_embed(int dtype, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
+                        const int32_t* rows, const int32_t* n_rows, int max_rows, int d, void* x,
+                        hipStream_t s);
 hipError_t launch_rmsnorm(int dtype, const void* x, const int32_t* n_rows, int max_rows, int d,
                           const void* gain, float eps, void* out, hipStream_t s);
 
@@ -149,6 +141,10 @@ struct AttnArgs {
   // kPathSmall: split-KV kernel and merge (<= 128 rows); kPathLarge: unsplit
   // kernel (> 128 rows), as for GemmArgs.
   unsigned paths = kPathSmall | kPathLarge;
+  // Optional tighter bound on the device row count whenever that count is at
+  // most 128 (the split-KV plan is made for it); 0 = max_rows.  The caller
+  // guarantees it.
+  int small_rows = 0;
 };
 size_t attn_ws_bytes(int max_rows, int L, int Hq, int Hkv, int dh);
 hipError_t launch_attention(const AttnArgs& a, void* ws, hipStream_t s);

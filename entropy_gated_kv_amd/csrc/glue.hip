@@ -1,7 +1,7 @@
-// Step glue: RMSNorm of the selected rows.  (The embedding gather runs with
-// the row selection in select.hip; the decode and decision kernel, which
-// unmasks tokens, appends to the decode history and takes the threshold
-// decision, runs with the entropy pass in entropy.hip.)
+// Step glue: embedding gather of the selected rows and RMSNorm.  (The decode
+// and decision kernel, which unmasks tokens, appends to the decode history
+// and takes the threshold decision, runs with the entropy pass in
+// entropy.hip.)
 #include <math.h>
 
 #include "ec_device.h"
@@ -10,6 +10,8 @@
 namespace ec {
 
 namespace {
+
+constexpr int kEmbedWgPerCu = 8;
 
 // 16-byte vectors of a storage type, as floats
 template <typename T> struct Vec16;
@@ -33,6 +35,36 @@ template <> struct Vec16<bf16_t> {
     return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
   }
 };
+
+// x[r, :] = tok_emb[tokens[rows[r]], :] + pos_emb[rows[r], :] (fp32 add, one
+// rounding): a workgroup per row, 16-byte vectors (d is a multiple of the
+// vector width).  The grid is at most kEmbedWgPerCu per CU, so a partial step
+// of a long sequence does not dispatch a workgroup per cache row.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ tok_emb,
+                                                   const T* __restrict__ pos_emb,
+                                                   const int32_t* __restrict__ tokens,
+                                                   const int32_t* __restrict__ rows,
+                                                   const int32_t* __restrict__ n_rows, int d,
+                                                   T* __restrict__ x) {
+  using V = Vec16<T>;
+  const int n = *n_rows;
+  for (int r = blockIdx.x; r < n; r += gridDim.x) {     // the grid is capped; rows stride over it
+    const int p = rows[r];
+    const int t = tokens[p];
+    const u32x4* te = reinterpret_cast<const u32x4*>(tok_emb + int64_t(t) * d);
+    const u32x4* pe = reinterpret_cast<const u32x4*>(pos_emb + int64_t(p) * d);
+    u32x4* xr = reinterpret_cast<u32x4*>(x + int64_t(r) * d);
+    for (int v = threadIdx.x; v < d / V::N; v += 256) {
+      float a[V::N], b[V::N];
+      V::unpack(te[v], a);
+      V::unpack(pe[v], b);
+#pragma unroll
+      for (int i = 0; i < V::N; ++i) a[i] += b[i];
+      xr[v] = V::pack(a);
+    }
+  }
+}
 
 // out[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * gain   (one workgroup per row)
 // The row and the gain are loaded once, as 16-byte vectors, and kept in
@@ -96,6 +128,22 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x,
 }
 
 }  // namespace
+
+hipError_t launch_embed(int dtype, const void* tok_emb, const void* pos_emb, const int32_t* tokens,
+                        const int32_t* rows, const int32_t* n_rows, int max_rows, int d, void* x,
+                        hipStream_t s) {
+  const int cap = kEmbedWgPerCu * device_cu_count();
+  max_rows = max_rows < cap ? max_rows : cap;
+  if (dtype == 1)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(max_rows), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(tok_emb), static_cast<const bf16_t*>(pos_emb),
+                       tokens, rows, n_rows, d, static_cast<bf16_t*>(x));
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(max_rows), dim3(256), 0, s,
+                       static_cast<const float*>(tok_emb), static_cast<const float*>(pos_emb),
+                       tokens, rows, n_rows, d, static_cast<float*>(x));
+  return hipGetLastError();
+}
 
 hipError_t launch_rmsnorm(int dtype, const void* x, const int32_t* n_rows, int max_rows, int d,
                           const void* gain, float eps, void* out, hipStream_t s) {

@@ -46,55 +46,36 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int& tot
   return s_wave[w] + incl - v;
 }
 
-// The selection, computed by one workgroup into LDS (`bits`: the union as a
-// bitmap; s_chunk[t]: the rank of thread t's first row).  With `out` set it
-// also writes rows, n_rows and the candidate lists.  Returns whether the
-// step is full and the row count; *my_rows, when given, receives the
-// positions of ranks r = part, part + parts, ... (partial steps only).
-struct SelOut {
-  int32_t* rows;
-  int32_t* n_rows;
-  int32_t* cand_pos;
-  int32_t* cand_idx;
-  int32_t* n_cand;
-};
-
-__device__ __forceinline__ void select_body(
+__global__ __launch_bounds__(kThreads) void select_rows_kernel(
     const int32_t* __restrict__ full_flag, const uint8_t* __restrict__ is_masked, int32_t L,
     int32_t block_start, int32_t block_len, const int32_t* __restrict__ history,
-    const int32_t* __restrict__ history_len, int32_t history_cap, int32_t k, const SelOut* out,
-    uint32_t* bits, int* s_wave, int* s_chunk, int* s_first, int* my_rows, int part, int parts,
-    bool& full_out, int& n_out) {
-  int32_t* rows = out ? out->rows : nullptr;
-  int32_t* n_rows = out ? out->n_rows : nullptr;
-  int32_t* cand_pos = out ? out->cand_pos : nullptr;
-  int32_t* cand_idx = out ? out->cand_idx : nullptr;
-  int32_t* n_cand = out ? out->n_cand : nullptr;
-  int& s_first_ = *s_first;
+    const int32_t* __restrict__ history_len, int32_t history_cap, int32_t k,
+    int32_t* __restrict__ rows, int32_t* __restrict__ n_rows, int32_t* __restrict__ cand_pos,
+    int32_t* __restrict__ cand_idx, int32_t* __restrict__ n_cand) {
+  extern __shared__ uint32_t bits[];                 // ceil(L / 32) words
+  __shared__ int s_wave[kThreads / kWave + 1];
+  __shared__ int s_chunk[kThreads];                  // rows before each thread's word run
+  __shared__ int s_first;
   const int tid = threadIdx.x;
   const int nwords = (L + 31) / 32;
   const bool full = (*full_flag != 0);
   if (block_start < 0) {
     // sliding window: block_len positions from the first masked one, clipped at L
-    if (tid == 0) s_first_ = L;
+    if (tid == 0) s_first = L;
     __syncthreads();
     int f = L;
     for (int p = tid; p < L; p += kThreads)
       if (is_masked[p]) { f = p; break; }
-    atomicMin(&s_first_, f);
+    atomicMin(&s_first, f);
     __syncthreads();
-    block_start = s_first_;
+    block_start = s_first;
     block_len = min(block_len, L - block_start);
   }
   const int bend = block_start + block_len;
-  full_out = full;
-  n_out = L;
 
   if (full) {
-    if (rows != nullptr) {
-      for (int p = tid; p < L; p += kThreads) rows[p] = p;
-      if (tid == 0) *n_rows = L;
-    }
+    for (int p = tid; p < L; p += kThreads) rows[p] = p;
+    if (tid == 0) *n_rows = L;
   } else {
     for (int w = tid; w < nwords; w += kThreads) bits[w] = 0u;
     __syncthreads();
@@ -115,18 +96,15 @@ __device__ __forceinline__ void select_body(
     int total;
     int pos = block_exclusive_scan(cnt, s_wave, total);
     s_chunk[tid] = pos;
-    n_out = total;
     for (int w = w0; w < w1; ++w) {
       uint32_t b = bits[w];
       while (b) {
         const int bit = __ffs(b) - 1;
         b &= b - 1;
-        if (rows != nullptr) rows[pos] = w * 32 + bit;
-        if (my_rows != nullptr && pos % parts == part) my_rows[pos / parts] = w * 32 + bit;
-        ++pos;
+        rows[pos++] = w * 32 + bit;
       }
     }
-    if (tid == 0 && n_rows != nullptr) *n_rows = total;
+    if (tid == 0) *n_rows = total;
   }
 
   if (cand_pos != nullptr) {
@@ -155,104 +133,9 @@ __device__ __forceinline__ void select_body(
   }
 }
 
-__global__ __launch_bounds__(kThreads) void select_rows_kernel(
-    const int32_t* __restrict__ full_flag, const uint8_t* __restrict__ is_masked, int32_t L,
-    int32_t block_start, int32_t block_len, const int32_t* __restrict__ history,
-    const int32_t* __restrict__ history_len, int32_t history_cap, int32_t k,
-    int32_t* __restrict__ rows, int32_t* __restrict__ n_rows, int32_t* __restrict__ cand_pos,
-    int32_t* __restrict__ cand_idx, int32_t* __restrict__ n_cand) {
-  extern __shared__ uint32_t bits[];                 // ceil(L / 32) words
-  __shared__ int s_wave[kThreads / kWave + 1];
-  __shared__ int s_chunk[kThreads];                  // rows before each thread's word run
-  __shared__ int s_first;
-  const SelOut out{rows, n_rows, cand_pos, cand_idx, n_cand};
-  bool full;
-  int n;
-  select_body(full_flag, is_masked, L, block_start, block_len, history, history_len, history_cap,
-              k, &out, bits, s_wave, s_chunk, &s_first, nullptr, 0, 1, full, n);
-}
-
-// Selection and embedding in one launch.  Every workgroup computes the
-// selection in its own LDS (a bitmap over L and one prefix sum, cheap next to
-// a launch); workgroup 0 also writes it out.  Workgroup b then embeds the rows
-// of rank b, b + grid, ...:
-//   x[r, :] = tok_emb[tokens[rows[r]], :] + pos_emb[rows[r], :]
-// (fp32 add, one rounding), 16-byte vectors over d.
-constexpr int kMaxRowsPerWG = 512;
-
-template <typename T>
-__global__ __launch_bounds__(kThreads) void select_embed_kernel(
-    const int32_t* __restrict__ full_flag, const uint8_t* __restrict__ is_masked, int32_t L,
-    int32_t block_start, int32_t block_len, const int32_t* __restrict__ history,
-    const int32_t* __restrict__ history_len, int32_t history_cap, int32_t k,
-    int32_t* __restrict__ rows, int32_t* __restrict__ n_rows, int32_t* __restrict__ cand_pos,
-    int32_t* __restrict__ cand_idx, int32_t* __restrict__ n_cand, const T* __restrict__ tok_emb,
-    const T* __restrict__ pos_emb, const int32_t* __restrict__ tokens, int d, T* __restrict__ x) {
-  extern __shared__ uint32_t bits[];                 // ceil(L / 32) words
-  __shared__ int s_wave[kThreads / kWave + 1];
-  __shared__ int s_chunk[kThreads];
-  __shared__ int s_first;
-  __shared__ int my_rows[kMaxRowsPerWG];
-  const SelOut out{rows, n_rows, cand_pos, cand_idx, n_cand};
-  bool full;
-  int n;
-  select_body(full_flag, is_masked, L, block_start, block_len, history, history_len, history_cap,
-              k, blockIdx.x == 0 ? &out : nullptr, bits, s_wave, s_chunk, &s_first, my_rows,
-              int(blockIdx.x), int(gridDim.x), full, n);
-  __syncthreads();
-  constexpr int VE = 16 / int(sizeof(T));              // elements per 16-byte vector
-  const int nv = d / VE;
-  for (int r = blockIdx.x, i = 0; r < n; r += gridDim.x, ++i) {
-    const int p = full ? r : my_rows[i];
-    const u32x4* te = reinterpret_cast<const u32x4*>(tok_emb + int64_t(tokens[p]) * d);
-    const u32x4* pe = reinterpret_cast<const u32x4*>(pos_emb + int64_t(p) * d);
-    u32x4* xr = reinterpret_cast<u32x4*>(x + int64_t(r) * d);
-    for (int v = threadIdx.x; v < nv; v += kThreads) {
-      const u32x4 a = te[v], b = pe[v];
-      u32x4 o;
-      if constexpr (VE == 8) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          o[j] = pack_bf16x2(bf16_lo(a[j]) + bf16_lo(b[j]), bf16_hi(a[j]) + bf16_hi(b[j]));
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = __float_as_uint(__uint_as_float(a[j]) + __uint_as_float(b[j]));
-      }
-      xr[v] = o;
-    }
-  }
-}
-
 }  // namespace
 
 int32_t select_max_L() { return kSelectMaxL; }
-
-hipError_t launch_select_embed(int dtype, const int32_t* full_flag, const uint8_t* is_masked,
-                               int32_t L, int32_t block_start, int32_t block_len,
-                               const int32_t* history, const int32_t* history_len,
-                               int32_t history_cap, int32_t k, int32_t* rows, int32_t* n_rows,
-                               int32_t* cand_pos, int32_t* cand_idx, int32_t* n_cand,
-                               const void* tok_emb, const void* pos_emb, const int32_t* tokens,
-                               int max_rows, int d, void* x, hipStream_t s) {
-  // two workgroups per CU, and at most kMaxRowsPerWG rows each
-  int grid = max_rows < 2 * device_cu_count() ? max_rows : 2 * device_cu_count();
-  if (grid < 1) grid = 1;
-  if ((max_rows + grid - 1) / grid > kMaxRowsPerWG) grid = (max_rows + kMaxRowsPerWG - 1) / kMaxRowsPerWG;
-  const size_t lds = size_t((L + 31) / 32) * sizeof(uint32_t);
-  if (dtype == 1)
-    hipLaunchKernelGGL(select_embed_kernel<bf16_t>, dim3(unsigned(grid)), dim3(kThreads), lds, s,
-                       full_flag, is_masked, L, block_start, block_len, history, history_len,
-                       history_cap, k, rows, n_rows, cand_pos, cand_idx, n_cand,
-                       static_cast<const bf16_t*>(tok_emb), static_cast<const bf16_t*>(pos_emb),
-                       tokens, d, static_cast<bf16_t*>(x));
-  else
-    hipLaunchKernelGGL(select_embed_kernel<float>, dim3(unsigned(grid)), dim3(kThreads), lds, s,
-                       full_flag, is_masked, L, block_start, block_len, history, history_len,
-                       history_cap, k, rows, n_rows, cand_pos, cand_idx, n_cand,
-                       static_cast<const float*>(tok_emb), static_cast<const float*>(pos_emb),
-                       tokens, d, static_cast<float*>(x));
-  return hipGetLastError();
-}
 
 hipError_t launch_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
                               int32_t block_start, int32_t block_len, const int32_t* history,
