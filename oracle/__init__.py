@@ -37,4 +37,4 @@ from .selection import select_rows, candidates, sliding_window  # noqa: F401
 from .layers import linear, kv_refresh, bidir_attention, rmsnorm, swiglu  # noqa: F401
 from .drift import cosine_distance, value_drift  # noqa: F401
 from .step import (Model, State, StepTrace, step, step_external, generate, init_state,  # noqa: F401
-                   forward_rows)
+                   forward_rows, commit, generate_block_diffusion)

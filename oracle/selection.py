@@ -43,12 +43,23 @@ def candidates(masked, block_start: int, block_len: int) -> np.ndarray:
 
 
 def select_rows(full: int, masked, block_start: int, block_len: int,
-                history: Sequence[int], k: int) -> np.ndarray:
-    """Ascending list of the positions whose Q/K/V are recomputed this step."""
+                history: Sequence[int], k: int, block_causal: bool = False) -> np.ndarray:
+    """Ascending list of the positions whose Q/K/V are recomputed this step.
+
+    block_causal (block diffusion, see oracle.step.step): only positions of
+    the current block are ever recomputed.  A full step takes all of them; a
+    partial step takes the block's masked positions and those of the last k
+    decoded positions that lie inside the block (earlier blocks are final)."""
     L = len(masked)
+    end = block_start + block_len
     if full:
+        if block_causal:
+            return np.arange(block_start, end, dtype=np.int64)
         return np.arange(L, dtype=np.int64)
     chosen = set(int(p) for p in candidates(masked, block_start, block_len))
     if k > 0:
-        chosen |= set(int(p) for p in list(history)[-k:])
+        recent = [int(p) for p in list(history)[-k:]]
+        if block_causal:
+            recent = [p for p in recent if block_start <= p < end]
+        chosen |= set(recent)
     return np.array(sorted(chosen), dtype=np.int64)

@@ -20,6 +20,18 @@ EntropyCache (pt) §2 gives the same flow.  Readings where the pages are silent
     optionally times a per-position scale, and stored in the storage dtype;
   * when the block has no masked position left the host moves to the next
     block (the schedule is fixed on the host).
+
+Block diffusion (block_causal=True).  The Chinese page (§5, generality) names
+block diffusion as a place where the entropy signal could drive the recompute
+of a sub-block, and describes no further.  The reading taken: the sequence is
+split into blocks of block_len (the prompt included); attention is
+block-causal, a position attending to every position of its own and earlier
+blocks; the blocks before the current one are final, their K/V computed once
+by a commit pass when the block is finished.  The entropy gate then decides,
+inside the current block, between recomputing all of its rows (full step) and
+only its masked rows plus the last k decoded positions that lie in it
+(partial step), every recomputed row attending to the keys before the block's
+end.  A commit is a full step that decodes nothing (commit below).
 """
 from __future__ import annotations
 
@@ -108,7 +120,8 @@ def init_state(model: Model, tokens, masked) -> State:
 
 
 def forward_rows(model: Model, state: State, rows: np.ndarray,
-                 drift: Optional[list] = None, attn: Optional[list] = None) -> np.ndarray:
+                 drift: Optional[list] = None, attn: Optional[list] = None,
+                 n_keys: Optional[int] = None) -> np.ndarray:
     """Run every layer over the selected rows, refreshing their K/V in each cache.
 
     Returns the final activations of those rows (after the final norm, if any).
@@ -116,6 +129,8 @@ def forward_rows(model: Model, state: State, rows: np.ndarray,
     cache before and after its refresh is appended to it (oracle.drift).
     When `attn` is a list, each layer's attention output of the selected rows
     ([n, Hq, dh], storage precision) is appended to it.
+    n_keys: the rows attend to cache positions [0, n_keys) only (block
+    diffusion: the end of the current block); None: every position.
     """
     dt = model.dtype
     n = len(rows)
@@ -128,7 +143,8 @@ def forward_rows(model: Model, state: State, rows: np.ndarray,
                        model.dh, dt)
         if drift is not None:
             drift.append(value_drift(stale, state.V[l]))
-        o = to_storage(bidir_attention(q, state.K[l], state.V[l], scale), dt)
+        nk = state.K[l].shape[1] if n_keys is None else n_keys
+        o = to_storage(bidir_attention(q, state.K[l][:, :nk], state.V[l][:, :nk], scale), dt)
         if attn is not None:
             attn.append(o)
         x = to_storage(x + linear(o.reshape(n, model.n_q * model.dh), lw["w_o"]), dt)
@@ -142,18 +158,25 @@ def forward_rows(model: Model, state: State, rows: np.ndarray,
 
 
 def step(model: Model, state: State, tau: float, k: int, block_start: int, block_len: int,
-         n_unmask: int, keep_logits: bool = True, drift: bool = False) -> StepTrace:
+         n_unmask: int, keep_logits: bool = True, drift: bool = False,
+         block_causal: bool = False) -> StepTrace:
     """One denoising step; mutates `state` and returns what the step computed.
 
     drift: on a full step, also report each layer's Value drift (oracle.drift).
     block_start < 0: sliding-window decoding, the block being the block_len
-    positions from the first masked one (oracle.selection.sliding_window)."""
+    positions from the first masked one (oracle.selection.sliding_window).
+    block_causal: block diffusion (module docstring): rows of the current
+    block only, attending to the keys before the block's end."""
     if block_start < 0:
+        if block_causal:
+            raise ValueError("block diffusion needs an explicit block")
         block_start, block_len = sliding_window(state.masked, block_len)
     flag_used = state.flag
-    rows = select_rows(flag_used, state.masked, block_start, block_len, state.history, k)
+    rows = select_rows(flag_used, state.masked, block_start, block_len, state.history, k,
+                       block_causal)
     dl = [] if (drift and flag_used) else None
-    x = forward_rows(model, state, rows, dl)
+    x = forward_rows(model, state, rows, dl,
+                     n_keys=(block_start + block_len) if block_causal else None)
     cand = candidates(state.masked, block_start, block_len)
     ci = np.searchsorted(rows, cand)
     z = linear(x[ci], model.w_lm)
@@ -206,4 +229,32 @@ def generate(model: Model, state: State, schedule: Sequence[Tuple[int, int, int]
         if n_steps is not None and i >= n_steps:
             break
         out.append(step(model, state, tau, k, bs, bl, n, keep_logits))
+    return out
+
+
+def commit(model: Model, state: State, block_start: int, block_len: int, k: int) -> StepTrace:
+    """Block diffusion: make a finished block's K/V final.
+
+    A full step over the block's rows (keys before its end) that decodes
+    nothing: with no decoded row E = -inf, so the flag it leaves is 0."""
+    state.flag = 1
+    return step(model, state, 0.0, k, block_start, block_len, 0, block_causal=True)
+
+
+def generate_block_diffusion(model: Model, state: State, prompt_len: int,
+                             schedule: Sequence[Tuple[int, int, int]], tau: float, k: int,
+                             keep_logits: bool = False) -> List[StepTrace]:
+    """Block diffusion with the entropy gate inside the current block.
+
+    The prompt is committed block by block (blocks of the schedule's length),
+    then each generated block runs its denoising steps (block_causal) and is
+    committed once its last token is decoded."""
+    out = []
+    bl0 = schedule[0][1]
+    for bs in range(0, prompt_len, bl0):
+        out.append(commit(model, state, bs, min(bl0, prompt_len - bs), k))
+    for i, (bs, bl, n) in enumerate(schedule):
+        out.append(step(model, state, tau, k, bs, bl, n, keep_logits, block_causal=True))
+        if i + 1 == len(schedule) or schedule[i + 1][0] != bs:
+            out.append(commit(model, state, bs, bl, k))
     return out
