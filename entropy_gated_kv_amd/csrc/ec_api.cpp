@@ -95,15 +95,16 @@ int32_t ec_entropy_max(const void* logits, int32_t dtype, int64_t n_rows, int64_
 
 // ------------------------------------------------------------------ selection
 int32_t ec_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
-                       int32_t block_start, int32_t block_len, const int32_t* history,
-                       const int32_t* history_len, int32_t history_cap, int32_t k, int32_t* rows,
-                       int32_t* n_rows, hipStream_t stream) {
-  const int32_t st = ec::check_select(full_flag, is_masked, L, block_start, block_len, history,
-                                      history_len, history_cap, k, rows, n_rows);
+                       int32_t block_start, int32_t block_len, int32_t block_causal,
+                       const int32_t* history, const int32_t* history_len, int32_t history_cap,
+                       int32_t k, int32_t* rows, int32_t* n_rows, hipStream_t stream) {
+  const int32_t st = ec::check_select(full_flag, is_masked, L, block_start, block_len,
+                                      block_causal, history, history_len, history_cap, k, rows,
+                                      n_rows);
   if (st != EC_OK) return st;
-  EC_TRY(ec::launch_select_rows(full_flag, is_masked, L, block_start, block_len, history,
-                                history_len, history_cap, k, rows, n_rows, nullptr, nullptr,
-                                nullptr, stream));
+  EC_TRY(ec::launch_select_rows(full_flag, is_masked, L, block_start, block_len, block_causal,
+                                history, history_len, history_cap, k, rows, n_rows, nullptr,
+                                nullptr, nullptr, stream));
   return EC_OK;
 }
 
@@ -242,25 +243,33 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   const int dt = m->dtype;
   const int L = st->L;
   const int hd = m->Hq * m->dh;
-  // A partial step selects at most block_len + k rows (the block's masked
-  // positions and the last k decoded ones); a full step selects all L, which
-  // the small-row kernels see only when L <= kSmallMaxRows.
-  const int64_t part_rows = int64_t(c->block_len) + c->k;
-  const int part_hi = part_rows >= L ? L : int(part_rows);
-  const int sk_rows = L <= ec::kSmallMaxRows ? L : part_hi;
+  // A full step selects all L rows (block diffusion: the block_len rows of
+  // the current block); a partial step at most block_len + k (the block's
+  // masked positions and the last k decoded ones; block diffusion: those in
+  // the block).  The small-row kernels see a full step only when it selects
+  // at most kSmallMaxRows rows.
+  const bool causal = c->block_causal != 0;
+  const int full_rows = causal ? c->block_len : L;
+  const int64_t part_rows = causal ? int64_t(c->block_len) : int64_t(c->block_len) + c->k;
+  const int part_hi = part_rows >= full_rows ? full_rows : int(part_rows);
+  const int sk_rows = full_rows <= ec::kSmallMaxRows ? full_rows : part_hi;
   // The most rows this step can select, and the row-count paths it can reach
   // (a caller-stated mode leaves out the other mode's kernels).
-  const int hi = c->mode == EC_MODE_PARTIAL ? part_hi : L;
+  const int hi = c->mode == EC_MODE_PARTIAL ? part_hi : full_rows;
   unsigned paths = 0;
-  if (c->mode != EC_MODE_FULL || L <= ec::kSmallMaxRows) paths |= ec::kPathSmall;
+  if (c->mode != EC_MODE_FULL || full_rows <= ec::kSmallMaxRows) paths |= ec::kPathSmall;
   if (hi > ec::kSmallMaxRows) paths |= ec::kPathLarge;
+  // Keys each recomputed row attends to: the whole sequence, or (block
+  // diffusion) the positions before the current block's end.
+  const int L_keys = causal ? c->block_start + c->block_len : L;
   const bool maybe_full = c->mode != EC_MODE_PARTIAL;
   const PhaseTimer tm{phase_events, stream};
 
   EC_TRY(tm.begin(EC_PHASE_SELECT));
   EC_TRY(ec::launch_select_rows(st->full_flag, st->is_masked, L, c->block_start, c->block_len,
-                                st->history, st->history_len, st->history_cap, c->k, st->rows,
-                                st->n_rows, s.cand_pos, s.cand_idx, s.n_cand, stream));
+                                c->block_causal, st->history, st->history_len, st->history_cap,
+                                c->k, st->rows, st->n_rows, s.cand_pos, s.cand_idx, s.n_cand,
+                                stream));
   EC_TRY(tm.end(EC_PHASE_SELECT));
   EC_TRY(tm.begin(EC_PHASE_EMBED));
   EC_TRY(ec::launch_embed(dt, m->tok_emb, m->pos_emb, st->tokens, st->rows, st->n_rows, hi, m->d,
@@ -293,7 +302,7 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
 
     ec::AttnArgs a;
     a.dtype = dt; a.q = s.q; a.n_rows_dev = st->n_rows; a.max_rows = hi; a.k_cache = st->k_cache[l];
-    a.v_cache = st->v_cache[l]; a.L = L; a.L_cap = m->L_cap; a.Hq = m->Hq; a.Hkv = m->Hkv;
+    a.v_cache = st->v_cache[l]; a.L = L_keys; a.L_cap = m->L_cap; a.Hq = m->Hq; a.Hkv = m->Hkv;
     a.dh = m->dh; a.scale = 1.0f / sqrtf(float(m->dh)); a.out = s.o; a.paths = paths;
     a.small_rows = sk_rows;
     EC_TRY(ec::launch_attention(a, s.attn_ws, stream));

@@ -51,10 +51,11 @@ namespace ec {
 // ---- row selection -----------------------------------------------------------
 int32_t select_max_L();
 hipError_t launch_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
-                              int32_t block_start, int32_t block_len, const int32_t* history,
-                              const int32_t* history_len, int32_t history_cap, int32_t k,
-                              int32_t* rows, int32_t* n_rows, int32_t* cand_pos,
-                              int32_t* cand_idx, int32_t* n_cand, hipStream_t s);
+                              int32_t block_start, int32_t block_len, int32_t block_causal,
+                              const int32_t* history, const int32_t* history_len,
+                              int32_t history_cap, int32_t k, int32_t* rows, int32_t* n_rows,
+                              int32_t* cand_pos, int32_t* cand_idx, int32_t* n_cand,
+                              hipStream_t s);
 
 // ---- glue --------------------------------------------------------------------
 hipError_t launch_embed(int dtype, const void* tok_emb, const void* pos_emb, const int32_t* tokens,

@@ -28,13 +28,14 @@ int32_t check_entropy(const void* logits, int32_t dtype, int64_t n_rows, int64_t
 }
 
 int32_t check_select(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
-                     int32_t block_start, int32_t block_len, const int32_t* history,
-                     const int32_t* history_len, int32_t history_cap, int32_t k,
-                     const int32_t* rows, const int32_t* n_rows) {
+                     int32_t block_start, int32_t block_len, int32_t block_causal,
+                     const int32_t* history, const int32_t* history_len, int32_t history_cap,
+                     int32_t k, const int32_t* rows, const int32_t* n_rows) {
   if (!full_flag || !is_masked || !history || !history_len || !rows || !n_rows) return EC_E_NULL;
   if (L < 1 || block_start < -1 || block_len < 0 || block_len > L ||
       (block_start >= 0 && int64_t(block_start) + block_len > L) || k < 0 || history_cap < 1 ||
-      k > history_cap)
+      k > history_cap || (block_causal != 0 && block_causal != 1) ||
+      (block_causal && block_start < 0))
     return EC_E_SHAPE;
   if (L > kSelectMaxL) return EC_E_UNSUPPORTED;
   return EC_OK;
@@ -104,7 +105,8 @@ int32_t check_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, 
       c->block_len > st->L ||
       (c->block_start >= 0 && int64_t(c->block_start) + c->block_len > st->L) || c->k < 0 ||
       c->k > st->history_cap || c->n_unmask < 0 || st->history_cap < 1 ||
-      (c->mode != EC_MODE_DEVICE && c->mode != EC_MODE_FULL && c->mode != EC_MODE_PARTIAL))
+      (c->mode != EC_MODE_DEVICE && c->mode != EC_MODE_FULL && c->mode != EC_MODE_PARTIAL) ||
+      (c->block_causal != 0 && c->block_causal != 1) || (c->block_causal && c->block_start < 0))
     return EC_E_SHAPE;
   if (external && (c->n_unmask < 1 || c->n_unmask > c->block_len)) return EC_E_SHAPE;
   const int km = k_multiple(m->dtype);

@@ -18,9 +18,9 @@ int32_t check_entropy(const void* logits, int32_t dtype, int64_t n_rows, int64_t
                       int32_t max_decoded, const float* row_entropy, const float* e_max,
                       const int32_t* full_flag);
 int32_t check_select(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
-                     int32_t block_start, int32_t block_len, const int32_t* history,
-                     const int32_t* history_len, int32_t history_cap, int32_t k,
-                     const int32_t* rows, const int32_t* n_rows);
+                     int32_t block_start, int32_t block_len, int32_t block_causal,
+                     const int32_t* history, const int32_t* history_len, int32_t history_cap,
+                     int32_t k, const int32_t* rows, const int32_t* n_rows);
 int32_t check_refresh(const void* x, int64_t x_stride, const int32_t* rows, const int32_t* n_rows,
                       int32_t max_rows, const void* w_qkv, int32_t d, int32_t Hq, int32_t Hkv,
                       int32_t dh, int32_t dtype, const void* q_out, const void* k_cache,

@@ -12,6 +12,12 @@
 // name sliding-window decoding among the strategies the method applies to
 // (Portuguese page §5, Chinese page §5).
 //
+// Block diffusion (block_causal): only rows of the current block are ever
+// recomputed.  A full step takes the whole block; a partial step its masked
+// positions and those of the last k decoded positions that lie inside it (the
+// blocks before it are final).  The Chinese page (§5) names block diffusion
+// as a place for the entropy signal to drive sub-block recomputation.
+//
 // One workgroup: the union is marked in an LDS bitmap over [0, L), then
 // compacted with a workgroup prefix sum over popcounts, which yields the rows
 // in ascending order with duplicates removed.  The same pass can report, for
@@ -48,7 +54,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int& tot
 
 __global__ __launch_bounds__(kThreads) void select_rows_kernel(
     const int32_t* __restrict__ full_flag, const uint8_t* __restrict__ is_masked, int32_t L,
-    int32_t block_start, int32_t block_len, const int32_t* __restrict__ history,
+    int32_t block_start, int32_t block_len, int32_t block_causal, const int32_t* __restrict__ history,
     const int32_t* __restrict__ history_len, int32_t history_cap, int32_t k,
     int32_t* __restrict__ rows, int32_t* __restrict__ n_rows, int32_t* __restrict__ cand_pos,
     int32_t* __restrict__ cand_idx, int32_t* __restrict__ n_cand) {
@@ -72,10 +78,12 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(
     block_len = min(block_len, L - block_start);
   }
   const int bend = block_start + block_len;
+  // the positions a step may recompute: all of them, or the current block
+  const int lo = block_causal ? block_start : 0, hi = block_causal ? bend : L;
 
   if (full) {
-    for (int p = tid; p < L; p += kThreads) rows[p] = p;
-    if (tid == 0) *n_rows = L;
+    for (int p = lo + tid; p < hi; p += kThreads) rows[p - lo] = p;
+    if (tid == 0) *n_rows = hi - lo;
   } else {
     for (int w = tid; w < nwords; w += kThreads) bits[w] = 0u;
     __syncthreads();
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(
     const int kk = min(k, hl);
     for (int j = tid; j < kk; j += kThreads) {
       const int p = history[(hl - kk + j) % history_cap];
-      if (p >= 0 && p < L) atomicOr(&bits[p >> 5], 1u << (p & 31));
+      if (p >= lo && p < hi) atomicOr(&bits[p >> 5], 1u << (p & 31));
     }
     __syncthreads();
     // Each thread owns a contiguous run of words, so ranks come out ascending.
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(
     if (is_c) {
       int rank;
       if (full) {
-        rank = p;
+        rank = p - lo;
       } else {
         const int wp = p >> 5;
         const int owner = wp / per;
@@ -138,14 +146,15 @@ __global__ __launch_bounds__(kThreads) void select_rows_kernel(
 int32_t select_max_L() { return kSelectMaxL; }
 
 hipError_t launch_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
-                              int32_t block_start, int32_t block_len, const int32_t* history,
-                              const int32_t* history_len, int32_t history_cap, int32_t k,
-                              int32_t* rows, int32_t* n_rows, int32_t* cand_pos,
-                              int32_t* cand_idx, int32_t* n_cand, hipStream_t s) {
+                              int32_t block_start, int32_t block_len, int32_t block_causal,
+                              const int32_t* history, const int32_t* history_len,
+                              int32_t history_cap, int32_t k, int32_t* rows, int32_t* n_rows,
+                              int32_t* cand_pos, int32_t* cand_idx, int32_t* n_cand,
+                              hipStream_t s) {
   const size_t lds = size_t((L + 31) / 32) * sizeof(uint32_t);
   hipLaunchKernelGGL(select_rows_kernel, dim3(1), dim3(kThreads), lds, s, full_flag, is_masked, L,
-                     block_start, block_len, history, history_len, history_cap, k, rows, n_rows,
-                     cand_pos, cand_idx, n_cand);
+                     block_start, block_len, block_causal, history, history_len, history_cap, k,
+                     rows, n_rows, cand_pos, cand_idx, n_cand);
   return hipGetLastError();
 }
 

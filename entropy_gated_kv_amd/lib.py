@@ -21,7 +21,7 @@ EC_NOALLOC_SCRATCH_BYTES = 8 << 20     # of include/ec.h
 PHASES = ("select", "embed", "qkv", "attn", "oproj", "ffn", "lmhead", "entropy", "decide")
 
 _lib: Optional[C.CDLL] = None
-ABI_VERSION = 4                  # EC_ABI_VERSION of include/ec.h
+ABI_VERSION = 5                  # EC_ABI_VERSION of include/ec.h
 
 
 class EcError(RuntimeError):
@@ -57,7 +57,8 @@ class ec_state(C.Structure):
 
 class ec_step_cfg(C.Structure):
     _fields_ = [("tau", C.c_float), ("k", C.c_int32), ("n_unmask", C.c_int32),
-                ("block_start", C.c_int32), ("block_len", C.c_int32), ("mode", C.c_int32)]
+                ("block_start", C.c_int32), ("block_len", C.c_int32), ("mode", C.c_int32),
+                ("block_causal", C.c_int32)]
 
 
 _P, _I32, _I64, _F32, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
@@ -70,7 +71,7 @@ _SIGS = {
                               _P, _SZ, _P]),
     "ec_entropy_max_noalloc": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _I32, _F32, _P, _P, _P,
                                       _P, _P, _P]),
-    "ec_select_rows": (_I32, [_P, _P, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
+    "ec_select_rows": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _P]),
     "ec_kv_refresh_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "ec_kv_refresh": (_I32, [_P, _I64, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
                              _I32, _P, _SZ, _P]),
@@ -161,10 +162,11 @@ def ec_entropy_max_noalloc(logits, tau: float, row_entropy, e_max, full_flag, *,
 
 
 def ec_select_rows(full_flag, is_masked, block_start: int, block_len: int, history, history_len,
-                   k: int, rows, n_rows, *, L: Optional[int] = None, stream=None) -> None:
+                   k: int, rows, n_rows, *, L: Optional[int] = None, block_causal: int = 0,
+                   stream=None) -> None:
     L = is_masked.numel() if L is None else L
     _check("ec_select_rows", load().ec_select_rows(
-        _ptr(full_flag), _ptr(is_masked), L, block_start, block_len, _ptr(history),
+        _ptr(full_flag), _ptr(is_masked), L, block_start, block_len, block_causal, _ptr(history),
         _ptr(history_len), history.numel(), k, _ptr(rows), _ptr(n_rows), _stream(stream)))
 
 

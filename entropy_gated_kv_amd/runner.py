@@ -140,12 +140,20 @@ class DeviceSequence:
         self.struct.kv_drift = self.kv_drift.data_ptr()
 
     def step(self, tau: float, k: int, block_start: int, block_len: int, n_unmask: int,
-             phase_events=None, mode: int = L.EC_MODE_DEVICE) -> None:
+             phase_events=None, mode: int = L.EC_MODE_DEVICE, block_causal: bool = False) -> None:
         """One ec_step.  mode: EC_MODE_DEVICE (the flag stays on the device), or
-        EC_MODE_FULL / EC_MODE_PARTIAL when the caller has read full_flag."""
+        EC_MODE_FULL / EC_MODE_PARTIAL when the caller has read full_flag.
+        block_causal: block diffusion (rows of the current block only, keys
+        before its end)."""
         cfg = L.ec_step_cfg(float(tau), int(k), int(n_unmask), int(block_start), int(block_len),
-                            int(mode))
+                            int(mode), int(bool(block_causal)))
         L.ec_step(self.model.struct, self.struct, cfg, self.ws, phase_events)
+
+    def commit(self, k: int, block_start: int, block_len: int, phase_events=None) -> None:
+        """Block diffusion: make a finished block's K/V final (the flag set on
+        the device, then a full pass over the block that decodes nothing)."""
+        self.full_flag.fill_(1)
+        self.step(0.0, k, block_start, block_len, 0, phase_events, block_causal=True)
 
     def step_host_mode(self, tau: float, k: int, block_start: int, block_len: int, n_unmask: int,
                        phase_events=None) -> int:

@@ -54,7 +54,7 @@ const char* ec_status_string(int32_t status);
 
 /* ABI revision of this header; bumped on any signature or struct change. */
 int32_t ec_abi_version(void);
-#define EC_ABI_VERSION 4
+#define EC_ABI_VERSION 5
 
 /* --------------------------------------------------------------------------
  * Entropy pass (a1) and decision (a2).
@@ -152,12 +152,21 @@ int32_t ec_entropy_max_noalloc(const void* logits, int32_t dtype, int64_t n_rows
  * positions from the first masked position, clipped at L (empty when nothing
  * is masked), found on the device (Portuguese page §5 and Chinese page §5 name
  * sliding-window decoding among the strategies the method applies to).
+ * Block diffusion: block_causal = 1 restricts both sets to the current block
+ * (the blocks before it are final): a full step selects
+ *   rows = block_start, ..., block_start + block_len - 1
+ * and a partial step the block's masked positions plus those of the last
+ * min(k, *history_len) history entries that lie inside the block.  The
+ * Chinese page (§5, generality) names block diffusion as a place for the
+ * entropy signal to drive sub-block recomputation; the step runs such blocks
+ * with block-causal attention (ec_step_cfg.block_causal).
  * Outputs: rows [L] (device, first *n_rows valid) and *n_rows (device).
  * Errors: EC_E_NULL, EC_E_SHAPE (L < 1, block outside [0, L), block_start < -1,
- * block_len > L, k < 0, k > history_cap, history_cap < 1), EC_E_LAUNCH.
+ * block_len > L, k < 0, k > history_cap, history_cap < 1, block_causal not 0
+ * or 1, block_causal with block_start = -1), EC_E_LAUNCH.
  * ------------------------------------------------------------------------ */
 int32_t ec_select_rows(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
-                       int32_t block_start, int32_t block_len,
+                       int32_t block_start, int32_t block_len, int32_t block_causal,
                        const int32_t* history, const int32_t* history_len, int32_t history_cap,
                        int32_t k, int32_t* rows, int32_t* n_rows, hipStream_t stream);
 
@@ -335,6 +344,15 @@ typedef struct ec_step_cfg {
   int32_t block_start;        /* or -1: sliding window (see ec_select_rows) */
   int32_t block_len;          /* <= max_block of the workspace             */
   int32_t mode;               /* EC_MODE_* (EC_E_SHAPE otherwise)          */
+  /* 1: block diffusion.  Rows are selected inside the current block only
+   * (ec_select_rows with block_causal = 1) and attend to the keys at
+   * positions [0, block_start + block_len): attention is block-causal, the
+   * blocks before the current one being final.  A finished block is made
+   * final by one step with *full_flag set to 1 and n_unmask = 0 (a full pass
+   * over its rows that decodes nothing; it leaves *full_flag = 0).
+   * Requires block_start >= 0.  Chinese page §5 (generality): entropy as the
+   * recompute signal for sub-blocks in block diffusion. */
+  int32_t block_causal;
 } ec_step_cfg;
 
 /* Optional per-phase timing: when non-NULL, phase_events holds 2*EC_PHASE_COUNT

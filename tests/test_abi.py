@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ec_abi_version() == 4
+    assert lib.ec_abi_version() == 5
     for s in range(-7, 1):
         assert lib.ec_status_string(s)
     assert lib.ec_status_string(99) == b"unknown status"
@@ -94,9 +94,12 @@ def test_noalloc_entropy_argument_checks(lib):
 
 
 def test_select_and_refresh_and_attention_checks(lib):
-    assert lib.ec_select_rows(FAKE, FAKE, 10, 8, 4, FAKE, FAKE, 16, 4, FAKE, FAKE, None) == -2
-    assert lib.ec_select_rows(FAKE, FAKE, 10, 0, 4, FAKE, FAKE, 2, 4, FAKE, FAKE, None) == -2
-    assert lib.ec_select_rows(None, FAKE, 10, 0, 4, FAKE, FAKE, 16, 4, FAKE, FAKE, None) == -1
+    assert lib.ec_select_rows(FAKE, FAKE, 10, 8, 4, 0, FAKE, FAKE, 16, 4, FAKE, FAKE, None) == -2
+    assert lib.ec_select_rows(FAKE, FAKE, 10, 0, 4, 0, FAKE, FAKE, 2, 4, FAKE, FAKE, None) == -2
+    assert lib.ec_select_rows(None, FAKE, 10, 0, 4, 0, FAKE, FAKE, 16, 4, FAKE, FAKE, None) == -1
+    # block diffusion: the flag is 0 or 1 and needs an explicit block
+    assert lib.ec_select_rows(FAKE, FAKE, 10, 0, 4, 2, FAKE, FAKE, 16, 4, FAKE, FAKE, None) == -2
+    assert lib.ec_select_rows(FAKE, FAKE, 10, -1, 4, 1, FAKE, FAKE, 16, 4, FAKE, FAKE, None) == -2
     assert lib.ec_kv_refresh(FAKE, 256, FAKE, FAKE, 4, FAKE, 256, 4, 4, 48, 1, FAKE, FAKE, FAKE,
                              16, None, 0, None) == -7              # head dim 48
     assert lib.ec_kv_refresh(FAKE, 64, FAKE, FAKE, 4, FAKE, 64, 4, 4, 32, 1, FAKE, FAKE, FAKE,

@@ -10,7 +10,7 @@ from synth import generators as G
 pytestmark = pytest.mark.gpu
 
 
-def gpu_select(full, masked, bs, bl, hist, k, cap):
+def gpu_select(full, masked, bs, bl, hist, k, cap, causal=False):
     Lq = len(masked)
     ring = np.full(cap, -1, dtype=np.int32)
     for i, p in enumerate(hist):
@@ -18,7 +18,8 @@ def gpu_select(full, masked, bs, bl, hist, k, cap):
     t = lambda a, dt=torch.int32: torch.tensor(np.asarray(a), dtype=dt, device="cuda")  # noqa: E731
     rows = torch.full((Lq,), -1, dtype=torch.int32, device="cuda")
     n = torch.zeros(1, dtype=torch.int32, device="cuda")
-    L.ec_select_rows(t([full]), t(masked, torch.uint8), bs, bl, t(ring), t([len(hist)]), k, rows, n)
+    L.ec_select_rows(t([full]), t(masked, torch.uint8), bs, bl, t(ring), t([len(hist)]), k, rows, n,
+                     block_causal=int(causal))
     torch.cuda.synchronize()
     return rows.cpu().numpy()[: int(n.item())]
 
@@ -52,6 +53,32 @@ def test_history_ring_wraps():
     want = O.select_rows(0, masked, 272, 16, hist, 20)
     got = gpu_select(0, masked, 272, 16, hist, 20, 20)
     np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("L_", [40, 1000, 8224, 32800])
+def test_block_causal_selection_matches_oracle(L_):
+    """Block diffusion: full steps take the block, partial steps its masked
+    positions and the history entries inside it; history entries before the
+    block (earlier blocks) and past it are left out."""
+    for seed in range(6):
+        bl = 32
+        bs = (L_ // 2) // bl * bl if L_ > 2 * bl else 0
+        masked = np.zeros(L_, dtype=np.uint8)
+        masked[bs:bs + bl] = G.random_mask(seed, L_, 0.5)[bs:bs + bl]
+        masked[bs + bl:] = 1
+        inside = np.flatnonzero(masked[bs:bs + bl] == 0) + bs
+        before = np.arange(0, bs)
+        hist = list(G.random_history(seed, before, min(len(before), 50))) + \
+            list(G.random_history(seed + 3, inside, len(inside)))
+        if bs + bl < L_:
+            hist.insert(len(hist) // 2, bs + bl)        # a position past the block
+        for k in (0, 1, 8, 64):
+            cap = max(k, 1) + seed * 5
+            want = O.select_rows(0, masked, bs, bl, hist, k, block_causal=True)
+            got = gpu_select(0, masked, bs, bl, hist, k, cap, causal=True)
+            np.testing.assert_array_equal(got, want, err_msg=f"L={L_} seed={seed} k={k}")
+        got = gpu_select(1, masked, bs, bl, hist, 8, 16, causal=True)
+        np.testing.assert_array_equal(got, np.arange(bs, bs + bl))
 
 
 @pytest.mark.parametrize("L_", [1, 77, 1000, 32800])

@@ -109,6 +109,47 @@ def test_tiny_fp32_trajectory_free_running(tau):
         assert_close(v, st.V[l], "f32", "final V cache")
 
 
+@pytest.mark.parametrize("tau", [1.5, math.inf, -math.inf])
+def test_tiny_fp32_block_diffusion_free_running(tau):
+    """Block diffusion (block-causal attention, the entropy gate inside the
+    current block, commits), free-running: rows, decisions and tokens exact,
+    logits and caches within the fp32 tolerance, for gated, always-partial
+    and always-full steps."""
+    cfg = C.scaled(C.TINY, name="tiny_bd", block_len=16, k=4)
+    model, st, dm, ds = setup(cfg)
+    n_partial = 0
+    for i, (kind, bs, bl, n) in enumerate(block_diffusion_actions(cfg, 10 ** 6)):
+        if kind == "commit":
+            tr = O.commit(model, st, bs, bl, cfg.k)
+            ds.commit(cfg.k, bs, bl)
+        else:
+            tr = O.step(model, st, tau, cfg.k, bs, bl, n, block_causal=True)
+            ds.step(tau, cfg.k, bs, bl, n, block_causal=True)
+        g = read(ds, len(tr.cand))
+        n_partial += int(kind == "step" and tr.flag_used == 0 and len(tr.rows) < bl)
+        np.testing.assert_array_equal(g["rows"], tr.rows, err_msg=f"step {i} rows")
+        np.testing.assert_array_equal(g["chosen"], tr.chosen, err_msg=f"step {i} chosen")
+        np.testing.assert_array_equal(g["tokens"], st.tokens, err_msg=f"step {i} tokens")
+        assert g["flag"] == tr.flag_next, i
+        if kind == "step":
+            np.testing.assert_array_equal(g["argmax"], tr.argmax, err_msg=f"step {i} argmax")
+            assert abs(g["E"] - tr.E) <= 1e-4 + 1e-5 * abs(tr.E), (i, g["E"], tr.E)
+            assert_close(g["logits"], tr.logits, "f32", f"step {i} logits")
+            assert decisions_on_stored_logits(g, tr.cand, n, tau, f"step {i}") == 0
+    if tau == math.inf:
+        assert n_partial > 5
+    for l in range(cfg.model.n_layers):
+        k, v = ds.caches(l)
+        assert_close(k, st.K[l], "f32", "final K cache")
+        assert_close(v, st.V[l], "f32", "final V cache")
+
+
+@pytest.mark.parametrize("cfg_fn", [gpu_single_cfg, gpu_stack_cfg])
+def test_bf16_block_diffusion_teacher_forced(cfg_fn):
+    _, _, _, n_partial = check_teacher_forced(cfg_fn(), 40, 1.0, block_causal=True)
+    assert n_partial > 3
+
+
 def test_tiny_fp32_tau_near_each_E():
     """The decision inside the step, bit for bit: before each step tau is set
     within 1e-3 nats of that step's E (known from the oracle, since E does not
@@ -248,22 +289,41 @@ def tie_guard(ambiguous):
     return 2 + math.ceil(ambiguous / 3)
 
 
-def check_teacher_forced(cfg, n_steps, tau):
+def block_diffusion_actions(cfg, n_steps):
+    """Block diffusion: the prompt's blocks committed, then the first n_steps
+    denoising steps, each finished block committed after its last step."""
+    acts = [("commit", bs, cfg.block_len, 0) for bs in range(0, cfg.prompt_len, cfg.block_len)]
+    sched = C.unmask_schedule(cfg)
+    for i, (bs, bl, n) in enumerate(sched[:n_steps]):
+        acts.append(("step", bs, bl, n))
+        if i + 1 == len(sched) or sched[i + 1][0] != bs:
+            acts.append(("commit", bs, bl, 0))
+    return acts
+
+
+def check_teacher_forced(cfg, n_steps, tau, block_causal=False):
     """Returns (ties against the oracle's trajectory, oracle decisions inside
     the logit-tolerance zone, float32 ties on the GPU's own logits, partial
-    steps)."""
+    steps).  block_causal: block diffusion, commits included."""
     model, st, dm, ds = setup(cfg)
-    sched = C.unmask_schedule(cfg)[:n_steps]
+    if block_causal:
+        acts = block_diffusion_actions(cfg, n_steps)
+    else:
+        acts = [("step", bs, bl, n) for bs, bl, n in C.unmask_schedule(cfg)[:n_steps]]
     ties = 0
     ambiguous = 0
     p1_ties = 0
     n_partial = 0
     worst = 0.0
-    for i, (bs, bl, n) in enumerate(sched):
+    for i, (kind, bs, bl, n) in enumerate(acts):
         ds.load_state(st.tokens, st.masked, st.history, st.flag, st.K, st.V)
         before = st.copy()
-        tr = O.step(model, st, tau, cfg.k, bs, bl, n)
-        ds.step(tau, cfg.k, bs, bl, n)
+        if kind == "commit":
+            tr = O.commit(model, st, bs, bl, cfg.k)
+            ds.commit(cfg.k, bs, bl)
+        else:
+            tr = O.step(model, st, tau, cfg.k, bs, bl, n, block_causal=block_causal)
+            ds.step(tau, cfg.k, bs, bl, n, block_causal=block_causal)
         g = read(ds, len(tr.cand))
         n_partial += int(tr.flag_used == 0)
         np.testing.assert_array_equal(g["rows"], tr.rows, err_msg=f"step {i} rows")
@@ -274,6 +334,9 @@ def check_teacher_forced(cfg, n_steps, tau):
             keep = np.setdiff1d(np.arange(cfg.L), tr.rows)
             assert np.array_equal(k[:, keep], before.K[l][:, keep]), "unselected K rows changed"
             assert np.array_equal(v[:, keep], before.V[l][:, keep]), "unselected V rows changed"
+        if kind == "commit":
+            assert g["flag"] == tr.flag_next == 0 and len(g["chosen"]) == 0, i
+            continue
         tol = logit_tol(model, tr)
         err = np.abs(g["logits"] - tr.logits)
         assert np.all(err <= tol), (i, float((err / tol).max()))
@@ -317,7 +380,7 @@ def check_teacher_forced(cfg, n_steps, tau):
             assert abs(tr.E - tau) < e_tol, (i, tr.E, tau)
             ties += 1
             print(f"tie: step {i} flag, E = {tr.E} tau = {tau}", file=sys.stderr)
-    print(f"{cfg.name}: {len(sched)} steps ({n_partial} partial), {ties} ties against the "
+    print(f"{cfg.name}: {len(acts)} steps ({n_partial} partial), {ties} ties against the "
           f"oracle's trajectory ({ambiguous} oracle decisions the measured logit error could "
           f"flip), {p1_ties} "
           f"float32 ties on the GPU's logits, worst logit error / tolerance = {worst:.3f}",

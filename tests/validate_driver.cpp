@@ -73,10 +73,13 @@ void hand_cases() {
   EXPECT(ec::check_entropy(A, EC_BF16, 4, 100, INT64_MAX, nullptr, nullptr, 0, f, f, i) == EC_E_UNSUPPORTED);
   EXPECT(ec::check_entropy(A, EC_BF16, 4, 100, 104, i, nullptr, 4, f, f, i) == EC_E_NULL);
   // selection
-  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, 0, 4, i, i, 16, 4, i, i) == EC_OK);
-  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, 8, 4, i, i, 16, 4, i, i) == EC_E_SHAPE);
-  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, INT32_MAX, 4, i, i, 16, 4, i, i) == EC_E_SHAPE);
-  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 262145, 0, 4, i, i, 16, 4, i, i) == EC_E_UNSUPPORTED);
+  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, 0, 4, 0, i, i, 16, 4, i, i) == EC_OK);
+  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, 0, 4, 1, i, i, 16, 4, i, i) == EC_OK);
+  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, 8, 4, 0, i, i, 16, 4, i, i) == EC_E_SHAPE);
+  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, INT32_MAX, 4, 0, i, i, 16, 4, i, i) == EC_E_SHAPE);
+  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 262145, 0, 4, 0, i, i, 16, 4, i, i) == EC_E_UNSUPPORTED);
+  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, -1, 4, 1, i, i, 16, 4, i, i) == EC_E_SHAPE);
+  EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, 0, 4, 2, i, i, 16, 4, i, i) == EC_E_SHAPE);
   // refresh and attention
   EXPECT(ec::check_refresh(A, 4096, i, i, 96, A, 4096, 32, 32, 128, EC_BF16, A, A, A, 1024, nullptr) == EC_OK);
   EXPECT(ec::check_refresh(A, 4096, i, i, 96, A, 4096, 32, 32, 48, EC_BF16, A, A, A, 1024, nullptr) == EC_E_UNSUPPORTED);
@@ -111,7 +114,7 @@ struct StepCase {
     st.n_chosen = static_cast<int32_t*>(A); st.e_max = static_cast<float*>(A);
     st.kv_drift = nullptr; st.attn_out = nullptr;
     c.tau = 1.f; c.k = 16; c.n_unmask = 2; c.block_start = 96; c.block_len = 32;
-    c.mode = EC_MODE_DEVICE;
+    c.mode = EC_MODE_DEVICE; c.block_causal = 0;
   }
 };
 
@@ -144,7 +147,7 @@ void fuzz(int rounds) {
     (void)ec::check_entropy(ptr<void>(), pick32() % 3, pick64(), pick64(), pick64(),
                             ptr<int32_t>(), ptr<int32_t>(), pick32(), ptr<float>(), ptr<float>(),
                             ptr<int32_t>());
-    (void)ec::check_select(ptr<int32_t>(), ptr<uint8_t>(), pick32(), pick32(), pick32(),
+    (void)ec::check_select(ptr<int32_t>(), ptr<uint8_t>(), pick32(), pick32(), pick32(), pick32() % 3,
                            ptr<int32_t>(), ptr<int32_t>(), pick32(), pick32(), ptr<int32_t>(),
                            ptr<int32_t>());
     (void)ec::check_refresh(ptr<void>(), pick64(), ptr<int32_t>(), ptr<int32_t>(), pick32(),
@@ -162,7 +165,7 @@ void fuzz(int rounds) {
     if (rng() % 4 == 0) s.m.norm_final = ptr<void>();
     s.st.L = pick32(); s.st.history_cap = pick32();
     s.c.k = pick32(); s.c.n_unmask = pick32(); s.c.block_start = pick32();
-    s.c.block_len = pick32(); s.c.mode = pick32() % 4;
+    s.c.block_len = pick32(); s.c.mode = pick32() % 4; s.c.block_causal = pick32() % 3;
     if (rng() % 4 == 0) s.st.attn_out = ptr<void>();
     if (rng() % 4 == 0) s.layers[rng() % size_t(n_layers)].w_o = ptr<void>();
     if (rng() % 4 == 0) s.kc[rng() % size_t(n_layers)] = ptr<void>();
