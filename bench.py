@@ -521,6 +521,38 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
                                 "speedup_vs_vanilla": round(sl_ec["steps_per_s"] / sl_van["steps_per_s"], 3)}
     _log(f"sliding window: {out['sliding_window_32']}")
 
+    # block diffusion: block-causal attention over blocks of 32 (the prompt's
+    # 16 blocks committed first, untimed), the entropy gate inside the current
+    # block, each finished block committed after its last step.  Timed: the
+    # 352 denoising steps and the 16 commits of the generated blocks.
+    def block_diffusion(t):
+        reset()
+        for b0 in range(0, cfg.prompt_len, cfg.block_len):
+            ds.commit(cfg.k, b0, cfg.block_len)
+        torch.cuda.synchronize()
+        fl2 = torch.zeros(len(sched), dtype=torch.int32, device="cuda")
+        t1 = time.perf_counter()
+        for i, (bs, bl, nn) in enumerate(sched):
+            fl2[i].copy_(ds.full_flag[0])
+            ds.step(t, cfg.k, bs, bl, nn, block_causal=True)
+            if i + 1 == len(sched) or sched[i + 1][0] != bs:
+                ds.commit(cfg.k, bs, bl)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t1
+        return ({"steps_per_s": round(len(sched) / dt, 2),
+                 "partial_fraction": round(float(1.0 - fl2.float().mean().item()), 3)},
+                ds.tokens.cpu().numpy())
+
+    bd_van, bd_van_tok = block_diffusion(float("-inf"))
+    bd_ec, bd_tok = block_diffusion(tau)
+    bd_ec["token_agreement_vs_vanilla"] = round(float((bd_tok[gen] == bd_van_tok[gen]).mean()), 4)
+    out["block_diffusion_32"] = {
+        "entropycache_tau_1": bd_ec, "vanilla": bd_van,
+        "speedup_vs_vanilla": round(bd_ec["steps_per_s"] / bd_van["steps_per_s"], 3),
+        "note": "block-causal attention; full step = the current block's 32 rows; "
+                "steps/s counts denoising steps, the time includes the 16 block commits"}
+    _log(f"block diffusion: {out['block_diffusion_32']}")
+
     # KV drift on full steps (untimed): the E that triggered each full step
     # next to the Value drift that step measured
     reset()
@@ -1027,6 +1059,7 @@ def main() -> int:
             "k_ablation_tau_1": res["k_ablation_tau_1"],
             "kv_drift_tau_1": res.get("kv_drift_tau_1"),
             "sliding_window_32": res.get("sliding_window_32"),
+            "block_diffusion_32": res.get("block_diffusion_32"),
         }
         if "cpu_baseline" in res:
             line["cpu_baseline"] = res["cpu_baseline"]
