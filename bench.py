@@ -104,6 +104,39 @@ def record_traffic(fetch_dir: str, write_dir: str) -> dict:
     return rec
 
 
+def _kernel_key(r):
+    import re
+    name = re.sub(r"\(anonymous namespace\)::", "", r["Kernel_Name"])
+    name = re.sub(r"^void ", "", name.split("(")[0]).replace("ec::", "")
+    grid = r["Grid_Size"] if "Grid_Size" in r else r["Grid_Size_X"]          # counter / trace CSVs
+    wg = r["Workgroup_Size"] if "Workgroup_Size" in r else r["Workgroup_Size_X"]
+    return name, int(grid) // max(1, int(wg))
+
+
+def summarize_trace(trace_dir: str, min_us: float) -> str:
+    """Markdown table of a `rocprofv3 --kernel-trace` run (CSV output
+    directory), per kernel and grid: calls, the calls longer than min_us
+    (device-gated launches that exit at once are shorter), the median and
+    maximum duration of those, and the total time of all calls."""
+    import collections
+    import csv
+    import glob
+    import statistics
+
+    groups = collections.defaultdict(list)
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                groups[_kernel_key(r)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    out = [f"| kernel | workgroups | calls | calls > {min_us:g} us | median of those (us) | max (us) | total (ms) |",
+           "|---|---|---|---|---|---|---|"]
+    for (name, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        big = [x for x in v if x > min_us]
+        med = f"{statistics.median(big):.1f}" if big else "-"
+        out.append(f"| `{name}` | {wg} | {len(v)} | {len(big)} | {med} | {max(v):.1f} | {sum(v) / 1e3:.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def summarize_counters(dirs) -> str:
     """Markdown table of `rocprofv3 --pmc` runs (CSV output directories), per
     kernel and grid, over the dispatches that did work (device-gated launches
@@ -1005,6 +1038,10 @@ def main() -> int:
                     help="run the fixed short sequence used for hardware-counter runs")
     ap.add_argument("--profile-mfma", choices=("dream8k", "dream32k", "llada", "stack"),
                     help="run one workload's fixed short sequence, for counter runs")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown table of a rocprofv3 --kernel-trace run and exit")
+    ap.add_argument("--min-us", type=float, default=3.0,
+                    help="with --summarize-trace: calls at most this long count as gated exits")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                     help="print a markdown table of rocprofv3 --pmc runs (CSV directories)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -1015,6 +1052,9 @@ def main() -> int:
         return 0
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
+        return 0
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.min_us))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
