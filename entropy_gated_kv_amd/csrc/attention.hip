@@ -538,7 +538,8 @@ struct BP {
   float* mlpart;        // split (m, l)     [smax][Hkv][mcap][2]
   int mcap;             // packed-row capacity of the split workspace
   int smax;             // split capacity of the split workspace
-  int partial;          // 1: split-KV variant (n <= 128), 0: unsplit
+  int partial;          // 1: split-KV variant (n <= 128), 0: unsplit, 2: the
+                        // launch takes either role, by the device row count
   // split-KV variant: the plan, made on the host for a bound nb on the row
   // count (min(max_rows, 128)): qa query tiles, S splits of `per` kv tiles,
   // over the packed rows of nb rows (mb = nb * G)
@@ -718,8 +719,9 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
   // exits before loading anything.
   const int n_dev = *p.n_rows;
   const int j = xcd_work_index(blockIdx.x, gridDim.x);
+  const bool part = p.partial == 2 ? min(n_dev, p.max_rows) <= kPartialMaxRows : p.partial != 0;
   int n, M, g, qt, kv0, kv1, split = 0;
-  if (p.partial) {
+  if (part) {
     if (j >= p.Hkv * p.S * p.qa) return;
     qt = j % p.qa;
     split = (j / p.qa) % p.S;
@@ -784,7 +786,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
         qf[qb][it * B::VH + v] = ok ? *reinterpret_cast<const u32x4*>(qrow + it * 128 + (h * B::VH + v) * 16)
                                     : u32x4{0u, 0u, 0u, 0u};
   }
-  if (p.partial && p.spec) {
+  if (part && p.spec) {
     // the device row count: a query tile past the rows (or a count outside
     // this variant's range) ends the workgroup once its copies have landed
     n = min(n_dev, p.max_rows);
@@ -893,7 +895,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(BP p) {
     const float l_tot = halves_sum(l_run[qb]);
     const int rho = rho0 + qb * 32 + (lane & 31);
     if (rho >= M) continue;
-    if (p.partial) {
+    if (part) {
       const int64_t prow = (int64_t(split) * p.Hkv + g) * p.mcap + rho;
       uint16_t* op = p.opart + prow * DH;
       // bf16 partials: half the bytes written here and read by the merge
@@ -1061,30 +1063,51 @@ hipError_t launch_bf16(const AttnArgs& a, void* ws, hipStream_t s) {
                              b.grid_p, b.smax);
   p.qa = d.qa; p.S = d.S; p.per = d.per; p.mb = nb * p.G;
   p.spec = (a.max_rows <= kPartialMaxRows || !(a.paths & kPathLarge)) ? 1 : 0;
-  hipError_t e = hipSuccess;
-  if (a.paths & kPathSmall) {
-    p.partial = 1;
-    e = launch_bf16_shape<DH>(p, b.sp, unsigned(b.grid_p), s);
-    if (e != hipSuccess) return e;
-    const int64_t rows = int64_t(a.Hkv) * p.mb;                     // (g, rho) rows of the bound
-    hipLaunchKernelGGL((attn_bf16_merge_kernel<DH>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
-                       p, b.sp.nw * 32 * b.sp.qb, b.grid_p);
-    e = hipGetLastError();
-  }
-  if (e != hipSuccess || a.max_rows <= kPartialMaxRows || !(a.paths & kPathLarge)) return e;
+  const bool small = (a.paths & kPathSmall) != 0;
+  const bool large = a.max_rows > kPartialMaxRows && (a.paths & kPathLarge);
   // unsplit variant (n > 128); when the eight-wave query tiles would leave CUs
   // idle (e.g. MHA at L = 1024: 32 heads x 4 tiles), four-wave tiles of 128
   // rows double the workgroups
-  p.partial = 0;
   BShape sh = full_shape(DH);
-  int qt = sh.nw * 32 * sh.qb;
-  int64_t groups = (int64_t(a.max_rows) * p.G + qt - 1) / qt * a.Hkv;
-  if (DH >= 64 && groups < device_cu_count()) {
-    sh = BShape{4, 1, 3, 1, 0};
-    qt = sh.nw * 32 * sh.qb;
-    groups = (int64_t(a.max_rows) * p.G + qt - 1) / qt * a.Hkv;
+  unsigned grid_full = 0;
+  if (large) {
+    int qt = sh.nw * 32 * sh.qb;
+    int64_t groups = (int64_t(a.max_rows) * p.G + qt - 1) / qt * a.Hkv;
+    if (DH >= 64 && groups < device_cu_count()) {
+      sh = BShape{4, 1, 3, 1, 0};
+      qt = sh.nw * 32 * sh.qb;
+      groups = (int64_t(a.max_rows) * p.G + qt - 1) / qt * a.Hkv;
+    }
+    grid_full = unsigned((groups + 7) / 8 * 8);
   }
-  return launch_bf16_shape<DH>(p, sh, unsigned((groups + 7) / 8 * 8), s);
+  auto merge = [&]() {
+    const int64_t rows = int64_t(a.Hkv) * p.mb;                     // (g, rho) rows of the bound
+    hipLaunchKernelGGL((attn_bf16_merge_kernel<DH>), dim3(unsigned((rows + 3) / 4)), dim3(256), 0, s,
+                       p, b.sp.nw * 32 * b.sp.qb, b.grid_p);
+    return hipGetLastError();
+  };
+  // Both variants with one kernel shape and an unsplit grid no larger than
+  // the split one (the LLaDA-shaped layer): one launch whose workgroups take
+  // the split or the unsplit role from the device row count, saving the
+  // launch of the variant that does not apply.  With a larger unsplit grid
+  // (the Dream-shaped layer: 3592 workgroups at L = 32800) the workgroups
+  // that exit at once on a partial step would queue behind the working ones
+  // (one workgroup's LDS fills a CU) and cost far more than a launch.
+  if (small && large && sh.nw == b.sp.nw && sh.qb == b.sp.qb && sh.ns == b.sp.ns &&
+      sh.pipe == b.sp.pipe && grid_full <= unsigned(b.grid_p)) {
+    p.partial = 2;
+    const hipError_t e = launch_bf16_shape<DH>(p, sh, unsigned(b.grid_p), s);
+    return e != hipSuccess ? e : merge();
+  }
+  if (small) {
+    p.partial = 1;
+    hipError_t e = launch_bf16_shape<DH>(p, b.sp, unsigned(b.grid_p), s);
+    if (e == hipSuccess) e = merge();
+    if (e != hipSuccess) return e;
+  }
+  if (!large) return hipSuccess;
+  p.partial = 0;
+  return launch_bf16_shape<DH>(p, sh, grid_full, s);
 }
 
 }  // namespace
