@@ -5,7 +5,9 @@ cache rows not selected must be bitwise unchanged (sentinel-filled caches).
 Row counts cover 1..4 row blocks of the skinny kernel (each row-bound
 instance), the 128-row boundary, split-K over a non-power-of-two count,
 the tiled kernel with a ragged last tile (in each of its tile
-configurations), and the LLaDA-shaped full size.
+configurations), and the LLaDA- and Dream-shaped full sizes (every row of the
+partial-step shapes; 64 rows of the 1024-row full step, all tile edges
+among them).
 """
 import numpy as np
 import pytest
@@ -73,17 +75,35 @@ def test_bf16_every_tile_config(tile, consecutive, monkeypatch):
     run_case("bf16", 512, 8, 2, 128, Lc, rows, seed=int(tile) + 40)
 
 
-@pytest.mark.parametrize("n", [96, 1024])
-def test_llada_full_size_sampled(n):
-    Lc = 1024
-    rows = np.arange(Lc) if n == Lc else np.sort(np.random.default_rng(3).choice(Lc, n, replace=False))
-    run_case("bf16", 4096, 32, 32, 128, Lc, rows, seed=5, sample=[0, 1, n // 2, n - 1])
+def tile_edge_sample(n, tile, count, seed):
+    """Rows at both edges of every `tile`-row tile, the last row, and random
+    rows up to `count`."""
+    edges = sorted({r for t in range(0, n, tile) for r in (t, t + 1, min(n, t + tile) - 1)})
+    rest = np.setdiff1d(np.arange(n), edges)
+    extra = np.random.default_rng(seed).choice(rest, max(0, count - len(edges)), replace=False)
+    return np.sort(np.concatenate([edges, extra]).astype(np.int64))
+
+
+def test_llada_full_size_partial_every_row():
+    """The LLaDA-shaped refresh of a partial step (96 scattered rows of 1024,
+    d 4096, 32 x 128 heads): every row of Q, K and V against the oracle."""
+    Lc, n = 1024, 96
+    rows = np.sort(np.random.default_rng(3).choice(Lc, n, replace=False))
+    run_case("bf16", 4096, 32, 32, 128, Lc, rows, seed=5)
+
+
+def test_llada_full_size_full_step_sampled():
+    """A full step (all 1024 rows, the tiled kernel): 64 rows checked, among
+    them both edges of every 256-row tile."""
+    Lc = n = 1024
+    run_case("bf16", 4096, 32, 32, 128, Lc, np.arange(Lc), seed=5,
+             sample=tile_edge_sample(n, 256, 64, 7))
 
 
 @pytest.mark.parametrize("n", [40, 96])
-def test_dream_shape_split_k_sampled(n):
+def test_dream_shape_split_k_every_row(n):
     """Dream-shaped refresh (d = 3584, 28/4 heads of 128): 28 k-iterations
-    split seven ways, with the four- and six-block row instances."""
+    split seven ways, with the four- and six-block row instances; every row."""
     Lc = 1024
     rows = np.sort(np.random.default_rng(11 + n).choice(Lc, n, replace=False))
-    run_case("bf16", 3584, 28, 4, 128, Lc, rows, seed=60 + n, sample=[0, 1, n // 2, n - 1])
+    run_case("bf16", 3584, 28, 4, 128, Lc, rows, seed=60 + n)
