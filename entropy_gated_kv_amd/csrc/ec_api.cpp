@@ -226,6 +226,14 @@ struct PhaseTimer {
 
 extern "C" {
 
+int32_t ec_pack_lm_head(const void* w_lm, int32_t V, int32_t d, int32_t dtype, void* w_packed,
+                        hipStream_t stream) {
+  const int32_t st = ec::check_pack(w_lm, V, d, dtype, w_packed);
+  if (st != EC_OK) return st;
+  EC_TRY(ec::launch_pack_fragments(w_lm, V, d, w_packed, stream));
+  return EC_OK;
+}
+
 size_t ec_step_workspace_bytes(const ec_model* m, int32_t max_block) {
   if (!m || !ec::model_ok(m) || !dtype_ok(m->dtype) || max_block < 1) return 0;
   return step_layout(m, max_block, nullptr).total;
@@ -363,6 +371,7 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   gl.dtype = dt; gl.epi = ec::Epi::kLogits; gl.A = xf; gl.lda = m->d; gl.a_idx = s.cand_idx;
   gl.n_rows_dev = s.n_cand; gl.max_rows = max_block; gl.W = m->w_lm; gl.N = m->V; gl.K = m->d;
   gl.C = st->logits; gl.ldc = m->V; gl.scale = m->logit_scale; gl.scale_pos = s.cand_pos;
+  gl.W_packed = m->w_lm_packed;
   EC_TRY(ec::launch_gemm_rows(gl, s.gemm_ws, stream));
   EC_TRY(tm.end(EC_PHASE_LMHEAD));
 

@@ -99,6 +99,9 @@ struct GemmArgs {
   unsigned paths = kPathSmall | kPathLarge;
   const void* W = nullptr;
   const void* W2 = nullptr;
+  // kLogits, bf16: W in the fragment layout (launch_pack_fragments), or null;
+  // the skinny LM-head kernel then reads it instead of W
+  const void* W_packed = nullptr;
   int N = 0, K = 0;
   void* C = nullptr;
   int64_t ldc = 0;
@@ -116,6 +119,9 @@ size_t gemm_ws_bytes(const GemmArgs& a);
 // Reduction dimensions (d, Hq*dh, d_ffn) must be multiples of this (128 bf16, 64 fp32).
 int gemm_k_multiple(int dtype);
 hipError_t launch_gemm_rows(const GemmArgs& a, void* ws, hipStream_t s);
+// Repack a bf16 [N, K] weight (N % 16 == 0, K % 32 == 0) into the fragment
+// layout read by the skinny LM-head kernel; out holds N * K elements.
+hipError_t launch_pack_fragments(const void* W, int64_t N, int64_t K, void* out, hipStream_t s);
 
 // ---- KV drift of a full step (diagnostic) ------------------------------------------
 // Workspace: a copy of one layer's transposed Value cache [nrow = Hkv * dh, L_cap]

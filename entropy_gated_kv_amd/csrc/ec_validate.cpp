@@ -4,6 +4,7 @@
 #include "ec_validate.h"
 
 #include <math.h>
+#include <stdint.h>
 
 #include "ec_limits.h"
 
@@ -81,6 +82,18 @@ bool model_ok(const ec_model* m) {
          m->Hq % m->Hkv == 0 && m->V >= 1 && m->L_cap >= 1 && m->d_ffn >= 0;
 }
 
+int32_t check_pack(const void* w_lm, int32_t V, int32_t d, int32_t dtype, const void* w_packed) {
+  if (!w_lm || !w_packed) return EC_E_NULL;
+  if (dtype != EC_BF16) return EC_E_DTYPE;
+  if (V < 16 || V % 16 != 0 || d < 32 || d % 32 != 0) return EC_E_SHAPE;
+  if (int64_t(V) * d > (int64_t(1) << 40)) return EC_E_UNSUPPORTED;
+  if (!aligned16(w_lm) || !aligned16(w_packed)) return EC_E_ALIGN;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w_lm), b = reinterpret_cast<uintptr_t>(w_packed);
+  const uintptr_t n = uintptr_t(int64_t(V) * d * 2);
+  if (a < b + n && b < a + n) return EC_E_SHAPE;              // the copy may not overlap its source
+  return EC_OK;
+}
+
 int32_t check_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, const void* ws) {
   if (!m || !st || !c || !ws) return EC_E_NULL;
   if (!dtype_ok(m->dtype)) return EC_E_DTYPE;
@@ -122,6 +135,12 @@ int32_t check_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, 
       (int64_t(m->L_cap) * int64_t(elem_size(m->dtype))) % 16 != 0)
     return EC_E_ALIGN;
   if (m->d_ffn && !external && !aligned16(m->norm_final)) return EC_E_ALIGN;
+  if (m->w_lm_packed) {
+    if (external) return EC_E_NULL;                          // a packed copy of no LM head
+    if (m->dtype != EC_BF16) return EC_E_DTYPE;
+    if (m->V % 16 != 0) return EC_E_SHAPE;
+    if (!aligned16(m->w_lm_packed)) return EC_E_ALIGN;
+  }
   if (st->attn_out && !aligned16(st->attn_out)) return EC_E_ALIGN;
   for (int l = 0; l < m->n_layers; ++l) {
     const ec_layer& ly = m->layers[l];

@@ -17,6 +17,8 @@ int32_t check_entropy(const void* logits, int32_t dtype, int64_t n_rows, int64_t
                       int64_t row_stride, const int32_t* decoded_rows, const int32_t* n_decoded,
                       int32_t max_decoded, const float* row_entropy, const float* e_max,
                       const int32_t* full_flag);
+// ec_pack_lm_head
+int32_t check_pack(const void* w_lm, int32_t V, int32_t d, int32_t dtype, const void* w_packed);
 int32_t check_select(const int32_t* full_flag, const uint8_t* is_masked, int32_t L,
                      int32_t block_start, int32_t block_len, int32_t block_causal,
                      const int32_t* history, const int32_t* history_len, int32_t history_cap,

@@ -70,6 +70,7 @@ struct GP {
   int max_rows;
   const void* W;
   const void* W2;
+  const void* Wpk;   // the same W in 1 KB fragments (pack_fragments), or null
   int N, K;
   void* C;
   int64_t ldc;
@@ -159,7 +160,7 @@ template <typename T, int NV = kNV> constexpr int skit() { return NV * 4 * (16 /
 // which streams its weights 3-4% faster with eight (512 contiguous bytes of
 // each of a wave's 16 rows per iteration, half the barriers per byte); at
 // four the smaller ring leaves registers for the larger row bounds.
-template <typename T, int MB, bool DUAL, int EPI, int NV>
+template <typename T, int MB, bool DUAL, int EPI, int NV, bool PK = false>
 __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem) {
   constexpr int VPL = 16 / int(sizeof(T));
   constexpr int KIT = skit<T, NV>();
@@ -171,7 +172,12 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
   const int nit = p.KS / KIT;                               // K splits evenly (host plan)
   const int col = tile * kSkinnyNT + wave * 16 + (lane & 15);
   const T* A = static_cast<const T*>(p.A);
-  const T* Wp = static_cast<const T*>(p.W) + int64_t(min(col, p.N - 1)) * p.K + k0 + g * VPL;
+  // PK: W read from its fragment layout, where the 16 rows x 32 k that one
+  // load instruction of a wave takes are one contiguous 1 KB block in lane
+  // order, and a wave's blocks follow one another (8 KB per iteration)
+  const int grp = min(tile * (kSkinnyNT / 16) + wave, p.N / 16 - 1);
+  const T* Wp = PK ? static_cast<const T*>(p.Wpk) + (int64_t(grp) * (p.K / 32) + k0 / 32) * 64 * VPL + lane * VPL
+                   : static_cast<const T*>(p.W) + int64_t(min(col, p.N - 1)) * p.K + k0 + g * VPL;
   const T* W2p = DUAL ? static_cast<const T*>(p.W2) + int64_t(min(col, p.N - 1)) * p.K + k0 + g * VPL
                       : nullptr;
 
@@ -209,7 +215,7 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
   auto w_load = [&](WBuf& dst, const T* src, int it) {
 #pragma unroll
     for (int v = 0; v < NV; ++v)
-      dst[v] = *reinterpret_cast<const u32x4*>(src + it * KIT + v * 4 * VPL);
+      dst[v] = *reinterpret_cast<const u32x4*>(src + (PK ? (it * NV + v) * 64 * VPL : it * KIT + v * 4 * VPL));
   };
 
   f32x4 acc[MB], acc2[DUAL ? MB : 1];
@@ -331,13 +337,14 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
 // row count.  Each instance holds only the bodies up to MBX, so its register
 // footprint (and with it the waves per SIMD) follows the bound: at 96 rows the
 // six-block instance keeps three waves per SIMD where the eight-block one has two.
-template <typename T, int MBX, bool DUAL, int EPI, int NV = kNV>
+template <typename T, int MBX, bool DUAL, int EPI, int NV = kNV, bool PK = false>
 __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(GP p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int n_rows = min(*p.n_rows, p.max_rows);
   if (n_rows <= 0 || n_rows > kSkinnyMaxRows) return;
   const int mb = (n_rows + 15) / 16;
-  if (MBX == 2 || mb <= 2) skinny_body<T, 2, DUAL, EPI, NV>(p, n_rows, smem);
+  static_assert(!PK || MBX == 2, "the fragment layout serves the LM-head instance");
+  if (MBX == 2 || mb <= 2) skinny_body<T, 2, DUAL, EPI, NV, PK>(p, n_rows, smem);
   else if constexpr (MBX >= 4) {
     if (MBX == 4 || mb <= 4) skinny_body<T, 4, DUAL, EPI, NV>(p, n_rows, smem);
     else if constexpr (MBX >= 6) {
@@ -870,9 +877,9 @@ Plan plan_skinny(const GemmArgs& a) {
 
 size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
 
-template <typename T, int MBX, bool DUAL, int EPI, int NV = kNV>
+template <typename T, int MBX, bool DUAL, int EPI, int NV = kNV, bool PK = false>
 void go_skinny(dim3 g, size_t lds, hipStream_t s, const GP& p) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, MBX, DUAL, EPI, NV>), g, dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, MBX, DUAL, EPI, NV, PK>), g, dim3(kThreads), lds, s, p);
 }
 
 template <typename T, int EPI, bool DUAL = false>
@@ -891,6 +898,12 @@ hipError_t dispatch_skinny(Epi epi, const Plan& pl, dim3 g, size_t lds, hipStrea
     case Epi::kResidual: skinny_by_shape<T, 2>(pl, g, lds, s, p); break;
     case Epi::kSwiGLU: skinny_by_shape<T, 3, true>(pl, g, lds, s, p); break;
     case Epi::kLogits:
+      if constexpr (sizeof(T) == 2) {
+        if (pl.NV == 2 * kNV && p.Wpk != nullptr) {
+          go_skinny<T, 2, false, 4, 2 * kNV, true>(g, lds, s, p);
+          break;
+        }
+      }
       if (pl.NV == 2 * kNV) go_skinny<T, 2, false, 4, 2 * kNV>(g, lds, s, p);
       else skinny_by_shape<T, 4>(pl, g, lds, s, p);
       break;
@@ -915,6 +928,8 @@ hipError_t launch_typed(const GemmArgs& a, void* ws, hipStream_t s, bool allow_s
   GP p;
   p.A = a.A; p.lda = a.lda; p.a_idx = a.a_idx; p.n_rows = a.n_rows_dev; p.max_rows = a.max_rows;
   p.W = a.W; p.W2 = a.W2; p.N = a.N; p.K = a.K; p.C = a.C; p.ldc = a.ldc; p.epi = int(a.epi);
+  // the fragment layout: bf16 LM head, whole 16-row groups, one skinny split
+  p.Wpk = (sizeof(T) == 2 && a.epi == Epi::kLogits && a.N % 16 == 0) ? a.W_packed : nullptr;
   p.rows = a.rows; p.q = a.q_out; p.kc = a.k_cache; p.vc = a.v_cache; p.Hq = a.Hq; p.Hkv = a.Hkv;
   p.dh = a.dh; p.L_cap = a.L_cap; p.scale = a.scale; p.scale_pos = a.scale_pos;
   const bool dual = (a.epi == Epi::kSwiGLU);
@@ -981,6 +996,29 @@ size_t gemm_ws_bytes(const GemmArgs& a) {
   Plan pl = (a.dtype == 1) ? plan_skinny<bf16_t>(a) : plan_skinny<float>(a);
   if (pl.S <= 1) return 0;
   return up256(pl.part_floats * 4);
+}
+
+// The fragment layout of a bf16 [N, K] weight (N % 16 == 0, K % 32 == 0):
+// for each group of 16 rows, the K / 32 blocks of 16 rows x 32 k in k order,
+// a block being 1 KB in the lane order of one 16-byte load instruction of the
+// skinny kernel (lane l = 16 g + n holds row n, k 8g .. 8g + 7 of the block).
+// One thread per 16-byte chunk of W.
+__global__ __launch_bounds__(kThreads) void pack_fragments_kernel(const u32x4* __restrict__ W,
+                                                                  int64_t N, int64_t K,
+                                                                  u32x4* __restrict__ out) {
+  const int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t cpr = K / 8;                                   // chunks per row
+  if (idx >= N * cpr) return;
+  const int64_t r = idx / cpr, c = idx - r * cpr;
+  const int64_t block = (r / 16) * (K / 32) + c / 4;
+  out[block * 64 + (c % 4) * 16 + r % 16] = W[idx];
+}
+
+hipError_t launch_pack_fragments(const void* W, int64_t N, int64_t K, void* out, hipStream_t s) {
+  const int64_t chunks = N * (K / 8);
+  hipLaunchKernelGGL(pack_fragments_kernel, dim3(unsigned((chunks + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, static_cast<const u32x4*>(W), N, K, static_cast<u32x4*>(out));
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_rows(const GemmArgs& a, void* ws, hipStream_t s) {

@@ -21,7 +21,7 @@ EC_NOALLOC_SCRATCH_BYTES = 8 << 20     # of include/ec.h
 PHASES = ("select", "embed", "qkv", "attn", "oproj", "ffn", "lmhead", "entropy", "decide")
 
 _lib: Optional[C.CDLL] = None
-ABI_VERSION = 5                  # EC_ABI_VERSION of include/ec.h
+ABI_VERSION = 6                  # EC_ABI_VERSION of include/ec.h
 
 
 class EcError(RuntimeError):
@@ -42,7 +42,8 @@ class ec_model(C.Structure):
                 ("dh", C.c_int32), ("d_ffn", C.c_int32), ("V", C.c_int32), ("L_cap", C.c_int32),
                 ("dtype", C.c_int32), ("rms_eps", C.c_float), ("tok_emb", C.c_void_p),
                 ("pos_emb", C.c_void_p), ("layers", C.POINTER(ec_layer)),
-                ("norm_final", C.c_void_p), ("w_lm", C.c_void_p), ("logit_scale", C.c_void_p)]
+                ("norm_final", C.c_void_p), ("w_lm", C.c_void_p), ("logit_scale", C.c_void_p),
+                ("w_lm_packed", C.c_void_p)]
 
 
 class ec_state(C.Structure):
@@ -79,6 +80,7 @@ _SIGS = {
     "ec_bidir_attention": (_I32, [_P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32, _I32,
                                   _P, _P, _SZ, _P]),
     "ec_step_workspace_bytes": (_SZ, [C.POINTER(ec_model), _I32]),
+    "ec_pack_lm_head": (_I32, [_P, _I32, _I32, _I32, _P, _P]),
     "ec_step": (_I32, [C.POINTER(ec_model), C.POINTER(ec_state), C.POINTER(ec_step_cfg), _P, _SZ,
                        _P, _P]),
 }
@@ -198,6 +200,12 @@ def ec_bidir_attention(q, n_rows, k_cache, v_cache, L: int, out, ws, *, scale: O
     _check("ec_bidir_attention", load().ec_bidir_attention(
         _ptr(q), _ptr(n_rows), max_rows, _ptr(k_cache), _ptr(v_cache), L, L_cap, Hq, Hkv, dh,
         float(scale), dtype_code(q), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+
+
+def ec_pack_lm_head(w_lm, w_packed, *, stream=None) -> None:
+    V, d = w_lm.shape
+    _check("ec_pack_lm_head", load().ec_pack_lm_head(_ptr(w_lm), V, d, dtype_code(w_lm),
+                                                     _ptr(w_packed), _stream(stream)))
 
 
 def ec_step_workspace_bytes(model: ec_model, max_block: int) -> int:

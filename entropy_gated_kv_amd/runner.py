@@ -27,9 +27,13 @@ def to_device(a: np.ndarray, dtype: str):
 
 
 class DeviceModel:
-    """Weights in HBM plus the ec_model struct that points at them."""
+    """Weights in HBM plus the ec_model struct that points at them.
 
-    def __init__(self, shape, dtype: str, L_cap: int, weights: Dict[str, object]):
+    pack_lm_head: for a bf16 LM head with V % 16 == 0, also keep the copy that
+    ec_pack_lm_head lays out for streaming (the LM head then reads it)."""
+
+    def __init__(self, shape, dtype: str, L_cap: int, weights: Dict[str, object],
+                 pack_lm_head: bool = True):
         import torch
         self.shape, self.dtype, self.L_cap = shape, dtype, L_cap
         self.code = L.EC_BF16 if dtype == "bf16" else L.EC_F32
@@ -64,6 +68,13 @@ class DeviceModel:
         m.norm_final = None if self.norm_final is None else self.norm_final.data_ptr()
         m.w_lm = None if self.w_lm is None else self.w_lm.data_ptr()
         m.logit_scale = None if self.logit_scale is None else self.logit_scale.data_ptr()
+        self.w_lm_packed = None
+        if (pack_lm_head and self.w_lm is not None and dtype == "bf16" and shape.vocab % 16 == 0
+                and shape.d % 32 == 0):
+            self.w_lm_packed = torch.empty_like(self.w_lm)
+            L.ec_pack_lm_head(self.w_lm, self.w_lm_packed)
+            torch.cuda.synchronize()
+        m.w_lm_packed = None if self.w_lm_packed is None else self.w_lm_packed.data_ptr()
         self.struct = m
 
 

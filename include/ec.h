@@ -54,7 +54,7 @@ const char* ec_status_string(int32_t status);
 
 /* ABI revision of this header; bumped on any signature or struct change. */
 int32_t ec_abi_version(void);
-#define EC_ABI_VERSION 5
+#define EC_ABI_VERSION 6
 
 /* --------------------------------------------------------------------------
  * Entropy pass (a1) and decision (a2).
@@ -287,6 +287,11 @@ typedef struct ec_model {
   const void* norm_final;     /* [d] (d_ffn > 0 only)                      */
   const void* w_lm;           /* [V, d], or NULL: no LM head (see above)   */
   const float* logit_scale;   /* [L_cap] device float32, or NULL (= 1)     */
+  /* Optional: w_lm repacked by ec_pack_lm_head, or NULL.  When set (bf16,
+   * V % 16 == 0, 16-byte aligned), the LM head of steps whose block holds at
+   * most 32 positions reads it instead of w_lm (same arithmetic, same bits);
+   * w_lm must still be given. */
+  const void* w_lm_packed;
 } ec_model;
 
 typedef struct ec_state {
@@ -364,6 +369,22 @@ enum {
   EC_PHASE_SELECT = 0, EC_PHASE_EMBED, EC_PHASE_QKV, EC_PHASE_ATTN, EC_PHASE_OPROJ,
   EC_PHASE_FFN, EC_PHASE_LMHEAD, EC_PHASE_ENTROPY, EC_PHASE_DECIDE, EC_PHASE_COUNT
 };
+
+/* Repack the LM-head weight for streaming (an optional, one-time step at
+ * model load).  w_lm [V, d] bf16 row-major becomes, for each group of 16
+ * rows, its d / 32 blocks of 16 rows x 32 columns in column order; a block is
+ * 1 KB: entry (row n, columns 8g .. 8g + 7) of the block is its 16-byte
+ * chunk 16 g + n.  The LM head's loads then read each 8 KB of a group's
+ * weights from consecutive addresses.  The logits are those of w_lm (the
+ * LM head of Chinese page §2.2's forward pass; the layout changes only where
+ * the weights are read from).
+ * w_packed: device, V * d bf16 elements, caller-owned, 16-byte aligned, not
+ * overlapping w_lm.  Asynchronous on the stream.
+ * Errors: EC_E_NULL, EC_E_DTYPE (not bf16), EC_E_SHAPE (V < 16, V % 16 != 0,
+ * d < 32, d % 32 != 0), EC_E_UNSUPPORTED (V * d > 2^40), EC_E_ALIGN,
+ * EC_E_LAUNCH. */
+int32_t ec_pack_lm_head(const void* w_lm, int32_t V, int32_t d, int32_t dtype, void* w_packed,
+                        hipStream_t stream);
 
 size_t ec_step_workspace_bytes(const ec_model* model, int32_t max_block);
 

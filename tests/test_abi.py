@@ -34,7 +34,7 @@ def test_every_declared_function_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ec_abi_version() == 5
+    assert lib.ec_abi_version() == 6
     for s in range(-7, 1):
         assert lib.ec_status_string(s)
     assert lib.ec_status_string(99) == b"unknown status"
@@ -133,9 +133,10 @@ def test_step_rejects_misaligned_weights(lib):
         ly = L.ec_layer(**{f: bad.get(f, FAKE) for f in ("w_qkv", "w_o", "norm_attn", "norm_ffn",
                                                           "w_gate", "w_up", "w_down")})
         layers = (L.ec_layer * 1)(ly)
-        m = L.ec_model(n_layers=1, d=256, Hq=4, Hkv=4, dh=64, d_ffn=512, V=1024, L_cap=256, dtype=1,
-                       rms_eps=1e-5, tok_emb=FAKE, pos_emb=FAKE, layers=layers,
-                       norm_final=bad.get("norm_final", FAKE), w_lm=FAKE, logit_scale=None)
+        m = L.ec_model(n_layers=1, d=256, Hq=4, Hkv=4, dh=64, d_ffn=512, V=bad.get("V", 1024), L_cap=256,
+                       dtype=bad.get("dtype", 1), rms_eps=1e-5, tok_emb=FAKE, pos_emb=FAKE, layers=layers,
+                       norm_final=bad.get("norm_final", FAKE), w_lm=bad.get("w_lm", FAKE), logit_scale=None,
+                       w_lm_packed=bad.get("w_lm_packed"))
         caches = (C.c_void_p * 1)(FAKE)
         st = L.ec_state(L=256, tokens=FAKE, is_masked=FAKE, history=FAKE, history_len=FAKE,
                         history_cap=64, full_flag=FAKE, k_cache=caches, v_cache=caches, rows=FAKE,
@@ -154,6 +155,24 @@ def test_step_rejects_misaligned_weights(lib):
               "attn_out"):
         assert call(**{f: ODD}) == -5, f
     assert call(attn_out=FAKE) == -4                               # aligned: accepted
+    # the packed LM head: bf16, V % 16 == 0, aligned, and only with an LM head
+    assert call(w_lm_packed=FAKE) == -4
+    assert call(w_lm_packed=ODD) == -5
+    assert call(w_lm_packed=FAKE, V=1032) == -2
+    assert call(w_lm_packed=FAKE, dtype=0) == -3
+    assert call(w_lm_packed=FAKE, w_lm=None) == -1
+
+
+def test_pack_lm_head_argument_checks(lib):
+    f = lib.ec_pack_lm_head
+    other = FAKE + (1 << 30)
+    assert f(None, 1024, 256, 1, other, None) == -1
+    assert f(FAKE, 1024, 256, 0, other, None) == -3              # bf16 only
+    assert f(FAKE, 1032, 256, 1, other, None) == -2              # V % 16
+    assert f(FAKE, 1024, 250, 1, other, None) == -2              # d % 32
+    assert f(FAKE, 8, 256, 1, other, None) == -2
+    assert f(FAKE, 1024, 256, 1, ODD, None) == -5
+    assert f(FAKE, 1024, 256, 1, FAKE + 4096, None) == -2        # overlaps its source
 
 
 def test_validation_checks_under_host_sanitizers(tmp_path):

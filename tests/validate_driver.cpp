@@ -72,6 +72,14 @@ void hand_cases() {
   EXPECT(ec::check_entropy(U, EC_BF16, 4, 100, 104, nullptr, nullptr, 0, f, f, i) == EC_E_ALIGN);
   EXPECT(ec::check_entropy(A, EC_BF16, 4, 100, INT64_MAX, nullptr, nullptr, 0, f, f, i) == EC_E_UNSUPPORTED);
   EXPECT(ec::check_entropy(A, EC_BF16, 4, 100, 104, i, nullptr, 4, f, f, i) == EC_E_NULL);
+  // packed LM head
+  EXPECT(ec::check_pack(A, 1024, 256, EC_BF16, buf + 2048) == EC_E_SHAPE);   // overlaps its source
+  EXPECT(ec::check_pack(buf, 16, 32, EC_BF16, buf + 1024) == EC_OK);
+  EXPECT(ec::check_pack(nullptr, 16, 32, EC_BF16, buf + 1024) == EC_E_NULL);
+  EXPECT(ec::check_pack(buf, 16, 32, EC_F32, buf + 1024) == EC_E_DTYPE);
+  EXPECT(ec::check_pack(buf, 24, 32, EC_BF16, buf + 1024) == EC_E_SHAPE);
+  EXPECT(ec::check_pack(buf, 16, 32, EC_BF16, U) == EC_E_ALIGN);
+  EXPECT(ec::check_pack(buf, INT32_MAX - 15, INT32_MAX - 31, EC_BF16, buf + 1024) == EC_E_UNSUPPORTED);
   // selection
   EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, 0, 4, 0, i, i, 16, 4, i, i) == EC_OK);
   EXPECT(ec::check_select(i, reinterpret_cast<uint8_t*>(A), 10, 0, 4, 1, i, i, 16, 4, i, i) == EC_OK);
@@ -147,6 +155,7 @@ void fuzz(int rounds) {
     (void)ec::check_entropy(ptr<void>(), pick32() % 3, pick64(), pick64(), pick64(),
                             ptr<int32_t>(), ptr<int32_t>(), pick32(), ptr<float>(), ptr<float>(),
                             ptr<int32_t>());
+    (void)ec::check_pack(ptr<void>(), pick32(), pick32(), pick32() % 3, ptr<void>());
     (void)ec::check_select(ptr<int32_t>(), ptr<uint8_t>(), pick32(), pick32(), pick32(), pick32() % 3,
                            ptr<int32_t>(), ptr<int32_t>(), pick32(), pick32(), ptr<int32_t>(),
                            ptr<int32_t>());
@@ -167,6 +176,7 @@ void fuzz(int rounds) {
     s.c.k = pick32(); s.c.n_unmask = pick32(); s.c.block_start = pick32();
     s.c.block_len = pick32(); s.c.mode = pick32() % 4; s.c.block_causal = pick32() % 3;
     if (rng() % 4 == 0) s.st.attn_out = ptr<void>();
+    if (rng() % 4 == 0) s.m.w_lm_packed = ptr<void>();
     if (rng() % 4 == 0) s.layers[rng() % size_t(n_layers)].w_o = ptr<void>();
     if (rng() % 4 == 0) s.kc[rng() % size_t(n_layers)] = ptr<void>();
     (void)ec::check_step(&s.m, &s.st, &s.c, ptr<void>());
