@@ -26,9 +26,11 @@ that applies it.
 
 Pinned by tests/test_oracle_*.py against closed forms, library routines (scipy
 entropy, torch scaled-dot-product attention and rms_norm), brute force and the
-method's invariants.  The multi-layer partial trajectories (stale caches of
-unselected rows propagating through several layers) have no pin beyond the
-oracle's own definition: parity unpinned for that composite.
+method's invariants.  Two pins restate whole steps with torch full-sequence
+forwards: the storage rounding points (a correctly rounding float64 forward),
+and the multi-layer partial steps (stale caches of unselected rows propagating
+through several layers: a full forward whose unselected positions take their
+K/V from caches kept beside it), both bit for bit.
 """
 from .rounding import to_storage, round_bf16  # noqa: F401
 from .entropy import (softmax_entropy, row_stats, max_entropy, decide, entropy_max,  # noqa: F401
