@@ -234,12 +234,28 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
     if constexpr (DUAL) w_load(nxt2, W2p, min(it + 2, last));
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
+      if constexpr (PK) {
+        // The LM head reads the MB activation fragments of a column block
+        // together, then multiplies: one LDS round trip per block instead of
+        // MB, so each iteration ends (and the next weight loads go out) sooner.
+        // Four more registers, still three waves per SIMD; same products in
+        // the same order.
+        u32x4 af[MB];
 #pragma unroll
-      for (int rb = 0; rb < MB; ++rb) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(smem + (rb * 16 + (lane & 15)) * ROWB +
-                                                        (v * 4 + g) * 16);
-        Mma16<T>::run(acc[rb], a, cur[v]);
-        if constexpr (DUAL) Mma16<T>::run(acc2[rb], a, cur2[v]);
+        for (int rb = 0; rb < MB; ++rb)
+          af[rb] = *reinterpret_cast<const u32x4*>(smem + (rb * 16 + (lane & 15)) * ROWB + (v * 4 + g) * 16);
+        __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);   // the MB LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);   // then the MB MFMAs
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) Mma16<T>::run(acc[rb], af[rb], cur[v]);
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(smem + (rb * 16 + (lane & 15)) * ROWB +
+                                                          (v * 4 + g) * 16);
+          Mma16<T>::run(acc[rb], a, cur[v]);
+          if constexpr (DUAL) Mma16<T>::run(acc2[rb], a, cur2[v]);
+        }
       }
     }
     __syncthreads();                            // every wave is done with this stage
