@@ -69,5 +69,29 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+DRIVER_SRC = os.path.join(ROOT, "tests", "c_abi_driver.cpp")
+DRIVER = os.path.join(ROOT, "tests", "c_abi_driver")
+
+
+def build_c_driver() -> str:
+    """The test suite's plain C++ user of libec.so (host code only, so the
+    host compiler builds it against include/ec.h and the HIP runtime); it
+    finds libec.so next to the package through its run path."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        raise RuntimeError("g++ not found")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [gxx, "-std=c++17", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+           "-I", os.path.join(rocm, "include"), DRIVER_SRC, "-o", DRIVER + ".tmp",
+           "-L", PKG, "-lec", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../entropy_gated_kv_amd", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"driver build failed\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(DRIVER + ".tmp", DRIVER)
+    return DRIVER
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_driver())

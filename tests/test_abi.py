@@ -199,3 +199,24 @@ def test_validation_checks_under_host_sanitizers(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, (r.stdout + r.stderr)[-3000:]
     assert "all expectations held" in r.stdout
+
+
+def test_plain_cpp_driver_builds_against_the_header(tmp_path):
+    """tests/c_abi_driver.cpp, the suite's user of libec.so without the Python
+    binding, compiles and links with the host compiler from include/ec.h and
+    the HIP runtime alone (the GPU test runs it)."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no host C++ compiler")
+    lib_dir = os.path.join(ROOT, "entropy_gated_kv_amd")
+    if not os.path.exists(os.path.join(lib_dir, "libec.so")):
+        pytest.skip("libec.so is not built")
+    exe = str(tmp_path / "c_abi_driver")
+    cmd = [gxx, "-std=c++17", "-O1", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", "-I",
+           os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+           os.path.join(ROOT, "tests", "c_abi_driver.cpp"), "-o", exe, "-L", lib_dir, "-lec",
+           "-L", "/opt/rocm/lib", "-lamdhip64"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
