@@ -803,20 +803,23 @@ constexpr TileCfg kTileCfgs[] = {
     {256, 128, 1, 0.38f, 0.38f},    // 4 x 2 waves of 64 x 64
     {256, 192, 1, 0.47f, 0.47f},    // 4 x 2 waves of 64 x 96
     {256, 256, 1, 0.52f, 0.52f},    // 2 x 4 waves of 128 x 64
+    {128, 128, 1, 0.285f, 0.285f},  // 2 x 4 waves of 64 x 32, three stages: two waves per
+                                    // SIMD where a grid of 128 x 128 tiles fits one round
 };
+constexpr int kNumTileCfgs = int(sizeof(kTileCfgs) / sizeof(kTileCfgs[0]));
 constexpr int kDualCfgs[] = {1, 3};   // SwiGLU pair: columns of both matrices per tile
 
-// EC_GEMM_TILE=<0..3> forces a configuration (tests run every one; for the
+// EC_GEMM_TILE=<0..4> forces a configuration (tests run every one; for the
 // SwiGLU pair only configurations 1 and 3 exist and others are ignored).
 int pick_tile(int rows, int N, bool dual) {
   if (const char* e = getenv("EC_GEMM_TILE")) {
     const int c = atoi(e);
-    if (c >= 0 && c < 4 && (!dual || c == kDualCfgs[0] || c == kDualCfgs[1])) return c;
+    if (c >= 0 && c < kNumTileCfgs && (!dual || c == kDualCfgs[0] || c == kDualCfgs[1])) return c;
   }
   const int cus = device_cu_count();
   int best = -1;
   double best_cost = 0;
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < kNumTileCfgs; ++c) {
     if (dual && c != kDualCfgs[0] && c != kDualCfgs[1]) continue;
     const TileCfg& t = kTileCfgs[c];
     const int bn = dual ? t.bn / 2 : t.bn;            // per weight matrix
@@ -845,7 +848,8 @@ void tiled_by_cfg(int c, const GP& p, hipStream_t s) {
     case 0: go_tiled<128, 128, 2, 2, 2, 2, false, EPI>(p, s); break;
     case 1: go_tiled<256, 128, 4, 2, 3, 1, false, EPI>(p, s); break;
     case 2: go_tiled<256, 192, 4, 2, 2, 1, false, EPI>(p, s); break;
-    default: go_tiled<256, 256, 2, 4, 2, 1, false, EPI>(p, s); break;
+    case 3: go_tiled<256, 256, 2, 4, 2, 1, false, EPI>(p, s); break;
+    default: go_tiled<128, 128, 2, 4, 3, 1, false, EPI>(p, s); break;
   }
 }
 

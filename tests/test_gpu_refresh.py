@@ -64,7 +64,7 @@ def test_bf16_gqa_shapes(n, dh):
 
 
 @pytest.mark.parametrize("consecutive", [True, False], ids=["full", "scattered"])
-@pytest.mark.parametrize("tile", ["0", "1", "2", "3"])
+@pytest.mark.parametrize("tile", ["0", "1", "2", "3", "4"])
 def test_bf16_every_tile_config(tile, consecutive, monkeypatch):
     """Each tile configuration of the tiled kernel (forced), with a ragged
     last row tile and column tile; consecutive rows take the packed

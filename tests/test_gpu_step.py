@@ -394,7 +394,7 @@ def test_bf16_single_layer_teacher_forced():
     assert n_partial > 3
 
 
-@pytest.mark.parametrize("tile", [None, "0", "1", "2", "3"])
+@pytest.mark.parametrize("tile", [None, "0", "1", "2", "3", "4"])
 def test_bf16_two_layer_stack_teacher_forced(tile, monkeypatch):
     # full steps (160 rows) run the tiled GEMMs: the chosen tile, then each forced
     if tile is not None:
@@ -414,7 +414,7 @@ def test_bf16_stack_split_k_teacher_forced():
     assert n_partial > 3
 
 
-@pytest.mark.parametrize("tile", [None, "0", "1", "2", "3"])
+@pytest.mark.parametrize("tile", [None, "0", "1", "2", "3", "4"])
 def test_bf16_long_blocks_teacher_forced(tile, monkeypatch):
     """Two 160-position blocks, 16 tokens a step: the LM head takes up to 160
     candidate rows, so it runs the tiled (row-gathering) GEMM, and
