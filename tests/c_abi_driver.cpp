@@ -134,15 +134,14 @@ int main(int argc, char** argv) {
 
   FILE* out = fopen(argv[2], "wb");
   if (!out) return fail("cannot open output");
-  fwrite(st, sizeof st, 1, out);
-  fwrite(H, sizeof(float), n_rows, out);
-  fwrite(am, sizeof(int32_t), n_rows, out);
-  fwrite(p1, sizeof(float), n_rows, out);
-  fwrite(&E, sizeof E, 1, out);
-  fwrite(&flag, sizeof flag, 1, out);
-  fwrite(&n_sel, sizeof n_sel, 1, out);
-  fwrite(rows, sizeof(int32_t), n_sel, out);
-  fclose(out);
+  const bool wrote = fwrite(st, sizeof st, 1, out) == 1 &&
+                     fwrite(H, sizeof(float), n_rows, out) == size_t(n_rows) &&
+                     fwrite(am, sizeof(int32_t), n_rows, out) == size_t(n_rows) &&
+                     fwrite(p1, sizeof(float), n_rows, out) == size_t(n_rows) &&
+                     fwrite(&E, sizeof E, 1, out) == 1 && fwrite(&flag, sizeof flag, 1, out) == 1 &&
+                     fwrite(&n_sel, sizeof n_sel, 1, out) == 1 &&
+                     fwrite(rows, sizeof(int32_t), n_sel, out) == size_t(n_sel);
+  if (fclose(out) != 0 || !wrote) return fail("cannot write output");
 
   void* bufs[] = {d_logits, d_dec, d_ndec, d_H, d_argmax, d_p1, d_E, d_flag, d_ws, d_fflag, d_hist,
                   d_hlen, d_rows, d_nrows, d_masked};
