@@ -1062,7 +1062,7 @@ def main() -> int:
         print(summarize_trace(args.summarize_trace, args.min_us))
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the design notes describe how the step would shard)", file=sys.stderr)
         return 2
     import torch

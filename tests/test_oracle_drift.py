@@ -3,7 +3,7 @@ cosine distance, and the step's invariants.
 
 EntropyCache (zh) §2.1 and (pt) §2: the drift is measured on the Value vectors
 as a cosine distance; the aggregation (per position over the concatenated KV
-heads, then mean and max over positions) is this build's reading.
+heads, then mean and max over positions) is the reading taken here.
 """
 import numpy as np
 import pytest
