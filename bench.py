@@ -483,11 +483,21 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
                       "frac": round(iu / (by_mode[mode][name] * 1e3), 3)}
                for name, iu in ideal[mode].items() if name in by_mode[mode]}
         for mode in ideal}
+    # Each phase's events cost stream time of their own: the evented replay of
+    # the timed steps exceeds their event-free time by this much per phase
+    # (every phase the step runs records its pair, the empty decide phase
+    # included; a layer without FFN records none for it); the phase figures
+    # above are raw and include it.
+    evented = [k for k, name in enumerate(PHASES) if name != "ffn" or cfg.model.d_ffn > 0]
+    phase_sum_ms = float(np.mean([sum(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in evented)
+                                  for ev in bd_events]))
+    event_ovh_us = (phase_sum_ms - wall * 1e3 / steps) * 1e3 / len(evented)
     out = {
         "value": steps / wall,
         "ms_per_step": wall * 1e3 / steps,
         "partial_fraction": float(1.0 - fl.mean()),
         "phases_us": {k: round(v * 1e3, 2) for k, v in phase_ms.items()},
+        "phase_event_overhead_us": round(event_ovh_us, 2),
         "decision_overhead_frac": decide_ms / sum(phase_ms.values()),
         "phase_roofline": phase_roofline,
         "roofline": {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -1097,6 +1107,7 @@ def main() -> int:
             "roofline": res["roofline"],
             "partial_fraction": round(res["partial_fraction"], 3),
             "phases_us": res["phases_us"],
+            "phase_event_overhead_us": res["phase_event_overhead_us"],
             "decision_overhead_frac": round(res["decision_overhead_frac"], 4),
             "phase_roofline": res["phase_roofline"],
             "tau_sweep": res["tau_sweep"],
