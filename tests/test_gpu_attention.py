@@ -64,6 +64,29 @@ def test_bf16_shapes(n, Hq, Hkv, dh, q_std):
         assert np.abs(want).mean() > 0.05          # outputs above the tolerance floor
 
 
+@pytest.mark.parametrize("n", [1, 96, 127, 128, 129, 200])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (28, 4)])
+def test_device_row_count_below_the_buffer_bound(n, Hq, Hkv):
+    """A 200-row query buffer with the row count on the device: the launch
+    can take either role (split KV up to 128 rows, unsplit above), and the
+    count decides.  Rows past the count keep what the output held."""
+    dh, Lq, Lc, cap = 128, 1000, 1032, 200
+    q = G.random_matrix(n + Hq, (3,), (cap, Hq, dh), 2.0, "bf16")
+    K = G.random_matrix(n + Hq, (4,), (Hkv, Lc, dh), 1.0, "bf16")
+    V = G.random_matrix(n + Hq, (5,), (Hkv, Lc, dh), 1.0, "bf16")
+    out = torch.full((cap, Hq, dh), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(max(L.ec_attention_workspace_bytes(cap, Lq, Hq, Hkv, dh), 1), dtype=torch.uint8,
+                     device="cuda")
+    Vt = dev(np.ascontiguousarray(V.transpose(0, 2, 1)), "bf16")
+    L.ec_bidir_attention(dev(q, "bf16"), i32([n]), dev(K, "bf16"), Vt, Lq, out, ws)
+    torch.cuda.synchronize()
+    got = host(out)
+    want = O.bidir_attention(q[:n].astype(np.float64), K[:, :Lq].astype(np.float64),
+                             V[:, :Lq].astype(np.float64), 1 / math.sqrt(dh))
+    assert_close(got[:n], want, "bf16", "attention")
+    assert np.all(got[n:] == 7.0)
+
+
 @pytest.mark.parametrize("Lq", [8224, 32800])
 def test_dream_partial_step_every_output(Lq):
     """The long-context partial step's shape (96 rows, 28/4 heads x 128) over
