@@ -49,6 +49,35 @@ def run_case(dtype, d, Hq, Hkv, dh, Lc, rows, seed, sample=None):
     assert np.all(Kg[:, keep] == sentinel) and np.all(Vg[:, keep] == -sentinel), "unselected rows changed"
 
 
+@pytest.mark.parametrize("n", [1, 96, 128, 129, 300])
+def test_device_row_count_below_the_buffer_bound(n):
+    """A 300-row activation buffer with the row count on the device: the
+    small-row kernel runs up to 128 rows and the tiled one above, each
+    launched with the buffer's bound; only the first n rows are refreshed and
+    only their cache positions and Q rows change."""
+    d, Hq, Hkv, dh, Lc, cap = 512, 8, 2, 128, 644, 300
+    rows_all = np.sort(np.random.default_rng(n).choice(Lc, cap, replace=False))
+    x = G.random_matrix(n, (1, cap, d), (cap, d), 1.0, "bf16")
+    W = G.random_matrix(n, (2, d), ((Hq + 2 * Hkv) * dh, d), 0.02, "bf16")
+    K = torch.full((Hkv, Lc, dh), 7.0, dtype=torch.bfloat16, device="cuda")
+    Vt = torch.full((Hkv, dh, Lc), -7.0, dtype=torch.bfloat16, device="cuda")
+    q = torch.full((cap, Hq, dh), 3.0, dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(max(L.ec_kv_refresh_workspace_bytes(cap, d, Hq, Hkv, dh, L.EC_BF16), 1),
+                     dtype=torch.uint8, device="cuda")
+    L.ec_kv_refresh(dev(x, "bf16"), i32(rows_all), i32([n]), dev(W, "bf16"), Hq, Hkv, dh, q, K, Vt, ws)
+    torch.cuda.synchronize()
+    rows = rows_all[:n]
+    Ko, Vo = np.zeros((Hkv, Lc, dh)), np.zeros((Hkv, Lc, dh))
+    qo = O.kv_refresh(x[:n].astype(np.float64), rows, W.astype(np.float64), Ko, Vo, Hq, Hkv, dh, "bf16")
+    Kg, Vg, qg = host(K), host(Vt).transpose(0, 2, 1), host(q)
+    assert_close(qg[:n], qo, "bf16", "Q")
+    assert_close(Kg[:, rows], Ko[:, rows], "bf16", "K cache")
+    assert_close(Vg[:, rows], Vo[:, rows], "bf16", "V cache")
+    keep = np.setdiff1d(np.arange(Lc), rows)
+    assert np.all(Kg[:, keep] == 7.0) and np.all(Vg[:, keep] == -7.0), "unselected rows changed"
+    assert np.all(qg[n:] == 3.0), "Q rows past the count changed"
+
+
 @pytest.mark.parametrize("n", [1, 20, 64, 256])
 def test_tiny_fp32_shapes(n):
     rows = np.sort(np.random.default_rng(n).choice(256, n, replace=False))
