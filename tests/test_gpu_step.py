@@ -58,13 +58,13 @@ def gpu_stack_cfg():
                     model_d_ffn=512, prompt_len=96, gen_len=64, block_len=32, k=16)
 
 
-def setup(cfg, dtype=None):
+def setup(cfg, dtype=None, L_cap=None):
     dtype = dtype or cfg.dtype
     w = G.model_weights(cfg)
     model = O.Model.from_arrays(cfg.model, dtype, w)
     toks, masked = G.initial_sequence(cfg)
     st = O.init_state(model, toks, masked)
-    dm = DeviceModel(cfg.model, dtype, cfg.L, w)
+    dm = DeviceModel(cfg.model, dtype, L_cap or cfg.L, w)
     ds = DeviceSequence(dm, toks, masked, history_cap=max(cfg.gen_len, cfg.k), max_block=cfg.block_len)
     return model, st, dm, ds
 
@@ -107,6 +107,44 @@ def test_tiny_fp32_trajectory_free_running(tau):
         k, v = ds.caches(l)
         assert_close(k, st.K[l], "f32", "final K cache")
         assert_close(v, st.V[l], "f32", "final V cache")
+
+
+def fill_cache_tail(ds, L):
+    """Large K and V past position L (a cache longer than the sequence): a
+    step that attended past L would move every output."""
+    for l in range(len(ds.k_cache)):
+        ds.k_cache[l][:, L:, :] = 50.0
+        ds.v_cache[l][:, :, L:] = -50.0
+
+
+def cache_tail_untouched(ds, L):
+    return all(bool((ds.k_cache[l][:, L:, :] == 50.0).all()) and bool((ds.v_cache[l][:, :, L:] == -50.0).all())
+               for l in range(len(ds.k_cache)))
+
+
+@pytest.mark.parametrize("tau", [1.5, math.inf])
+def test_tiny_fp32_cache_longer_than_the_sequence(tau):
+    """L_cap = L + 72: the step attends over the L positions only and never
+    writes past them."""
+    cfg = C.TINY
+    model, st, dm, ds = setup(cfg, L_cap=cfg.L + 72)
+    fill_cache_tail(ds, cfg.L)
+    for i, (bs, bl, n) in enumerate(C.unmask_schedule(cfg)):
+        tr = O.step(model, st, tau, cfg.k, bs, bl, n)
+        ds.step(tau, cfg.k, bs, bl, n)
+        g = read(ds, len(tr.cand))
+        np.testing.assert_array_equal(g["rows"], tr.rows, err_msg=f"step {i} rows")
+        np.testing.assert_array_equal(g["chosen"], tr.chosen, err_msg=f"step {i} chosen")
+        assert g["flag"] == tr.flag_next, i
+        assert_close(g["logits"], tr.logits, "f32", f"step {i} logits")
+    assert cache_tail_untouched(ds, cfg.L)
+
+
+def test_bf16_stack_cache_longer_than_the_sequence():
+    """The two-layer bf16 stack teacher-forced with L_cap = L + 72."""
+    cfg = gpu_stack_cfg()
+    _, _, _, n_partial = check_teacher_forced(cfg, 12, 1.0, L_cap=cfg.L + 72)
+    assert n_partial > 3
 
 
 @pytest.mark.parametrize("tau", [1.5, math.inf, -math.inf])
@@ -301,11 +339,14 @@ def block_diffusion_actions(cfg, n_steps):
     return acts
 
 
-def check_teacher_forced(cfg, n_steps, tau, block_causal=False):
+def check_teacher_forced(cfg, n_steps, tau, block_causal=False, L_cap=None):
     """Returns (ties against the oracle's trajectory, oracle decisions inside
     the logit-tolerance zone, float32 ties on the GPU's own logits, partial
-    steps).  block_causal: block diffusion, commits included."""
-    model, st, dm, ds = setup(cfg)
+    steps).  block_causal: block diffusion, commits included.  L_cap: cache
+    capacity past the sequence, its tail filled with large values that no
+    step may read or write."""
+    model, st, dm, ds = setup(cfg, L_cap=L_cap)
+    fill_cache_tail(ds, cfg.L)
     if block_causal:
         acts = block_diffusion_actions(cfg, n_steps)
     else:
@@ -386,6 +427,7 @@ def check_teacher_forced(cfg, n_steps, tau, block_causal=False):
           f"float32 ties on the GPU's logits, worst logit error / tolerance = {worst:.3f}",
           file=sys.stderr)
     assert ties <= tie_guard(ambiguous), (ties, ambiguous)
+    assert cache_tail_untouched(ds, cfg.L), "cache positions past L changed"
     return ties, ambiguous, p1_ties, n_partial
 
 
