@@ -59,7 +59,7 @@ def _src_hash(*names: str) -> str:
 # carry, the source file, and which launches count (all, or the largest grid)
 TRAFFIC_KERNELS = {
     "entropy_partials_kernel<bf16>": ("entropy_partials_kernel<ec::bf16_t>", "entropy.hip", "largest"),
-    "gemm_skinny_kernel<bf16,lmhead>": ("gemm_skinny_kernel<ec::bf16_t, 2, false, 4, 8, true>", "gemm.hip", "all"),
+    "lmhead_packed_kernel<3>": ("lmhead_packed_kernel<3>", "gemm.hip", "all"),
 }
 
 
@@ -502,8 +502,9 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         "phase_roofline": phase_roofline,
         "roofline": {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic("gemm_skinny_kernel<bf16,lmhead>", "gemm.hip", 1),
-                     "kernel": "LM-head skinny GEMM on the packed weight (gemm_skinny_kernel<bf16, 2, false, 4, 8, true>)",
+                     "traffic": _traffic("lmhead_packed_kernel<3>", "gemm.hip", 1),
+                     "kernel": "LM head on the packed weight, three column tiles per workgroup "
+                               "(lmhead_packed_kernel<3>)",
                      "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)},
     }
     _log(f"step: {out['value']:.1f} steps/s, {out['ms_per_step'] * 1e3:.1f} us/step, "

@@ -127,7 +127,7 @@ int32_t check_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, 
       m->d_ffn % 32 != 0 || !head_dim_ok(m->dh) || m->Hq / m->Hkv > kMaxGroup ||
       c->block_len > kStepMaxRows || st->L > kSelectMaxL || m->L_cap > kSelectMaxL ||
       m->n_layers > 4096 || int64_t(m->Hq) * m->dh > (int64_t(1) << 20) ||
-      m->V > (1 << 30))
+      m->V > (1 << 30) || (!external && m->V % 32 != 0))   // the LM head's GEMM takes whole 32-column blocks
     return EC_E_UNSUPPORTED;
   if (!aligned16(ws) || !aligned16(m->tok_emb) || !aligned16(m->pos_emb) ||
       (!external && !aligned16(m->w_lm)) || !aligned16(st->logits) ||

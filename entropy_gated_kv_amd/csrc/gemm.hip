@@ -160,7 +160,7 @@ template <typename T, int NV = kNV> constexpr int skit() { return NV * 4 * (16 /
 // which streams its weights 3-4% faster with eight (512 contiguous bytes of
 // each of a wave's 16 rows per iteration, half the barriers per byte); at
 // four the smaller ring leaves registers for the larger row bounds.
-template <typename T, int MB, bool DUAL, int EPI, int NV, bool PK = false>
+template <typename T, int MB, bool DUAL, int EPI, int NV>
 __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem) {
   constexpr int VPL = 16 / int(sizeof(T));
   constexpr int KIT = skit<T, NV>();
@@ -172,12 +172,7 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
   const int nit = p.KS / KIT;                               // K splits evenly (host plan)
   const int col = tile * kSkinnyNT + wave * 16 + (lane & 15);
   const T* A = static_cast<const T*>(p.A);
-  // PK: W read from its fragment layout, where the 16 rows x 32 k that one
-  // load instruction of a wave takes are one contiguous 1 KB block in lane
-  // order, and a wave's blocks follow one another (8 KB per iteration)
-  const int grp = min(tile * (kSkinnyNT / 16) + wave, p.N / 16 - 1);
-  const T* Wp = PK ? static_cast<const T*>(p.Wpk) + (int64_t(grp) * (p.K / 32) + k0 / 32) * 64 * VPL + lane * VPL
-                   : static_cast<const T*>(p.W) + int64_t(min(col, p.N - 1)) * p.K + k0 + g * VPL;
+  const T* Wp = static_cast<const T*>(p.W) + int64_t(min(col, p.N - 1)) * p.K + k0 + g * VPL;
   const T* W2p = DUAL ? static_cast<const T*>(p.W2) + int64_t(min(col, p.N - 1)) * p.K + k0 + g * VPL
                       : nullptr;
 
@@ -215,7 +210,7 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
   auto w_load = [&](WBuf& dst, const T* src, int it) {
 #pragma unroll
     for (int v = 0; v < NV; ++v)
-      dst[v] = *reinterpret_cast<const u32x4*>(src + (PK ? (it * NV + v) * 64 * VPL : it * KIT + v * 4 * VPL));
+      dst[v] = *reinterpret_cast<const u32x4*>(src + it * KIT + v * 4 * VPL);
   };
 
   f32x4 acc[MB], acc2[DUAL ? MB : 1];
@@ -234,28 +229,12 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
     if constexpr (DUAL) w_load(nxt2, W2p, min(it + 2, last));
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      if constexpr (PK) {
-        // The LM head reads the MB activation fragments of a column block
-        // together, then multiplies: one LDS round trip per block instead of
-        // MB, so each iteration ends (and the next weight loads go out) sooner.
-        // Four more registers, still three waves per SIMD; same products in
-        // the same order.
-        u32x4 af[MB];
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb)
-          af[rb] = *reinterpret_cast<const u32x4*>(smem + (rb * 16 + (lane & 15)) * ROWB + (v * 4 + g) * 16);
-        __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);   // the MB LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);   // then the MB MFMAs
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) Mma16<T>::run(acc[rb], af[rb], cur[v]);
-      } else {
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(smem + (rb * 16 + (lane & 15)) * ROWB +
-                                                          (v * 4 + g) * 16);
-          Mma16<T>::run(acc[rb], a, cur[v]);
-          if constexpr (DUAL) Mma16<T>::run(acc2[rb], a, cur2[v]);
-        }
+      for (int rb = 0; rb < MB; ++rb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(smem + (rb * 16 + (lane & 15)) * ROWB +
+                                                        (v * 4 + g) * 16);
+        Mma16<T>::run(acc[rb], a, cur[v]);
+        if constexpr (DUAL) Mma16<T>::run(acc2[rb], a, cur2[v]);
       }
     }
     __syncthreads();                            // every wave is done with this stage
@@ -348,19 +327,208 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
   }
 }
 
+// The LM head on the packed weight (bf16, at most 32 candidate rows, K not
+// split).  A workgroup owns groups of TPW column tiles (64 columns each);
+// for every k-block it multiplies the one staged block of activations with
+// the weights of all TPW tiles, so each activation stage and its barriers
+// serve TPW tiles.  It walks its groups blockIdx.x, blockIdx.x + gridDim.x,
+// ... (a persistent grid when there are more groups than resident slots) as
+// one flat sequence of (group, k-block, tile) steps, with the weight ring
+// running on across group boundaries.  For each tile the products and their
+// order are those of the skinny kernel (k-blocks ascending, the same MFMA
+// chain), so the logits are the same bits.  A finished group's logits leave
+// through an LDS area of their own.
+constexpr int kLmNV = 2 * kNV;                        // 512 B of each weight row per k-block
+constexpr int kLmROWB = skit<bf16_t, kLmNV>() * 2 + 16;
+constexpr int kLmOP = kSkinnyNT * 2 + 16;             // staged logits row (bytes)
+constexpr size_t lm_lds(int tpw) { return size_t(2 * 16) * kLmROWB + size_t(tpw) * 2 * 16 * kLmOP; }
+template <int N> struct IC { static constexpr int value = N; };
+
+template <int TPW>
+__global__ __launch_bounds__(kThreads) void lmhead_packed_kernel(GP p) {
+  using T = bf16_t;
+  constexpr int MB = 2, NV = kLmNV, VPL = 8, KIT = skit<T, NV>(), ROWB = kLmROWB, OP = kLmOP;
+  constexpr int KB = KIT / 32;                          // 1 KB fragments per row group and k-block
+  static_assert(KB == NV, "one fragment per vector of a lane");
+  static_assert(TPW >= 1 && TPW <= 3, "tiles per group");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const lg = smem + MB * 16 * ROWB;               // logits staging, TPW tiles
+  const int n_rows = min(*p.n_rows, p.max_rows);
+  if (n_rows <= 0 || n_rows > MB * 16) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+  const int nit = p.K / KIT;                            // K is a multiple of KIT (host plan)
+  const int ntiles = (p.N + kSkinnyNT - 1) / kSkinnyNT;
+  const int ngroups = (ntiles + TPW - 1) / TPW;
+  const int G = int(gridDim.x);
+  const int nmine = (ngroups - int(blockIdx.x) + G - 1) / G;
+  if (nmine <= 0 || nit <= 0) return;
+  const int nsteps = nmine * nit * TPW;                 // this workgroup's (group, k-block, tile) steps
+  // tile j of the workgroup's group m; past the last tile, the last tile again
+  // (a short last group computes and stores that tile more than once, the
+  // same values each time)
+  auto tile_of = [&](int m, int j) { return min((int(blockIdx.x) + m * G) * TPW + j, ntiles - 1); };
+  // weights of k-block kb of a tile: the wave's 16-row group (clamped to the
+  // last group; columns past N are never stored), one 8 KB run
+  const T* const Wb = static_cast<const T*>(p.Wpk) + lane * VPL;
+  auto wsrc = [&](int tile, int kb) {
+    const int grp = min(tile * (kSkinnyNT / 16) + wave, p.N / 16 - 1);
+    return Wb + (int64_t(grp) * (p.K / 32) + kb * KB) * 64 * VPL;
+  };
+  typedef u32x4 WBuf[NV];
+  // prefetch cursor: group and k-block of the next weights loaded (which
+  // tile of the group is known at each step)
+  int pf_m = 0, pf_kb = 0;
+  auto w_load = [&](WBuf& dst, auto PJ) {
+    constexpr int j = decltype(PJ)::value;
+    const T* src = wsrc(tile_of(pf_m, j), pf_kb);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) dst[v] = *reinterpret_cast<const u32x4*>(src + v * 64 * VPL);
+    if constexpr (j == TPW - 1) {
+      if (++pf_kb == nit) {
+        pf_kb = 0;
+        ++pf_m;
+      }
+    }
+  };
+  // activations: the candidate rows (gathered), KIT k per k-block
+  constexpr int AV = MB * 16 * (KIT / VPL);
+  constexpr int APT = AV / kThreads;
+  static_assert(AV % kThreads == 0, "A stage must split evenly over the workgroup");
+  const T* A = static_cast<const T*>(p.A);
+  const T* arow[APT];
+#pragma unroll
+  for (int i = 0; i < APT; ++i) {
+    const int v = tid + i * kThreads;
+    const int r = v / (KIT / VPL), c = v % (KIT / VPL);
+    const int ar = (r < n_rows) ? ((p.a_idx != nullptr) ? p.a_idx[r] : r) : 0;
+    arow[i] = A + int64_t(ar) * p.lda + c * VPL;
+  }
+  u32x4 areg[APT];
+  auto a_load = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < APT; ++i) areg[i] = *reinterpret_cast<const u32x4*>(arow[i] + kb * KIT);
+  };
+  auto a_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < APT; ++i) {
+      const int v = tid + i * kThreads;
+      const int r = v / (KIT / VPL), c = v % (KIT / VPL);
+      *reinterpret_cast<u32x4*>(smem + r * ROWB + c * 16) = areg[i];
+    }
+  };
+  f32x4 acc[TPW][MB];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) acc[j][rb] = f32x4{};
+  bf16_t* const C = static_cast<bf16_t*>(p.C);
+  // logits of a finished group (acc x scale, rounded once): each wave rounds
+  // its 16 columns of every tile into the staging area; then each thread
+  // stores 16-byte chunks of rows, a row of a tile being one 128-byte line
+  // (the host launches this kernel only for 16-byte aligned rows).  The area
+  // is written again only after a whole group of barriers.
+  auto epilogue = [&](int m) {
+#pragma unroll
+    for (int j = 0; j < TPW; ++j)
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rb * 16 + 4 * g + e;
+          const float sc = (r < n_rows && p.scale != nullptr) ? p.scale[p.scale_pos[r]] : 1.0f;
+          *reinterpret_cast<uint16_t*>(lg + (j * MB * 16 + r) * OP + (wave * 16 + (lane & 15)) * 2) =
+              f32_to_bf16(acc[j][rb][e] * sc);
+          acc[j][rb][e] = 0.f;
+        }
+    __syncthreads();
+#pragma unroll
+    for (int k = tid; k < TPW * MB * 16 * (kSkinnyNT / 8); k += kThreads) {
+      const int j = k / (MB * 16 * (kSkinnyNT / 8)), rk = k % (MB * 16 * (kSkinnyNT / 8));
+      const int r = rk / (kSkinnyNT / 8), c0 = tile_of(m, j) * kSkinnyNT;
+      const int n = c0 + (rk % (kSkinnyNT / 8)) * 8;
+      if (r >= n_rows || n >= p.N) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lg + (j * MB * 16 + r) * OP + (n - c0) * 2);
+      if (n + 8 <= p.N) {
+        *reinterpret_cast<u32x4*>(C + int64_t(r) * p.ldc + n) = v;
+      } else {                                          // ragged last chunk of the row
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < p.N) C[int64_t(r) * p.ldc + n + e].bits = uint16_t(v[e >> 1] >> ((e & 1) * 16));
+      }
+    }
+  };
+  int cu_kb = 0, cu_m = 0;                              // k-block and group of the current step
+  WBuf r0, r1, r2;
+  // one step (ring slot S, tile J of the group): prefetch the weights two
+  // steps ahead; multiply the staged activations with this tile's weights.
+  // After the group's last tile, stage the next k-block's activations, and
+  // after the last k-block, the group's logits.
+  auto step = [&](auto S, auto J) {
+    constexpr int s = decltype(S)::value, j = decltype(J)::value;
+    WBuf& cur = s == 0 ? r0 : s == 1 ? r1 : r2;
+    WBuf& nxt = s == 0 ? r2 : s == 1 ? r0 : r1;
+    if constexpr (j == 0) a_load(cu_kb + 1 == nit ? 0 : cu_kb + 1);   // before the W prefetch
+    w_load(nxt, IC<(j + 2) % TPW>{});
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      // the MB activation fragments of a column block read together, then
+      // multiplied: one LDS round trip per block
+      u32x4 af[MB];
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb)
+        af[rb] = *reinterpret_cast<const u32x4*>(smem + (rb * 16 + (lane & 15)) * ROWB + (v * 4 + g) * 16);
+      __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);   // the MB LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, MB, 0);   // then the MB MFMAs
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) Mma16<T>::run(acc[j][rb], af[rb], cur[v]);
+    }
+    if constexpr (j == TPW - 1) {
+      __syncthreads();                                  // every wave is done with this stage
+      a_store();
+      __syncthreads();
+      if (++cu_kb == nit) {
+        epilogue(cu_m);
+        cu_kb = 0;
+        ++cu_m;
+      }
+    }
+  };
+  w_load(r0, IC<0>{});
+  w_load(r1, IC<1 % TPW>{});
+  a_load(0);
+  a_store();
+  __syncthreads();
+  int u = 0;
+  if constexpr (TPW == 2) {
+    for (; u + 6 <= nsteps; u += 6) {
+      step(IC<0>{}, IC<0>{}); step(IC<1>{}, IC<1>{}); step(IC<2>{}, IC<0>{});
+      step(IC<0>{}, IC<1>{}); step(IC<1>{}, IC<0>{}); step(IC<2>{}, IC<1>{});
+    }
+    if (u < nsteps) { step(IC<0>{}, IC<0>{}); step(IC<1>{}, IC<1>{}); }
+    if (u + 2 < nsteps) { step(IC<2>{}, IC<0>{}); step(IC<0>{}, IC<1>{}); }
+  } else {
+    for (; u + 3 <= nsteps; u += 3) {
+      step(IC<0>{}, IC<0 % TPW>{}); step(IC<1>{}, IC<1 % TPW>{}); step(IC<2>{}, IC<2 % TPW>{});
+    }
+    if constexpr (TPW == 1) {                           // with three tiles, nsteps is a multiple of 3
+      if (u < nsteps) step(IC<0>{}, IC<0>{});
+      if (u + 1 < nsteps) step(IC<1>{}, IC<0>{});
+    }
+  }
+}
+
 // MBX: largest count of 16-row blocks this launch can see (2, 4, 6 or 8, from
 // the host's bound on the row count); the kernel picks the body for the device
 // row count.  Each instance holds only the bodies up to MBX, so its register
 // footprint (and with it the waves per SIMD) follows the bound: at 96 rows the
 // six-block instance keeps three waves per SIMD where the eight-block one has two.
-template <typename T, int MBX, bool DUAL, int EPI, int NV = kNV, bool PK = false>
+template <typename T, int MBX, bool DUAL, int EPI, int NV = kNV>
 __global__ __launch_bounds__(kThreads) void gemm_skinny_kernel(GP p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int n_rows = min(*p.n_rows, p.max_rows);
   if (n_rows <= 0 || n_rows > kSkinnyMaxRows) return;
   const int mb = (n_rows + 15) / 16;
-  static_assert(!PK || MBX == 2, "the fragment layout serves the LM-head instance");
-  if (MBX == 2 || mb <= 2) skinny_body<T, 2, DUAL, EPI, NV, PK>(p, n_rows, smem);
+  if (MBX == 2 || mb <= 2) skinny_body<T, 2, DUAL, EPI, NV>(p, n_rows, smem);
   else if constexpr (MBX >= 4) {
     if (MBX == 4 || mb <= 4) skinny_body<T, 4, DUAL, EPI, NV>(p, n_rows, smem);
     else if constexpr (MBX >= 6) {
@@ -897,9 +1065,9 @@ Plan plan_skinny(const GemmArgs& a) {
 
 size_t up256(size_t b) { return (b + 255) & ~size_t(255); }
 
-template <typename T, int MBX, bool DUAL, int EPI, int NV = kNV, bool PK = false>
+template <typename T, int MBX, bool DUAL, int EPI, int NV = kNV>
 void go_skinny(dim3 g, size_t lds, hipStream_t s, const GP& p) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, MBX, DUAL, EPI, NV, PK>), g, dim3(kThreads), lds, s, p);
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, MBX, DUAL, EPI, NV>), g, dim3(kThreads), lds, s, p);
 }
 
 template <typename T, int EPI, bool DUAL = false>
@@ -908,6 +1076,41 @@ void skinny_by_shape(const Plan& pl, dim3 g, size_t lds, hipStream_t s, const GP
   else if (pl.MBX == 4) go_skinny<T, 4, DUAL, EPI>(g, lds, s, p);
   else if (pl.MBX == 6) go_skinny<T, 6, DUAL, EPI>(g, lds, s, p);
   else go_skinny<T, 8, DUAL, EPI>(g, lds, s, p);
+}
+
+// The packed LM head over `tiles` column tiles: groups of TPW = ceil(tiles /
+// resident slots) tiles, one workgroup per group, when that is at most three;
+// otherwise single tiles on a persistent grid of one workgroup per slot.
+// Slots per CU come from the occupancy query (once per instance and process).
+template <int TPW>
+int lm_slots_per_cu() {
+  static const int n = [] {
+    int nb = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, lmhead_packed_kernel<TPW>, kThreads, lm_lds(TPW)) ==
+                   hipSuccess ? nb : 0;
+  }();
+  return n;
+}
+
+template <int TPW>
+void go_lmhead(unsigned grid, hipStream_t s, const GP& p) {
+  hipLaunchKernelGGL(lmhead_packed_kernel<TPW>, dim3(grid), dim3(kThreads), lm_lds(TPW), s, p);
+}
+
+void launch_lmhead(unsigned tiles, hipStream_t s, const GP& p) {
+  const unsigned cus = unsigned(device_cu_count());
+  const unsigned slots3 = unsigned(lm_slots_per_cu<3>()) * cus;
+  const unsigned per = slots3 > 0 ? (tiles + slots3 - 1) / slots3 : 0;
+  if (per == 3 || per == 2) {
+    const unsigned slots = per == 3 ? slots3 : unsigned(lm_slots_per_cu<2>()) * cus;
+    if ((tiles + per - 1) / per <= slots) {
+      if (per == 3) go_lmhead<3>((tiles + 2) / 3, s, p);
+      else go_lmhead<2>((tiles + 1) / 2, s, p);
+      return;
+    }
+  }
+  const unsigned slots1 = unsigned(lm_slots_per_cu<1>()) * cus;
+  go_lmhead<1>((slots1 > 0 && slots1 < tiles) ? slots1 : tiles, s, p);
 }
 
 template <typename T>
@@ -919,8 +1122,9 @@ hipError_t dispatch_skinny(Epi epi, const Plan& pl, dim3 g, size_t lds, hipStrea
     case Epi::kSwiGLU: skinny_by_shape<T, 3, true>(pl, g, lds, s, p); break;
     case Epi::kLogits:
       if constexpr (sizeof(T) == 2) {
-        if (pl.NV == 2 * kNV && p.Wpk != nullptr) {
-          go_skinny<T, 2, false, 4, 2 * kNV, true>(g, lds, s, p);
+        if (pl.NV == 2 * kNV && p.Wpk != nullptr && (p.ldc & 7) == 0 &&
+            (reinterpret_cast<uintptr_t>(p.C) & 15) == 0) {
+          launch_lmhead(g.x, s, p);
           break;
         }
       }

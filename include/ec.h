@@ -264,8 +264,8 @@ int32_t ec_bidir_attention(const void* q, const int32_t* n_rows, int32_t max_row
  * ws (ec_step_workspace_bytes(model, max_block) bytes) is scratch: every
  * region is written before it is read, so no initial contents are required.
  * Norms and FFN are present iff d_ffn > 0.  d, Hq*dh and d_ffn must be
- * multiples of 128 (bf16) or 64 (fp32) (EC_E_UNSUPPORTED otherwise); block_len
- * is at most 1024.  The block (block_start,
+ * multiples of 128 (bf16) or 64 (fp32), and V of 32 when w_lm is given
+ * (EC_E_UNSUPPORTED otherwise); block_len is at most 1024.  The block (block_start,
  * block_len) and n_unmask are host values: the schedule is fixed on the host.
  * ------------------------------------------------------------------------ */
 typedef struct ec_layer {
@@ -289,8 +289,8 @@ typedef struct ec_model {
   const float* logit_scale;   /* [L_cap] device float32, or NULL (= 1)     */
   /* Optional: w_lm repacked by ec_pack_lm_head, or NULL.  When set (bf16,
    * V % 16 == 0, 16-byte aligned), the LM head of steps whose block holds at
-   * most 32 positions reads it instead of w_lm (same arithmetic, same bits);
-   * w_lm must still be given. */
+   * most 32 positions reads it instead of w_lm if V > 32704 and d % 256 == 0
+   * (same arithmetic, same bits); w_lm must still be given. */
   const void* w_lm_packed;
 } ec_model;
 

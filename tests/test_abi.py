@@ -158,7 +158,9 @@ def test_step_rejects_misaligned_weights(lib):
     # the packed LM head: bf16, V % 16 == 0, aligned, and only with an LM head
     assert call(w_lm_packed=FAKE) == -4
     assert call(w_lm_packed=ODD) == -5
-    assert call(w_lm_packed=FAKE, V=1032) == -2
+    assert call(w_lm_packed=FAKE, V=1040) == -7                    # V % 32 != 0: no LM head GEMM for it
+    assert call(V=1040) == -7
+    assert call(V=1040, w_lm=None) == -4                           # no LM head: any V
     assert call(w_lm_packed=FAKE, dtype=0) == -3
     assert call(w_lm_packed=FAKE, w_lm=None) == -1
 

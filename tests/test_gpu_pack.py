@@ -6,7 +6,12 @@
   of a block being its 16-byte chunk 16 g + n.
 * Steps whose LM head reads the packed copy give the same bits as steps that
   read w_lm (logits, entropies, decisions, tokens), on the LLaDA-shaped layer
-  at full size (V = 126464, where the packed LM-head kernel runs).
+  at full size (V = 126464), and on one-layer models whose vocabulary sizes
+  reach each launch shape of the packed LM head on a 256-CU part with three
+  resident workgroups per CU: single tiles one per workgroup, pairs, triples
+  (with a short last group that repeats a tile) and single tiles on a
+  persistent grid; ragged last tiles (V % 64 = 32) and d = 256, 512, 768
+  (one, two, three k-blocks).
 """
 import numpy as np
 import pytest
@@ -37,8 +42,7 @@ def test_packed_layout(V, d):
     np.testing.assert_array_equal(out.view(torch.int16).cpu().numpy().reshape(-1), want)
 
 
-def test_packed_lm_head_steps_are_bit_identical():
-    cfg = C.LLADA_LAYER
+def steps_bit_identical(cfg):
     w = G.model_weights(cfg)
     toks, masked = G.initial_sequence(cfg)
     packed = DeviceModel(cfg.model, cfg.dtype, cfg.L, w, pack_lm_head=True)
@@ -56,3 +60,19 @@ def test_packed_lm_head_steps_are_bit_identical():
         for f in ("row_entropy", "row_top1", "row_argmax", "tokens", "is_masked", "full_flag",
                   "e_max", "chosen", "n_chosen"):
             assert torch.equal(getattr(a, f), getattr(b, f)), (i, f)
+
+
+def test_packed_lm_head_steps_are_bit_identical():
+    steps_bit_identical(C.LLADA_LAYER)
+
+
+# (V, d): column tiles of 64 and the launch shape they get
+@pytest.mark.parametrize("V,d", [(40032, 256),     # 626 tiles: one per workgroup
+                                 (65568, 512),     # 1025 tiles: pairs, the last pair repeats a tile
+                                 (128032, 768),    # 2001 tiles: triples
+                                 (160032, 256)],   # 2501 tiles: single tiles, persistent grid
+                         ids=["single", "pairs", "triples", "persistent"])
+def test_packed_lm_head_launch_shapes_are_bit_identical(V, d):
+    heads = d // 128
+    steps_bit_identical(C.scaled(C.LLADA_LAYER, model_vocab=V, model_d=d, model_n_q_heads=heads,
+                                 model_n_kv_heads=heads))

@@ -146,6 +146,13 @@ void step_cases() {
     s.m.Hq = INT32_MAX; s.m.Hkv = 1; s.m.dh = 128;     // Hq * dh must not wrap
     EXPECT(ec::check_step(&s.m, &s.st, &s.c, A) == EC_E_UNSUPPORTED);
   }
+  {
+    StepCase s(1);
+    s.m.V = 2064;                                      // not whole 32-column blocks
+    EXPECT(ec::check_step(&s.m, &s.st, &s.c, A) == EC_E_UNSUPPORTED);
+    s.m.w_lm = nullptr;                                // no LM head: the caller decodes
+    EXPECT(ec::check_step(&s.m, &s.st, &s.c, A) == EC_OK);
+  }
 }
 
 void fuzz(int rounds) {
