@@ -171,7 +171,7 @@ def summarize_counters(dirs) -> str:
         groups[key].append((us, c))
     rows = []
     for key, ds in groups.items():
-        if not key[0].startswith(("attn", "gemm", "entropy", "select", "rmsnorm", "value_drift")):
+        if not key[0].startswith(("attn", "gemm", "lmhead", "entropy", "select", "rmsnorm", "value_drift")):
             continue
         big = max(c.get("SQ_WAVE_CYCLES", c.get("SQ_BUSY_CYCLES", 0.0)) for _, c in ds)
         act = [(us, c) for us, c in ds

@@ -66,9 +66,17 @@ def test_counter_summary_scales_flops_and_leaves_out_exited_dispatches(tmp_path)
                                                   "GRBM_GUI_ACTIVE": 8 * 300 * 1000 * 2.0})
          + counter_rows(3, k, 256 * 256, 3.0, {"SQ_INSTS_VALU_MFMA_MOPS_BF16": 0.0,
                                                 "SQ_VALU_MFMA_BUSY_CYCLES": 0.0, "GRBM_GUI_ACTIVE": 0.0}))
+    lm = "void ec::(anonymous namespace)::lmhead_packed_kernel<3>(ec::(anonymous namespace)::GP)"
+    a += counter_rows(4, lm, 659 * 256, 190.0, {"SQ_INSTS_VALU_MFMA_MOPS_BF16": 6.5e7,
+                                               "SQ_VALU_MFMA_BUSY_CYCLES": 0.07 * 190 * 2400 * 1024,
+                                               "GRBM_GUI_ACTIVE": 8 * 190 * 1000 * 2.4})
+    a += counter_rows(5, "void at::native::fill_kernel(int)", 64, 2.0, {"SQ_INSTS_VALU_MFMA_MOPS_BF16": 0.0})
     write_csv(tmp_path / "a" / "x_counter_collection.csv", a)
     table = bench.summarize_counters([str(tmp_path / "a")]).splitlines()
-    assert len(table) == 3
+    assert len(table) == 4                                       # torch's own kernels are left out
+    lm_cells = [c.strip() for c in table[2].split("|")[1:-1]]   # most flops first
+    assert lm_cells[0] == "`lmhead_packed_kernel<3>`" and lm_cells[1] == "659" and lm_cells[2] == "1 / 1"
+    table = [table[0], table[1], table[3]]
     cells = [c.strip() for c in table[2].split("|")[1:-1]]
     assert cells[0] == "`attn_bf16_kernel<128>`" and cells[1] == "256"
     assert cells[2] == "2 / 3"                                   # dispatches with work / all
