@@ -320,7 +320,11 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
     w = G.model_weights(cfg)
     toks, masked = G.initial_sequence(cfg)
     dm = DeviceModel(cfg.model, cfg.dtype, cfg.L, w)
-    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len)
+    # No logits buffer: the packed LM head writes each candidate's softmax
+    # statistics instead of its logits, and the step decides from those (the
+    # with-logits rate is reported below)
+    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len,
+                        keep_logits=False)
     sched = C.unmask_schedule(cfg)
     init = (ds.tokens.clone(), ds.is_masked.clone())
     stream = torch.cuda.current_stream()
@@ -378,7 +382,7 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
     n_seq = max(1, min(steps, len(sched)))
     phases = [j * len(sched) // n_seq for j in range(n_seq)]
     seqs = [DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len,
-                           ws=ds.ws) for _ in range(n_seq)]
+                           ws=ds.ws, keep_logits=False) for _ in range(n_seq)]
     sched_flags = torch.zeros(len(sched), dtype=torch.int32, device="cuda")
 
     def stage():
@@ -445,8 +449,10 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
             if (fl == want).any():
                 by_mode[mode][name] = float(t[fl == want].mean())
     # LM-head algorithmic bytes per launch: W_lm read once, the candidates'
-    # activations read and their logits written (mean candidate count over the
-    # launches the events timed: the block's still-masked positions at each step)
+    # activations read and their softmax statistics written, 16 bytes per row
+    # and group of three column tiles (the launch plan at this V on 256 CUs);
+    # m = mean candidate count over the launches the events timed (the
+    # block's still-masked positions at each step)
     d, V = cfg.model.d, cfg.model.vocab
     cand = []
     left, cur = cfg.block_len, None
@@ -456,7 +462,7 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         cand.append(left)
         left -= nn
     m = float(np.mean([cand[idx[i]] for i in ev_steps]))
-    lm_bytes = int(V * d * 2 + m * d * 2 + m * V * 2)
+    lm_bytes = int(V * d * 2 + m * d * 2 + m * ((V + 191) // 192) * 16)
     lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
     decide_ms = phase_ms["select"] + phase_ms["entropy"] + phase_ms["decide"]
     # each phase against its roofline: max(bytes / HBM peak, flops / bf16 MFMA peak),
@@ -503,8 +509,8 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         "roofline": {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
                      "traffic": _traffic("lmhead_packed_kernel<3>", "gemm.hip", 1),
-                     "kernel": "LM head on the packed weight, three column tiles per workgroup "
-                               "(lmhead_packed_kernel<3>)",
+                     "kernel": "LM head on the packed weight, three column tiles per workgroup, "
+                               "softmax statistics in place of logits (lmhead_packed_kernel<3>)",
                      "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)},
     }
     _log(f"step: {out['value']:.1f} steps/s, {out['ms_per_step'] * 1e3:.1f} us/step, "
@@ -545,6 +551,36 @@ def step_leg(steps: int, warmup: int, cpu_baseline: bool) -> dict:
         kab[str(k)] = rec
     out["k_ablation_tau_1"] = kab
     _log(f"k ablation (tau 1.0): {kab}")
+
+    # the same tau = 1 generation when the step also returns the candidates'
+    # logits (a logits buffer: the LM head writes them and the entropy pass
+    # reads them back), and that LM head's time from events on every step of
+    # a second run
+    dl = DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len, ws=ds.ws)
+    fl_l = torch.zeros(len(sched), dtype=torch.int32, device="cuda")
+    def gen_logits(events):
+        dl.tokens.copy_(init[0])
+        dl.is_masked.copy_(init[1])
+        dl.history_len.zero_()
+        dl.full_flag.fill_(1)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i, (bs, bl, nn) in enumerate(sched):
+            fl_l[i].copy_(dl.full_flag[0])
+            dl.step(tau, cfg.k, bs, bl, nn, phase_events=None if events is None else events[i])
+        torch.cuda.synchronize()
+        return time.perf_counter() - t1
+    dt_l = gen_logits(None)
+    lm_ev = [event_set(True) for _ in sched]
+    gen_logits(lm_ev)
+    lm_l_us = float(np.mean([e[2 * LM].elapsed_time(e[2 * LM + 1]) for e in lm_ev])) * 1e3
+    out["with_logits"] = {"steps_per_s": round(len(sched) / dt_l, 2),
+                          "partial_fraction": round(float(1.0 - fl_l.float().mean().item()), 3),
+                          "lmhead_us": round(lm_l_us, 2),
+                          "note": "tau = 1 generation with a logits buffer; lmhead_us from events on "
+                                  "every step of a second run"}
+    _log(f"with logits: {out['with_logits']}")
+    del dl
 
     # sliding-window decoding: the same unmask counts, the block being the 32
     # positions from the first masked one (block_start = -1)
@@ -821,7 +857,8 @@ def stack_leg(n_steps: int = 66) -> dict:
     del w
     _log(f"{cfg.name}: weights in HBM after {time.perf_counter() - t_gen:.1f} s")
     toks, masked = G.initial_sequence(cfg)
-    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len)
+    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len,
+                        keep_logits=False)   # as in the step leg: statistics in place of logits
     sched = C.unmask_schedule(cfg)[:n_steps]
     init = (ds.tokens.clone(), ds.is_masked.clone())
 
@@ -970,14 +1007,16 @@ def profile_mfma_mode(workload: str) -> int:
         w = G.model_weights(sc)
         toks, masked = G.initial_sequence(sc)
         dm = DeviceModel(sc.model, sc.dtype, sc.L, w)
-        ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len)
+        ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len,
+                            keep_logits=False)
         for bs, bl, nn in C.unmask_schedule(sc)[:22]:
             ds.step(1.0, sc.k, bs, bl, nn)
     elif workload == "stack":
         sc = C.LLADA_STACK
         dm = DeviceModel(sc.model, sc.dtype, sc.L, G.model_weights_streamed(sc))
         toks, masked = G.initial_sequence(sc)
-        ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len)
+        ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len,
+                            keep_logits=False)
         for bs, bl, nn in C.unmask_schedule(sc)[:3]:
             ds.step(1.0, sc.k, bs, bl, nn, mode=L_mode(ds))
     else:
@@ -997,7 +1036,8 @@ def profile_mode() -> int:
     """A short, fixed sequence for hardware-counter runs (rocprofv3 --pmc):
     a 1 GiB device copy (the calibration of FETCH_SIZE / WRITE_SIZE), five
     entropy passes over the 4096 x 126464 logits, and one block (22 steps) of
-    the LLaDA-shaped EntropyCache loop."""
+    the LLaDA-shaped EntropyCache loop as the benchmark runs it (no logits
+    buffer)."""
     import torch
 
     from entropy_gated_kv_amd import lib as L
@@ -1030,7 +1070,8 @@ def profile_mode() -> int:
     w = G.model_weights(sc)
     toks, masked = G.initial_sequence(sc)
     dm = DeviceModel(sc.model, sc.dtype, sc.L, w)
-    ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len)
+    ds = DeviceSequence(dm, toks, masked, history_cap=sc.gen_len, max_block=sc.block_len,
+                        keep_logits=False)
     for bs, bl, nn in C.unmask_schedule(sc)[:22]:
         ds.step(1.0, sc.k, bs, bl, nn)
     torch.cuda.synchronize()
@@ -1117,6 +1158,8 @@ def main() -> int:
             "kv_drift_tau_1": res.get("kv_drift_tau_1"),
             "sliding_window_32": res.get("sliding_window_32"),
             "block_diffusion_32": res.get("block_diffusion_32"),
+            "lm_head_output": "softmax statistics per group of column tiles (no logits buffer)",
+            "with_logits": res.get("with_logits"),
         }
         if "cpu_baseline" in res:
             line["cpu_baseline"] = res["cpu_baseline"]

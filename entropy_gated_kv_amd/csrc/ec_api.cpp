@@ -206,7 +206,14 @@ StepLayout step_layout(const ec_model* m, int32_t max_block, void* ws) {
   }
   if (m->w_lm) need(ec::Epi::kLogits, max_block, m->V, m->d);
   s.gemm_ws = c.take<void>(gws);
-  s.ent_ws = c.take<void>(ec::entropy_ws_bytes(max_block, m->V, m->dtype));
+  // entropy partials: the entropy pass's segments, or the packed LM head's
+  // per-(row, tile group) statistics (one region serves both)
+  size_t ent = ec::entropy_ws_bytes(max_block, m->V, m->dtype);
+  if (m->w_lm && m->w_lm_packed && max_block <= ec::kLmStatRows) {
+    const size_t lm = size_t(max_block) * size_t(ec::lmhead_max_stat_groups(m->V)) * sizeof(ec::EntropyPartial);
+    if (lm > ent) ent = lm;
+  }
+  s.ent_ws = c.take<void>(ent);
   s.drift_ws = c.take<void>(ec::value_drift_ws_bytes(m->dtype, m->Hkv * m->dh, m->L_cap));
   s.cand_pos = c.take<int32_t>(size_t(max_block) * 4);
   s.cand_idx = c.take<int32_t>(size_t(max_block) * 4);
@@ -372,17 +379,35 @@ int32_t ec_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, voi
   gl.n_rows_dev = s.n_cand; gl.max_rows = max_block; gl.W = m->w_lm; gl.N = m->V; gl.K = m->d;
   gl.C = st->logits; gl.ldc = m->V; gl.scale = m->logit_scale; gl.scale_pos = s.cand_pos;
   gl.W_packed = m->w_lm_packed;
+  // Without a logits buffer the packed LM head writes each row's softmax
+  // statistics instead of its logits (the argument checks admit that only
+  // where the packed kernel runs)
+  int stat_groups = 0;
+  if (st->logits == nullptr) {
+    gl.stats = static_cast<ec::EntropyPartial*>(s.ent_ws);
+    gl.stats_groups = &stat_groups;
+  }
   EC_TRY(ec::launch_gemm_rows(gl, s.gemm_ws, stream));
   EC_TRY(tm.end(EC_PHASE_LMHEAD));
+  if (st->logits == nullptr && stat_groups == 0) return EC_E_LAUNCH;   // not reached after the checks
 
   // The entropy phase now includes the unmask choice and the decision, which
   // run in the same kernel as the per-row fold (the decide phase is empty).
+  // From the LM head's statistics, or the entropy pass over the logits.
   EC_TRY(tm.begin(EC_PHASE_ENTROPY));
-  EC_TRY(ec::launch_entropy_step(st->logits, dt, max_block, s.n_cand, m->V, m->V,
-                                 st->row_entropy, st->row_argmax, st->row_top1, s.cand_pos,
-                                 c->n_unmask, c->tau, st->chosen, st->n_chosen, st->tokens,
-                                 st->is_masked, st->history, st->history_len, st->history_cap,
-                                 st->e_max, st->full_flag, s.ent_ws, stream));
+  if (stat_groups > 0)
+    EC_TRY(ec::launch_entropy_step_fused(static_cast<const ec::EntropyPartial*>(s.ent_ws), stat_groups,
+                                         max_block, s.n_cand, st->row_entropy, st->row_argmax,
+                                         st->row_top1, s.cand_pos, c->n_unmask, c->tau, st->chosen,
+                                         st->n_chosen, st->tokens, st->is_masked, st->history,
+                                         st->history_len, st->history_cap, st->e_max, st->full_flag,
+                                         stream));
+  else
+    EC_TRY(ec::launch_entropy_step(st->logits, dt, max_block, s.n_cand, m->V, m->V,
+                                   st->row_entropy, st->row_argmax, st->row_top1, s.cand_pos,
+                                   c->n_unmask, c->tau, st->chosen, st->n_chosen, st->tokens,
+                                   st->is_masked, st->history, st->history_len, st->history_cap,
+                                   st->e_max, st->full_flag, s.ent_ws, stream));
   EC_TRY(tm.end(EC_PHASE_ENTROPY));
   EC_TRY(tm.begin(EC_PHASE_DECIDE));
   EC_TRY(tm.end(EC_PHASE_DECIDE));

@@ -32,6 +32,15 @@ int device_cu_count();
 // over all max_rows rows (n_rows_dev NULL); nothing else is written.
 // Then *flag = (E > tau) || isnan(E).
 int32_t step_max_rows();
+// The same decode and decision from partials the packed LM head wrote in its
+// epilogue (GemmArgs::stats): P per row, row r's at part[r * P ...], at most
+// kLmStatRows rows; the logits are not read.
+hipError_t launch_entropy_step_fused(const EntropyPartial* part, int32_t P, int32_t max_rows,
+                                     const int32_t* n_rows_dev, float* H, int32_t* argmax, float* p1,
+                                     const int32_t* cand_pos, int32_t n_unmask, float tau,
+                                     int32_t* chosen, int32_t* n_chosen, int32_t* tokens,
+                                     uint8_t* is_masked, int32_t* history, int32_t* history_len,
+                                     int32_t history_cap, float* e_max, int32_t* flag, hipStream_t s);
 hipError_t launch_entropy_step(const void* logits, int dtype, int32_t max_rows,
                                const int32_t* n_rows_dev, int64_t V, int64_t stride, float* H,
                                int32_t* argmax, float* p1, const int32_t* cand_pos,
@@ -100,7 +109,7 @@ struct GemmArgs {
   const void* W = nullptr;
   const void* W2 = nullptr;
   // kLogits, bf16: W in the fragment layout (launch_pack_fragments), or null;
-  // the skinny LM-head kernel then reads it instead of W
+  // the packed LM-head kernel then reads it instead of W
   const void* W_packed = nullptr;
   int N = 0, K = 0;
   void* C = nullptr;
@@ -114,13 +123,22 @@ struct GemmArgs {
   // kLogits
   const float* scale = nullptr;
   const int32_t* scale_pos = nullptr;
+  // kLogits, optional: where the packed LM-head kernel may also write each
+  // row's softmax statistics, one partial per group of column tiles in column
+  // order (row r's at stats[r * groups ...]; at most kLmStatRows rows times
+  // lmhead_max_stat_groups(N) partials).  The launcher sets *stats_groups (a
+  // host int) to the groups per row when it did, else to 0.
+  EntropyPartial* stats = nullptr;
+  int* stats_groups = nullptr;
 };
+// The most partials per row the packed LM head writes for N columns.
+int lmhead_max_stat_groups(int N);
 size_t gemm_ws_bytes(const GemmArgs& a);
 // Reduction dimensions (d, Hq*dh, d_ffn) must be multiples of this (128 bf16, 64 fp32).
 int gemm_k_multiple(int dtype);
 hipError_t launch_gemm_rows(const GemmArgs& a, void* ws, hipStream_t s);
 // Repack a bf16 [N, K] weight (N % 16 == 0, K % 32 == 0) into the fragment
-// layout read by the skinny LM-head kernel; out holds N * K elements.
+// layout read by the packed LM-head kernel; out holds N * K elements.
 hipError_t launch_pack_fragments(const void* W, int64_t N, int64_t K, void* out, hipStream_t s);
 
 // ---- KV drift of a full step (diagnostic) ------------------------------------------

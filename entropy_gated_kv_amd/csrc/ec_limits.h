@@ -20,5 +20,11 @@ inline int k_multiple(int32_t dtype) { return dtype == 1 ? kKMultipleBf16 : kKMu
 // Supported head dimensions and query heads per KV head.
 inline bool head_dim_ok(int32_t dh) { return dh == 32 || dh == 64 || dh == 128; }
 constexpr int kMaxGroup = 16;
+// The packed LM-head kernel runs for at most kLmStatRows rows, at least
+// kLmMinTiles column tiles of 64 and d a multiple of its k-block; only that
+// kernel can write a step's softmax statistics in place of its logits.
+constexpr int32_t kLmStatRows = 32;
+constexpr int32_t kLmMinTiles = 512;
+constexpr int32_t kLmKBlock = 256;
 
 }  // namespace ec

@@ -107,8 +107,13 @@ int32_t check_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, 
     if (m->d_ffn && (!ly.norm_attn || !ly.norm_ffn || !ly.w_gate || !ly.w_up || !ly.w_down))
       return EC_E_NULL;
   }
+  // Without a logits buffer the step folds the softmax statistics that the
+  // packed LM head writes in place of its logits: a model without LM head
+  // (whose caller supplies logits) or without the packed copy needs one.
+  const bool no_logits = (st->logits == nullptr);
+  if (no_logits && (external || !m->w_lm_packed)) return EC_E_NULL;
   if (!st->tokens || !st->is_masked || !st->history || !st->history_len || !st->full_flag ||
-      !st->k_cache || !st->v_cache || !st->rows || !st->n_rows || !st->logits ||
+      !st->k_cache || !st->v_cache || !st->rows || !st->n_rows ||
       !st->row_entropy || !st->row_argmax || !st->row_top1 || !st->chosen || !st->n_chosen ||
       !st->e_max)
     return EC_E_NULL;
@@ -127,10 +132,12 @@ int32_t check_step(const ec_model* m, const ec_state* st, const ec_step_cfg* c, 
       m->d_ffn % 32 != 0 || !head_dim_ok(m->dh) || m->Hq / m->Hkv > kMaxGroup ||
       c->block_len > kStepMaxRows || st->L > kSelectMaxL || m->L_cap > kSelectMaxL ||
       m->n_layers > 4096 || int64_t(m->Hq) * m->dh > (int64_t(1) << 20) ||
-      m->V > (1 << 30) || (!external && m->V % 32 != 0))   // the LM head's GEMM takes whole 32-column blocks
+      m->V > (1 << 30) || (!external && m->V % 32 != 0) ||   // the LM head's GEMM takes whole 32-column blocks
+      (no_logits && (c->block_len > kLmStatRows || (int64_t(m->V) + 63) / 64 < kLmMinTiles ||
+                     m->d % kLmKBlock != 0)))                // where the packed kernel does not run
     return EC_E_UNSUPPORTED;
   if (!aligned16(ws) || !aligned16(m->tok_emb) || !aligned16(m->pos_emb) ||
-      (!external && !aligned16(m->w_lm)) || !aligned16(st->logits) ||
+      (!external && !aligned16(m->w_lm)) || (!no_logits && !aligned16(st->logits)) ||
       (int64_t(m->V) * int64_t(elem_size(m->dtype))) % 16 != 0 ||
       (int64_t(m->L_cap) * int64_t(elem_size(m->dtype))) % 16 != 0)
     return EC_E_ALIGN;

@@ -42,61 +42,13 @@
 
 #include "ec_device.h"
 #include "ec_launch.h"
+#include "ec_softmax_stats.h"
 
 namespace ec {
 
 namespace {
 
-constexpr int32_t kNoIdx = 0x7fffffff;
 constexpr int32_t kRedo = -1;     // partial marker: the combine recomputes this segment exactly
-
-__device__ __forceinline__ EntropyPartial merge(const EntropyPartial& a, const EntropyPartial& b) {
-  EntropyPartial r;
-  r.m = fmaxf(a.m, b.m);
-  const bool ea = (a.m == -INFINITY), eb = (b.m == -INFINITY);
-  const float da = ea ? 0.f : (a.m - r.m) * kLog2e;
-  const float db = eb ? 0.f : (b.m - r.m) * kLog2e;
-  const float ra = ea ? 0.f : fast_exp2(da);
-  const float rb = eb ? 0.f : fast_exp2(db);
-  r.z = a.z * ra + b.z * rb;
-  r.s2 = ra * (a.s2 + da * a.z) + rb * (b.s2 + db * b.z);
-  r.idx = (a.m > b.m) ? a.idx : ((b.m > a.m) ? b.idx : min(a.idx, b.idx));
-  return r;
-}
-
-// Exact per-element accumulation (any value).
-struct SafeAcc {
-  float m = -INFINITY, z = 0.f, s2 = 0.f, best = -INFINITY;
-  int32_t idx = kNoIdx;
-  bool bad = false;
-  __device__ __forceinline__ void add(float x, int32_t j) {
-    if (x != x) { bad = true; return; }                      // NaN: ignored by argmax
-    if (x > best || idx == kNoIdx) { best = x; idx = j; }   // lowest index wins ties
-    if (x == INFINITY) { bad = true; return; }
-    if (x == -INFINITY) return;                              // weight exactly 0
-    if (x > m) {
-      if (m != -INFINITY) {
-        const float d = (m - x) * kLog2e;
-        const float r = fast_exp2(d);
-        s2 = r * (s2 + d * z);
-        z = r * z;
-      }
-      m = x;
-    }
-    const float u = (x - m) * kLog2e;
-    const float e = fast_exp2(u);
-    z += e;
-    s2 = fmaf(e, u, s2);
-  }
-  __device__ __forceinline__ EntropyPartial result() const {
-    EntropyPartial p;
-    p.m = best;          // includes +inf, so the argmax merge sees it
-    p.z = bad ? NAN : z;
-    p.s2 = bad ? NAN : s2;
-    p.idx = idx;
-    return p;
-  }
-};
 
 template <typename T> struct VecOf;
 template <> struct VecOf<float> { typedef f32x4 type; };
@@ -127,12 +79,6 @@ __device__ __forceinline__ uint32_t pk_max3(uint32_t a, uint32_t b, uint32_t c) 
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z));
 }
 constexpr uint32_t kPkNegInf = 0xfc00fc00u;   // fp16 -inf in both halves (padding)
-
-__device__ __forceinline__ EntropyPartial empty_partial() {
-  EntropyPartial p;
-  p.m = -INFINITY; p.z = 0.f; p.s2 = 0.f; p.idx = kNoIdx;
-  return p;
-}
 
 __device__ __forceinline__ EntropyPartial redo_partial() {
   EntropyPartial p;
@@ -435,7 +381,42 @@ __device__ __forceinline__ bool better(float pj, int posj, float pi, int posi) {
   return posj < posi;                      // equal (or both NaN): lower position first
 }
 
-template <typename T>
+// Partials written by the LM head's epilogue (one per row and tile group, no
+// segment to redo): 32 lanes per row, lane q folding partials q, q + 32, ...
+// in order, all of a batch's loads issued first (24 per lane: one batch up to
+// 768 partials per row), then a butterfly over the 32 lanes (lower lane
+// first).  Every lane of the row returns its statistics.
+constexpr int kFoldBatch = 24;
+__device__ __forceinline__ EntropyPartial fold_row32(const EntropyPartial* __restrict__ part, int P,
+                                                     int row, int q) {
+  const EntropyPartial* rp = part + int64_t(row) * P;
+  EntropyPartial acc = empty_partial();
+  for (int b = 0; b < P; b += 32 * kFoldBatch) {          // uniform across the row's lanes
+    EntropyPartial v[kFoldBatch];
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) {
+      const int k = b + 32 * i + q;
+      v[i] = (k < P) ? rp[k] : empty_partial();
+    }
+#pragma unroll
+    for (int i = 0; i < kFoldBatch; ++i) acc = merge(acc, v[i]);
+  }
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    EntropyPartial other;
+    other.m = __shfl_xor(acc.m, o, 32);
+    other.z = __shfl_xor(acc.z, o, 32);
+    other.s2 = __shfl_xor(acc.s2, o, 32);
+    other.idx = __shfl_xor(acc.idx, o, 32);
+    acc = (q & o) ? merge(other, acc) : merge(acc, other);
+  }
+  return acc;
+}
+
+// FUSED: the rows' partials come from the LM head (at most 32 rows, P per
+// row, see fold_row32) and logits is not read; otherwise from
+// entropy_partials_kernel (P segments per row, folded by combine_row).
+template <typename T, bool FUSED = false>
 __global__ __launch_bounds__(kStepThreads) void entropy_step_kernel(
     const T* __restrict__ logits, int64_t stride, int64_t V,
     const EntropyPartial* __restrict__ part, int P, int32_t max_rows,
@@ -460,11 +441,22 @@ __global__ __launch_bounds__(kStepThreads) void entropy_step_kernel(
   // every per-candidate load goes out at once (the arrays hold max_rows entries)
   const int posi = (choose && tid < max_rows) ? cand_pos[tid] : 0;
   const int hl = choose ? *history_len : 0;
-  for (int row = w; row < nc; row += kWaves) {             // wave-uniform
-    const EntropyPartial acc = combine_row<T>(logits, stride, V, part, P, row, lane);
-    if (lane == 0) {
-      finish_row(acc, row, H, A, p1);
-      finish_row(acc, row, s_h, s_am, s_p1);
+  if constexpr (FUSED) {
+    const int row = tid >> 5, q = tid & 31;
+    if (row < nc) {                                        // uniform across the row's 32 lanes
+      const EntropyPartial acc = fold_row32(part, P, row, q);
+      if (q == 0) {
+        finish_row(acc, row, H, A, p1);
+        finish_row(acc, row, s_h, s_am, s_p1);
+      }
+    }
+  } else {
+    for (int row = w; row < nc; row += kWaves) {           // wave-uniform
+      const EntropyPartial acc = combine_row<T>(logits, stride, V, part, P, row, lane);
+      if (lane == 0) {
+        finish_row(acc, row, H, A, p1);
+        finish_row(acc, row, s_h, s_am, s_p1);
+      }
     }
   }
   if (tid < nc) s_pos[tid] = posi;
@@ -571,6 +563,20 @@ hipError_t launch_entropy_step(const void* logits, int dtype, int32_t max_rows,
                        static_cast<const float*>(logits), stride, V, part, P, max_rows, n_rows_dev,
                        H, argmax, p1, cand_pos, n_unmask, tau, chosen, n_chosen, tokens, is_masked,
                        history, history_len, history_cap, e_max, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_entropy_step_fused(const EntropyPartial* part, int32_t P, int32_t max_rows,
+                                     const int32_t* n_rows_dev, float* H, int32_t* argmax, float* p1,
+                                     const int32_t* cand_pos, int32_t n_unmask, float tau,
+                                     int32_t* chosen, int32_t* n_chosen, int32_t* tokens,
+                                     uint8_t* is_masked, int32_t* history, int32_t* history_len,
+                                     int32_t history_cap, float* e_max, int32_t* flag, hipStream_t s) {
+  if (max_rows < 1 || max_rows > kLmStatRows || P < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((entropy_step_kernel<bf16_t, true>), dim3(1), dim3(kStepThreads), 0, s,
+                     static_cast<const bf16_t*>(nullptr), int64_t(0), int64_t(0), part, int(P), max_rows,
+                     n_rows_dev, H, argmax, p1, cand_pos, n_unmask, tau, chosen, n_chosen, tokens,
+                     is_masked, history, history_len, history_cap, e_max, flag);
   return hipGetLastError();
 }
 

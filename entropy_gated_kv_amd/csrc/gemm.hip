@@ -31,7 +31,10 @@
 #include <stdlib.h>
 
 #include "ec_device.h"
+#include <utility>
+
 #include "ec_launch.h"
+#include "ec_softmax_stats.h"
 
 namespace ec {
 
@@ -85,6 +88,8 @@ struct GP {
   float* part;       // split-K partials
   int S;             // K splits (skinny)
   int KS;            // k per split
+  EntropyPartial* stats;   // packed LM head: softmax statistics per (row, tile group), or null
+  int stat_groups;         // tile groups per row (the row stride of stats)
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -328,29 +333,41 @@ __device__ __forceinline__ void skinny_body(const GP& p, int n_rows, char* smem)
 }
 
 // The LM head on the packed weight (bf16, at most 32 candidate rows, K not
-// split).  A workgroup owns groups of TPW column tiles (64 columns each);
-// for every k-block it multiplies the one staged block of activations with
-// the weights of all TPW tiles, so each activation stage and its barriers
-// serve TPW tiles.  It walks its groups blockIdx.x, blockIdx.x + gridDim.x,
-// ... (a persistent grid when there are more groups than resident slots) as
-// one flat sequence of (group, k-block, tile) steps, with the weight ring
-// running on across group boundaries.  For each tile the products and their
-// order are those of the skinny kernel (k-blocks ascending, the same MFMA
-// chain), so the logits are the same bits.  A finished group's logits leave
-// through an LDS area of their own.
+// split).  Each workgroup owns one group of TPW column tiles (64 columns
+// each): for every k-block it stages the candidates' activations in LDS once
+// and multiplies them with the weights of all TPW tiles, so one activation
+// stage and its barriers serve TPW tiles, and the weight ring runs on across
+// tiles and k-blocks.  For each tile the products and their order are those
+// of the skinny kernel (k-blocks ascending, the same MFMA chain), so the
+// logits are the same bits.  After the loop, where the ring is no longer
+// live, the group's logits leave through an LDS area of their own, and/or
+// (p.stats) each row's softmax statistics over the group's columns.  The
+// epilogue stays out of the loop on purpose: inside it, its register demand
+// made the scheduler sink the weight prefetches and drain the ring (3-4x
+// slower).
 constexpr int kLmNV = 2 * kNV;                        // 512 B of each weight row per k-block
 constexpr int kLmROWB = skit<bf16_t, kLmNV>() * 2 + 16;
 constexpr int kLmOP = kSkinnyNT * 2 + 16;             // staged logits row (bytes)
+constexpr int kLmMaxTPW = 4;
 constexpr size_t lm_lds(int tpw) { return size_t(2 * 16) * kLmROWB + size_t(tpw) * 2 * 16 * kLmOP; }
 template <int N> struct IC { static constexpr int value = N; };
+
+// Steps I0, I0 + 1, ... of the sequence, step i taking ring slot i % 3 and
+// tile i % TPW (indices known at compile time); `guard` skips those at or past
+// `n` (the sequence's ragged end)
+template <int TPW, int I0, bool GUARD, typename F, int... I>
+__device__ __forceinline__ void lm_steps(F& f, int n, std::integer_sequence<int, I...>) {
+  ((!GUARD || I0 + I < n ? f(IC<(I0 + I) % 3>{}, IC<(I0 + I) % TPW>{}) : void()), ...);
+}
 
 template <int TPW>
 __global__ __launch_bounds__(kThreads) void lmhead_packed_kernel(GP p) {
   using T = bf16_t;
   constexpr int MB = 2, NV = kLmNV, VPL = 8, KIT = skit<T, NV>(), ROWB = kLmROWB, OP = kLmOP;
   constexpr int KB = KIT / 32;                          // 1 KB fragments per row group and k-block
+  constexpr int U = TPW % 3 == 0 ? TPW : 3 * TPW;       // steps per loop body: ring slot and tile repeat
   static_assert(KB == NV, "one fragment per vector of a lane");
-  static_assert(TPW >= 1 && TPW <= 3, "tiles per group");
+  static_assert(TPW >= 1 && TPW <= kLmMaxTPW, "tiles per group");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const lg = smem + MB * 16 * ROWB;               // logits staging, TPW tiles
   const int n_rows = min(*p.n_rows, p.max_rows);
@@ -358,15 +375,13 @@ __global__ __launch_bounds__(kThreads) void lmhead_packed_kernel(GP p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
   const int nit = p.K / KIT;                            // K is a multiple of KIT (host plan)
   const int ntiles = (p.N + kSkinnyNT - 1) / kSkinnyNT;
-  const int ngroups = (ntiles + TPW - 1) / TPW;
-  const int G = int(gridDim.x);
-  const int nmine = (ngroups - int(blockIdx.x) + G - 1) / G;
-  if (nmine <= 0 || nit <= 0) return;
-  const int nsteps = nmine * nit * TPW;                 // this workgroup's (group, k-block, tile) steps
-  // tile j of the workgroup's group m; past the last tile, the last tile again
-  // (a short last group computes and stores that tile more than once, the
-  // same values each time)
-  auto tile_of = [&](int m, int j) { return min((int(blockIdx.x) + m * G) * TPW + j, ntiles - 1); };
+  const int gi = int(blockIdx.x);                       // this workgroup's group
+  if (gi * TPW >= ntiles || nit <= 0) return;
+  const int nsteps = nit * TPW;                         // (k-block, tile) steps
+  // tile j of the group; past the last tile, the last tile again (a short
+  // last group computes and stores that tile more than once, the same values
+  // each time)
+  auto tile_of = [&](int j) { return min(gi * TPW + j, ntiles - 1); };
   // weights of k-block kb of a tile: the wave's 16-row group (clamped to the
   // last group; columns past N are never stored), one 8 KB run
   const T* const Wb = static_cast<const T*>(p.Wpk) + lane * VPL;
@@ -375,20 +390,15 @@ __global__ __launch_bounds__(kThreads) void lmhead_packed_kernel(GP p) {
     return Wb + (int64_t(grp) * (p.K / 32) + kb * KB) * 64 * VPL;
   };
   typedef u32x4 WBuf[NV];
-  // prefetch cursor: group and k-block of the next weights loaded (which
-  // tile of the group is known at each step)
-  int pf_m = 0, pf_kb = 0;
+  // prefetch cursor: the k-block of the next weights loaded (which tile is
+  // known at each step); past the end, the last k-block again
+  int pf_kb = 0;
   auto w_load = [&](WBuf& dst, auto PJ) {
     constexpr int j = decltype(PJ)::value;
-    const T* src = wsrc(tile_of(pf_m, j), pf_kb);
+    const T* src = wsrc(tile_of(j), min(pf_kb, nit - 1));
 #pragma unroll
     for (int v = 0; v < NV; ++v) dst[v] = *reinterpret_cast<const u32x4*>(src + v * 64 * VPL);
-    if constexpr (j == TPW - 1) {
-      if (++pf_kb == nit) {
-        pf_kb = 0;
-        ++pf_m;
-      }
-    }
+    if constexpr (j == TPW - 1) ++pf_kb;
   };
   // activations: the candidate rows (gathered), KIT k per k-block
   constexpr int AV = MB * 16 * (KIT / VPL);
@@ -427,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_packed_kernel(GP p) {
   // stores 16-byte chunks of rows, a row of a tile being one 128-byte line
   // (the host launches this kernel only for 16-byte aligned rows).  The area
   // is written again only after a whole group of barriers.
-  auto epilogue = [&](int m) {
+  auto epilogue = [&]() {
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
 #pragma unroll
@@ -441,10 +451,88 @@ __global__ __launch_bounds__(kThreads) void lmhead_packed_kernel(GP p) {
           acc[j][rb][e] = 0.f;
         }
     __syncthreads();
+    if (p.stats != nullptr) {
+      // each row's softmax statistics over the group's columns, from the
+      // rounded logits just staged: 8 lanes per row, lane q taking chunk q (8
+      // columns) of every tile of the group; a repeated last tile adds
+      // nothing.  The row's maximum M comes first, then every lane sums 2^u
+      // and 2^u u with u = (x - M) log2 e, exact 0 for the maximum, and the
+      // lanes add their sums in a fixed butterfly.  A row holding a NaN or an
+      // infinity takes the exact per-element accumulation instead.
+      const int r = tid >> 3, q = tid & 7;
+      if (r < n_rows) {                                 // uniform across the row's 8 lanes
+        // chunk j of this lane from the staging area, columns outside the
+        // group's logits as -inf (read twice rather than held in registers)
+        auto chunk = [&](int j, float (&x)[8]) {
+          unpack16(*reinterpret_cast<const u32x4*>(lg + (j * MB * 16 + r) * OP + q * 16), x);
+          const int c0 = (gi * TPW + j) * kSkinnyNT + q * 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gi * TPW + j >= ntiles || c0 + e >= p.N) x[e] = -INFINITY;
+        };
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+          float x[8];
+          chunk(j, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mx = __builtin_elementwise_maximum(mx, x[e]);   // NaN propagates
+        }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, o, 8));
+        EntropyPartial st;
+        if (fabsf(mx) < INFINITY) {
+          float z = 0.f, s2 = 0.f;
+          int idx = kNoIdx;
+#pragma unroll
+          for (int j = TPW - 1; j >= 0; --j) {
+            float x[8];
+            chunk(j, x);
+#pragma unroll
+            for (int e = 7; e >= 0; --e) {
+              const float u = (x[e] - mx) * kLog2e;
+              const float w = fast_exp2(u);
+              z += w;
+              s2 += (w > 0.f) ? w * u : 0.f;               // -inf columns weigh exactly 0
+              if (x[e] == mx) idx = (gi * TPW + j) * kSkinnyNT + q * 8 + e;
+            }
+          }
+#pragma unroll
+          for (int o = 1; o < 8; o <<= 1) {
+            const float zo = __shfl_xor(z, o, 8), so = __shfl_xor(s2, o, 8);
+            z = (q & o) ? zo + z : z + zo;
+            s2 = (q & o) ? so + s2 : s2 + so;
+            idx = min(idx, __shfl_xor(idx, o, 8));
+          }
+          st.m = mx; st.z = z; st.s2 = s2; st.idx = idx;
+        } else {
+          SafeAcc sa;
+          for (int j = 0; j < TPW; ++j) {
+            float x[8];
+            chunk(j, x);
+            const int c0 = (gi * TPW + j) * kSkinnyNT + q * 8;
+            for (int e = 0; e < 8; ++e)
+              if (gi * TPW + j < ntiles && c0 + e < p.N) sa.add(x[e], c0 + e);
+          }
+          st = sa.result();
+#pragma unroll
+          for (int o = 1; o < 8; o <<= 1) {
+            EntropyPartial other;
+            other.m = __shfl_xor(st.m, o, 8);
+            other.z = __shfl_xor(st.z, o, 8);
+            other.s2 = __shfl_xor(st.s2, o, 8);
+            other.idx = __shfl_xor(st.idx, o, 8);
+            st = (q & o) ? merge(other, st) : merge(st, other);
+          }
+        }
+        if (q == 0) p.stats[int64_t(r) * p.stat_groups + gi] = st;
+      }
+    }
+    if (C == nullptr) return;                           // statistics only
 #pragma unroll
     for (int k = tid; k < TPW * MB * 16 * (kSkinnyNT / 8); k += kThreads) {
       const int j = k / (MB * 16 * (kSkinnyNT / 8)), rk = k % (MB * 16 * (kSkinnyNT / 8));
-      const int r = rk / (kSkinnyNT / 8), c0 = tile_of(m, j) * kSkinnyNT;
+      const int r = rk / (kSkinnyNT / 8), c0 = tile_of(j) * kSkinnyNT;
       const int n = c0 + (rk % (kSkinnyNT / 8)) * 8;
       if (r >= n_rows || n >= p.N) continue;
       const u32x4 v = *reinterpret_cast<const u32x4*>(lg + (j * MB * 16 + r) * OP + (n - c0) * 2);
@@ -457,17 +545,16 @@ __global__ __launch_bounds__(kThreads) void lmhead_packed_kernel(GP p) {
       }
     }
   };
-  int cu_kb = 0, cu_m = 0;                              // k-block and group of the current step
+  int cu_kb = 0;                                        // k-block of the current step
   WBuf r0, r1, r2;
   // one step (ring slot S, tile J of the group): prefetch the weights two
   // steps ahead; multiply the staged activations with this tile's weights.
-  // After the group's last tile, stage the next k-block's activations, and
-  // after the last k-block, the group's logits.
+  // After the group's last tile, stage the next k-block's activations.
   auto step = [&](auto S, auto J) {
     constexpr int s = decltype(S)::value, j = decltype(J)::value;
     WBuf& cur = s == 0 ? r0 : s == 1 ? r1 : r2;
     WBuf& nxt = s == 0 ? r2 : s == 1 ? r0 : r1;
-    if constexpr (j == 0) a_load(cu_kb + 1 == nit ? 0 : cu_kb + 1);   // before the W prefetch
+    if constexpr (j == 0) a_load(min(cu_kb + 1, nit - 1));   // before the W prefetch
     w_load(nxt, IC<(j + 2) % TPW>{});
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -486,11 +573,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_packed_kernel(GP p) {
       __syncthreads();                                  // every wave is done with this stage
       a_store();
       __syncthreads();
-      if (++cu_kb == nit) {
-        epilogue(cu_m);
-        cu_kb = 0;
-        ++cu_m;
-      }
+      ++cu_kb;
     }
   };
   w_load(r0, IC<0>{});
@@ -499,22 +582,13 @@ __global__ __launch_bounds__(kThreads) void lmhead_packed_kernel(GP p) {
   a_store();
   __syncthreads();
   int u = 0;
-  if constexpr (TPW == 2) {
-    for (; u + 6 <= nsteps; u += 6) {
-      step(IC<0>{}, IC<0>{}); step(IC<1>{}, IC<1>{}); step(IC<2>{}, IC<0>{});
-      step(IC<0>{}, IC<1>{}); step(IC<1>{}, IC<0>{}); step(IC<2>{}, IC<1>{});
-    }
-    if (u < nsteps) { step(IC<0>{}, IC<0>{}); step(IC<1>{}, IC<1>{}); }
-    if (u + 2 < nsteps) { step(IC<2>{}, IC<0>{}); step(IC<0>{}, IC<1>{}); }
-  } else {
-    for (; u + 3 <= nsteps; u += 3) {
-      step(IC<0>{}, IC<0 % TPW>{}); step(IC<1>{}, IC<1 % TPW>{}); step(IC<2>{}, IC<2 % TPW>{});
-    }
-    if constexpr (TPW == 1) {                           // with three tiles, nsteps is a multiple of 3
-      if (u < nsteps) step(IC<0>{}, IC<0>{});
-      if (u + 1 < nsteps) step(IC<1>{}, IC<0>{});
-    }
-  }
+#pragma clang loop unroll(disable)
+  for (; u + U <= nsteps; u += U) lm_steps<TPW, 0, false>(step, 0, std::make_integer_sequence<int, U>{});
+  // the ragged end (TPW not a multiple of 3): fewer than U steps, starting at
+  // ring slot 0 and tile 0
+  if constexpr (U != TPW)
+    if (u < nsteps) lm_steps<TPW, 0, true>(step, nsteps - u, std::make_integer_sequence<int, U - 1>{});
+  epilogue();
 }
 
 // MBX: largest count of 16-row blocks this launch can see (2, 4, 6 or 8, from
@@ -1037,7 +1111,7 @@ Plan plan_skinny(const GemmArgs& a) {
   pl.tiles = (a.N + kSkinnyNT - 1) / kSkinnyNT;
   // eight vectors per lane for the LM head (<= 32 rows, enough tiles that K
   // is never split, K a multiple of the longer iteration)
-  pl.NV = (a.epi == Epi::kLogits && pl.MBX == 2 && pl.tiles >= 512 && a.K % skit<T, 2 * kNV>() == 0)
+  pl.NV = (a.epi == Epi::kLogits && pl.MBX == 2 && pl.tiles >= kLmMinTiles && a.K % skit<T, 2 * kNV>() == 0)
               ? 2 * kNV : kNV;
   const int KIT = pl.NV == kNV ? skit<T>() : skit<T, 2 * kNV>();
   const int iters = (a.K + KIT - 1) / KIT;
@@ -1078,10 +1152,11 @@ void skinny_by_shape(const Plan& pl, dim3 g, size_t lds, hipStream_t s, const GP
   else go_skinny<T, 8, DUAL, EPI>(g, lds, s, p);
 }
 
-// The packed LM head over `tiles` column tiles: groups of TPW = ceil(tiles /
-// resident slots) tiles, one workgroup per group, when that is at most three;
-// otherwise single tiles on a persistent grid of one workgroup per slot.
-// Slots per CU come from the occupancy query (once per instance and process).
+// The packed LM head over `tiles` column tiles: TPW = the smallest count of
+// tiles per workgroup (1 .. kLmMaxTPW) whose groups fit in one round of
+// resident workgroups, else kLmMaxTPW (then more than one round); one
+// workgroup per group.  Slots per CU come from the occupancy query (once per
+// instance and process).
 template <int TPW>
 int lm_slots_per_cu() {
   static const int n = [] {
@@ -1092,25 +1167,39 @@ int lm_slots_per_cu() {
   return n;
 }
 
-template <int TPW>
-void go_lmhead(unsigned grid, hipStream_t s, const GP& p) {
-  hipLaunchKernelGGL(lmhead_packed_kernel<TPW>, dim3(grid), dim3(kThreads), lm_lds(TPW), s, p);
+struct LmPlan {
+  int tpw;          // tiles per group
+  unsigned grid;    // workgroups = groups
+  int groups;       // tile groups (statistics per row)
+};
+
+LmPlan lm_plan(unsigned tiles) {
+  const unsigned cus = unsigned(device_cu_count());
+  const unsigned slots[kLmMaxTPW] = {unsigned(lm_slots_per_cu<1>()) * cus, unsigned(lm_slots_per_cu<2>()) * cus,
+                                     unsigned(lm_slots_per_cu<3>()) * cus, unsigned(lm_slots_per_cu<4>()) * cus};
+  int t = kLmMaxTPW;
+  for (int c = 1; c <= kLmMaxTPW; ++c)
+    if ((tiles + c - 1) / c <= slots[c - 1]) { t = c; break; }
+  const unsigned groups = (tiles + t - 1) / t;
+  return LmPlan{t, groups, int(groups)};
 }
 
-void launch_lmhead(unsigned tiles, hipStream_t s, const GP& p) {
-  const unsigned cus = unsigned(device_cu_count());
-  const unsigned slots3 = unsigned(lm_slots_per_cu<3>()) * cus;
-  const unsigned per = slots3 > 0 ? (tiles + slots3 - 1) / slots3 : 0;
-  if (per == 3 || per == 2) {
-    const unsigned slots = per == 3 ? slots3 : unsigned(lm_slots_per_cu<2>()) * cus;
-    if ((tiles + per - 1) / per <= slots) {
-      if (per == 3) go_lmhead<3>((tiles + 2) / 3, s, p);
-      else go_lmhead<2>((tiles + 1) / 2, s, p);
-      return;
-    }
+void launch_lmhead(const LmPlan& lp, hipStream_t s, const GP& p) {
+  switch (lp.tpw) {
+    case 1: hipLaunchKernelGGL(lmhead_packed_kernel<1>, dim3(lp.grid), dim3(kThreads), lm_lds(1), s, p); break;
+    case 2: hipLaunchKernelGGL(lmhead_packed_kernel<2>, dim3(lp.grid), dim3(kThreads), lm_lds(2), s, p); break;
+    case 3: hipLaunchKernelGGL(lmhead_packed_kernel<3>, dim3(lp.grid), dim3(kThreads), lm_lds(3), s, p); break;
+    default: hipLaunchKernelGGL(lmhead_packed_kernel<4>, dim3(lp.grid), dim3(kThreads), lm_lds(4), s, p); break;
   }
-  const unsigned slots1 = unsigned(lm_slots_per_cu<1>()) * cus;
-  go_lmhead<1>((slots1 > 0 && slots1 < tiles) ? slots1 : tiles, s, p);
+}
+
+// Whether the skinny LM head takes the packed kernel (bf16, at most 32 rows,
+// K a multiple of its k-block, the packed weight, 16-byte aligned logit rows
+// or no logits at all)
+template <typename T>
+bool packed_lmhead(const Plan& pl, const GP& p) {
+  return sizeof(T) == 2 && p.epi == int(Epi::kLogits) && pl.NV == 2 * kNV && p.Wpk != nullptr &&
+         (p.ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
 }
 
 template <typename T>
@@ -1122,9 +1211,8 @@ hipError_t dispatch_skinny(Epi epi, const Plan& pl, dim3 g, size_t lds, hipStrea
     case Epi::kSwiGLU: skinny_by_shape<T, 3, true>(pl, g, lds, s, p); break;
     case Epi::kLogits:
       if constexpr (sizeof(T) == 2) {
-        if (pl.NV == 2 * kNV && p.Wpk != nullptr && (p.ldc & 7) == 0 &&
-            (reinterpret_cast<uintptr_t>(p.C) & 15) == 0) {
-          launch_lmhead(g.x, s, p);
+        if (packed_lmhead<T>(pl, p)) {
+          launch_lmhead(lm_plan(g.x), s, p);
           break;
         }
       }
@@ -1164,6 +1252,14 @@ hipError_t launch_typed(const GemmArgs& a, void* ws, hipStream_t s, bool allow_s
   if (!allow_split || ws == nullptr) { pl.S = 1; pl.KS = a.K; }
   p.S = pl.S; p.KS = pl.KS;
   p.part = static_cast<float*>(ws);
+  p.stats = nullptr;
+  p.stat_groups = 0;
+  if (a.stats_groups != nullptr) *a.stats_groups = 0;
+  if (a.stats != nullptr && (a.paths & kPathSmall) && packed_lmhead<T>(pl, p)) {
+    p.stats = a.stats;
+    p.stat_groups = lm_plan(unsigned(pl.tiles)).groups;
+    if (a.stats_groups != nullptr) *a.stats_groups = p.stat_groups;
+  }
   if (a.paths & kPathSmall) {
     const int kit_sk = pl.NV == kNV ? skit<T>() : skit<T, 2 * kNV>();
     const size_t lds_sk = size_t(pl.MBX) * 16 * (kit_sk * sizeof(T) + 16);
@@ -1244,6 +1340,10 @@ hipError_t launch_pack_fragments(const void* W, int64_t N, int64_t K, void* out,
                      dim3(kThreads), 0, s, static_cast<const u32x4*>(W), N, K, static_cast<u32x4*>(out));
   return hipGetLastError();
 }
+
+int lmhead_max_stat_groups(int N) { return (N + kSkinnyNT - 1) / kSkinnyNT; }
+static_assert(skit<bf16_t, 2 * kNV>() == kLmKBlock && kSkinnyNT == 64 && kLmStatRows == 2 * 16,
+              "the host checks' conditions for the packed LM head");
 
 hipError_t launch_gemm_rows(const GemmArgs& a, void* ws, hipStream_t s) {
   if (a.N % 32 != 0 || a.K % gemm_k_multiple(a.dtype) != 0) return hipErrorNotSupported;

@@ -82,7 +82,7 @@ class DeviceSequence:
     """Per-sequence device state (tokens, mask, history, flag, KV caches, step outputs)."""
 
     def __init__(self, model: DeviceModel, tokens: np.ndarray, masked: np.ndarray,
-                 history_cap: int, max_block: int, ws=None):
+                 history_cap: int, max_block: int, ws=None, keep_logits: bool = True):
         import torch
         sh = model.shape
         self.model, self.L, self.max_block = model, len(tokens), max_block
@@ -100,7 +100,9 @@ class DeviceSequence:
                         for _ in range(sh.n_layers)]
         self.rows = torch.zeros(model.L_cap, dtype=i32, device=dev)
         self.n_rows = torch.zeros(1, dtype=i32, device=dev)
-        self.logits = torch.zeros((max_block, sh.vocab), dtype=td, device=dev)
+        # keep_logits=False: no logits buffer (a packed LM head then writes
+        # softmax statistics instead, see ec.h); self.logits is None
+        self.logits = torch.zeros((max_block, sh.vocab), dtype=td, device=dev) if keep_logits else None
         self.row_entropy = torch.zeros(max_block, dtype=torch.float32, device=dev)
         self.row_argmax = torch.zeros(max_block, dtype=i32, device=dev)
         self.row_top1 = torch.zeros(max_block, dtype=torch.float32, device=dev)
@@ -125,7 +127,8 @@ class DeviceSequence:
         s.full_flag = self.full_flag.data_ptr()
         s.k_cache = C.cast(self._k_arr, C.POINTER(C.c_void_p))
         s.v_cache = C.cast(self._v_arr, C.POINTER(C.c_void_p))
-        s.rows, s.n_rows, s.logits = self.rows.data_ptr(), self.n_rows.data_ptr(), self.logits.data_ptr()
+        s.rows, s.n_rows = self.rows.data_ptr(), self.n_rows.data_ptr()
+        s.logits = self.logits.data_ptr() if keep_logits else None
         s.row_entropy, s.row_argmax = self.row_entropy.data_ptr(), self.row_argmax.data_ptr()
         s.row_top1, s.chosen = self.row_top1.data_ptr(), self.chosen.data_ptr()
         s.n_chosen, s.e_max = self.n_chosen.data_ptr(), self.e_max.data_ptr()

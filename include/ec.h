@@ -308,7 +308,15 @@ typedef struct ec_state {
   /* per-step outputs (device, caller-owned) */
   int32_t* rows;              /* [L_cap]                                   */
   int32_t* n_rows;            /* [1]                                       */
-  void* logits;               /* [max_block, V] dtype                      */
+  /* [max_block, V] dtype.  May be NULL with an LM head whose packed copy the
+   * step reads (w_lm_packed set, block_len <= 32, V > 32704, d % 256 == 0;
+   * EC_E_UNSUPPORTED otherwise, EC_E_NULL without w_lm_packed): the LM head
+   * then writes no logits but each candidate's softmax statistics per group
+   * of column tiles (in the workspace), which the step folds into H, argmax
+   * and p1 in place of the entropy pass.  Every other output is as with a
+   * buffer; H, p1 and E may differ from it in the last float32 bits (the
+   * statistics are summed in another order). */
+  void* logits;
   float* row_entropy;         /* [max_block]                               */
   int32_t* row_argmax;        /* [max_block]                               */
   float* row_top1;            /* [max_block]                               */

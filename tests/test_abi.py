@@ -140,10 +140,10 @@ def test_step_rejects_misaligned_weights(lib):
         caches = (C.c_void_p * 1)(FAKE)
         st = L.ec_state(L=256, tokens=FAKE, is_masked=FAKE, history=FAKE, history_len=FAKE,
                         history_cap=64, full_flag=FAKE, k_cache=caches, v_cache=caches, rows=FAKE,
-                        n_rows=FAKE, logits=FAKE, row_entropy=FAKE, row_argmax=FAKE, row_top1=FAKE,
+                        n_rows=FAKE, logits=bad.get("logits", FAKE), row_entropy=FAKE, row_argmax=FAKE, row_top1=FAKE,
                         chosen=FAKE, n_chosen=FAKE, e_max=FAKE, kv_drift=None,
                         attn_out=bad.get("attn_out"))
-        cfg = L.ec_step_cfg(tau=1.0, k=16, n_unmask=2, block_start=192, block_len=32,
+        cfg = L.ec_step_cfg(tau=1.0, k=16, n_unmask=2, block_start=192, block_len=bad.get("block_len", 32),
                             mode=bad.get("mode", 0))
         return lib.ec_step(C.byref(m), C.byref(st), C.byref(cfg), FAKE, 0, None, None)
 
@@ -163,6 +163,14 @@ def test_step_rejects_misaligned_weights(lib):
     assert call(V=1040, w_lm=None) == -4                           # no LM head: any V
     assert call(w_lm_packed=FAKE, dtype=0) == -3
     assert call(w_lm_packed=FAKE, w_lm=None) == -1
+    # no logits buffer: only where the packed LM head runs (it then writes
+    # softmax statistics instead): a packed copy, block <= 32, V > 32704, d % 256 == 0
+    assert call(logits=None, w_lm_packed=FAKE, V=32768) == -4      # accepted: the workspace is short
+    assert call(logits=None, V=32768) == -1                        # no packed copy
+    assert call(logits=None, w_lm=None, V=32768) == -1             # no LM head: the caller's logits are input
+    assert call(logits=None, w_lm_packed=FAKE, V=32704) == -7      # 511 column tiles
+    assert call(logits=None, w_lm_packed=FAKE, V=32768, block_len=64) == -7
+    assert call(logits=ODD, w_lm_packed=FAKE, V=32768) == -5       # a buffer must be aligned
 
 
 def test_pack_lm_head_argument_checks(lib):

@@ -153,6 +153,20 @@ void step_cases() {
     s.m.w_lm = nullptr;                                // no LM head: the caller decodes
     EXPECT(ec::check_step(&s.m, &s.st, &s.c, A) == EC_OK);
   }
+  {
+    StepCase s(1);                                     // no logits buffer
+    s.st.logits = nullptr;
+    EXPECT(ec::check_step(&s.m, &s.st, &s.c, A) == EC_E_NULL);        // no packed copy
+    s.m.w_lm_packed = A;
+    EXPECT(ec::check_step(&s.m, &s.st, &s.c, A) == EC_E_UNSUPPORTED); // V = 2048: 32 column tiles
+    s.m.V = 32768;
+    EXPECT(ec::check_step(&s.m, &s.st, &s.c, A) == EC_OK);
+    s.m.d = 384;                                       // d % 256 != 0
+    EXPECT(ec::check_step(&s.m, &s.st, &s.c, A) == EC_E_UNSUPPORTED);
+    s.m.d = 256;
+    s.c.block_len = 33;
+    EXPECT(ec::check_step(&s.m, &s.st, &s.c, A) == EC_E_UNSUPPORTED);
+  }
 }
 
 void fuzz(int rounds) {
