@@ -1,7 +1,10 @@
 """ec_step under HIP graph capture: several steps captured into one graph and
 replayed three times (the state restored by eager copies, with eager work and
 synchronisation between replays) reproduce the eager trajectory bit for bit.
-The step records no memset and never synchronises, so it captures as is."""
+The step records no memset and never synchronises, so it captures as is.
+Cases: the tiny fp32 layer, a two-layer bf16 stack, and a one-layer bf16
+model stepping without a logits buffer (its packed LM head writes softmax
+statistics that the step folds)."""
 import numpy as np
 import pytest
 import torch
@@ -13,10 +16,15 @@ from synth import generators as G
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cfg_name", ["tiny_fp32", "stack_bf16"])
+@pytest.mark.parametrize("cfg_name", ["tiny_fp32", "stack_bf16", "no_logits_bf16"])
 def test_captured_steps_replay_like_eager(cfg_name):
+    keep_logits = True
     if cfg_name == "tiny_fp32":
         cfg, tau = C.TINY, float("inf")
+    elif cfg_name == "no_logits_bf16":
+        cfg = C.scaled(C.LLADA_LAYER, name="no_logits_graph", model_d=256, model_n_q_heads=2,
+                       model_n_kv_heads=2, model_vocab=40032, prompt_len=96, gen_len=64, block_len=32, k=16)
+        tau, keep_logits = 1.0, False
     else:
         cfg = C.scaled(C.LLADA_STACK, name="stack_graph", model_n_layers=2, model_d=256,
                        model_n_q_heads=4, model_n_kv_heads=2, model_head_dim=64, model_vocab=2048,
@@ -25,7 +33,8 @@ def test_captured_steps_replay_like_eager(cfg_name):
     w = G.model_weights(cfg)
     toks, masked = G.initial_sequence(cfg)
     dm = DeviceModel(cfg.model, cfg.dtype, cfg.L, w)
-    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len)
+    ds = DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=cfg.block_len,
+                        keep_logits=keep_logits)
     sched = C.unmask_schedule(cfg)
     state = lambda: [ds.tokens, ds.is_masked, ds.history, ds.history_len, ds.full_flag,
                      *ds.k_cache, *ds.v_cache]
@@ -36,7 +45,8 @@ def test_captured_steps_replay_like_eager(cfg_name):
     steps = sched[2:8]
 
     def outputs():
-        return [t.clone() for t in state()] + [ds.logits.clone(), ds.row_entropy.clone()]
+        out = [ds.row_entropy.clone(), ds.row_top1.clone(), ds.row_argmax.clone(), ds.e_max.clone()]
+        return [t.clone() for t in state()] + out + ([ds.logits.clone()] if keep_logits else [])
 
     for bs, bl, n in steps:                      # the eager reference
         ds.step(tau, cfg.k, bs, bl, n)
