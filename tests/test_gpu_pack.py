@@ -20,9 +20,13 @@
   tile) and four column tiles per workgroup; ragged last tiles (V % 64 = 32)
   and d = 256, 512, 768 (one, two, three k-blocks).
 """
+import math
+
 import numpy as np
 import pytest
 import torch
+
+import oracle as O
 
 from entropy_gated_kv_amd import lib as L
 from entropy_gated_kv_amd.runner import DeviceModel, DeviceSequence
@@ -110,3 +114,50 @@ def test_packed_lm_head_launch_shapes_agree(V, d):
     heads = d // 128
     steps_agree(C.scaled(C.LLADA_LAYER, model_vocab=V, model_d=d, model_n_q_heads=heads,
                                  model_n_kv_heads=heads))
+
+
+def test_non_finite_and_constant_rows_in_both_modes():
+    """Candidate rows whose logits hold +-inf or NaN (a logit scale of +inf,
+    -inf or NaN; 3e38 overflows some of a row) take the exact statistics path of the LM head's
+    epilogue, and a scale of 0 gives a row of zeros with H = ln V, p1 = 1/V
+    and argmax 0.  One full step decodes every candidate, with and without a
+    logits buffer: H is NaN exactly where the oracle's is (rows holding NaN
+    or +inf), finite rows within the step tests' bounds, argmax exact, and E
+    = NaN forces the next step full."""
+    cfg = C.scaled(C.LLADA_LAYER, name="non_finite", model_d=256, model_n_q_heads=2, model_n_kv_heads=2,
+                   model_vocab=40032, prompt_len=96, gen_len=64, block_len=32, k=16)
+    V = cfg.model.vocab
+    w = G.model_weights(cfg)
+    toks, masked = G.initial_sequence(cfg)
+    dm = DeviceModel(cfg.model, cfg.dtype, cfg.L, w, pack_lm_head=True)
+    bs, bl = cfg.prompt_len, cfg.block_len
+    special = {bs + 1: 0.0, bs + 5: math.inf, bs + 9: -math.inf, bs + 13: math.nan, bs + 17: 3e38}
+    for pos, v in special.items():
+        dm.logit_scale[pos] = v
+    a, f = [DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=bl, keep_logits=k)
+            for k in (True, False)]
+    cand = bs + np.flatnonzero(np.asarray(masked[bs:bs + bl], dtype=bool))
+    assert len(cand) == bl
+    for s in (a, f):
+        s.step(TAU, cfg.k, bs, bl, bl)
+    torch.cuda.synchronize()
+    z = a.logits[:bl].float().cpu().numpy().astype(np.float64)
+    Ho, Ao, Po = O.row_stats(z)
+    iz = int(np.searchsorted(cand, bs + 1))
+    assert np.all(z[iz] == 0) and Ao[iz] == 0 and abs(Ho[iz] - math.log(V)) < 1e-9
+    nan = np.isnan(Ho)
+    assert nan[[int(np.searchsorted(cand, p)) for p in (bs + 5, bs + 9, bs + 13)]].all()
+    shift = 2.0 ** -23 * np.where(np.isfinite(z), np.abs(z), 0.0).max(axis=1) * 1.4426950408889634
+    for s, name in ((a, "logits"), (f, "statistics")):
+        H, A, P = (s.row_entropy[:bl].cpu().numpy(), s.row_argmax[:bl].cpu().numpy(),
+                   s.row_top1[:bl].cpu().numpy())
+        np.testing.assert_array_equal(np.isnan(H), nan, err_msg=name)
+        assert np.all(np.abs(H[~nan] - Ho[~nan]) <= 1e-4 + 1e-5 * np.abs(Ho[~nan])), name
+        np.testing.assert_array_equal(A, Ao, err_msg=name)
+        np.testing.assert_array_equal(np.isnan(P), np.isnan(Po), err_msg=name)
+        ok = ~np.isnan(Po)
+        assert np.all(np.abs(P[ok] - Po[ok]) <= (1e-5 + shift[ok]) * Po[ok]), name
+        assert abs(P[iz] - 1.0 / V) <= 1e-6 / V, name
+        assert math.isnan(float(s.e_max.item())) and int(s.full_flag.item()) == 1, name
+        assert int(s.n_chosen.item()) == bl, name
+        np.testing.assert_array_equal(s.chosen[:bl].cpu().numpy(), cand, err_msg=name)
