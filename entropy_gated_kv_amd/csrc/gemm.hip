@@ -353,8 +353,8 @@ constexpr size_t lm_lds(int tpw) { return size_t(2 * 16) * kLmROWB + size_t(tpw)
 template <int N> struct IC { static constexpr int value = N; };
 
 // Steps I0, I0 + 1, ... of the sequence, step i taking ring slot i % 3 and
-// tile i % TPW (indices known at compile time); `guard` skips those at or past
-// `n` (the sequence's ragged end)
+// tile i % TPW (indices known at compile time); with GUARD, the steps at or
+// past n (the sequence's ragged end) are skipped
 template <int TPW, int I0, bool GUARD, typename F, int... I>
 __device__ __forceinline__ void lm_steps(F& f, int n, std::integer_sequence<int, I...>) {
   ((!GUARD || I0 + I < n ? f(IC<(I0 + I) % 3>{}, IC<(I0 + I) % TPW>{}) : void()), ...);
@@ -432,11 +432,11 @@ __global__ __launch_bounds__(kThreads) void lmhead_packed_kernel(GP p) {
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) acc[j][rb] = f32x4{};
   bf16_t* const C = static_cast<bf16_t*>(p.C);
-  // logits of a finished group (acc x scale, rounded once): each wave rounds
-  // its 16 columns of every tile into the staging area; then each thread
-  // stores 16-byte chunks of rows, a row of a tile being one 128-byte line
-  // (the host launches this kernel only for 16-byte aligned rows).  The area
-  // is written again only after a whole group of barriers.
+  // the group's logits (acc x scale, rounded once): each wave rounds its 16
+  // columns of every tile into the staging area; then each thread stores
+  // 16-byte chunks of rows, a row of a tile being one 128-byte line (the host
+  // launches this kernel only for 16-byte aligned rows), or computes
+  // statistics from the staged values.
   auto epilogue = [&]() {
 #pragma unroll
     for (int j = 0; j < TPW; ++j)
