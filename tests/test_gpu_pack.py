@@ -116,6 +116,14 @@ def test_packed_lm_head_launch_shapes_agree(V, d):
                                  model_n_kv_heads=heads))
 
 
+def test_packed_lm_head_stack_agrees():
+    """A two-layer RMSNorm / SwiGLU stack (the LM head reads the final norm's
+    output): the three twins as above."""
+    steps_agree(C.scaled(C.LLADA_STACK, name="stack2_pack", model_n_layers=2, model_d=256,
+                         model_n_q_heads=2, model_n_kv_heads=2, model_d_ffn=512, model_vocab=40032,
+                         prompt_len=96, gen_len=64, block_len=32, k=16))
+
+
 def test_non_finite_and_constant_rows_in_both_modes():
     """Candidate rows whose logits hold +-inf or NaN (a logit scale of +inf,
     -inf or NaN; 3e38 overflows some of a row) take the exact statistics path of the LM head's
