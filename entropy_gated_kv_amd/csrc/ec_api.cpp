@@ -207,10 +207,14 @@ StepLayout step_layout(const ec_model* m, int32_t max_block, void* ws) {
   if (m->w_lm) need(ec::Epi::kLogits, max_block, m->V, m->d);
   s.gemm_ws = c.take<void>(gws);
   // entropy partials: the entropy pass's segments, or the packed LM head's
-  // per-(row, tile group) statistics (one region serves both)
+  // per-(row, tile group) statistics (one region serves both).  The latter
+  // is sized for min(max_block, kLmStatRows) rows whatever max_block, so a
+  // workspace sized for a larger bound also serves blocks of at most
+  // kLmStatRows positions without a logits buffer.
   size_t ent = ec::entropy_ws_bytes(max_block, m->V, m->dtype);
-  if (m->w_lm && m->w_lm_packed && max_block <= ec::kLmStatRows) {
-    const size_t lm = size_t(max_block) * size_t(ec::lmhead_max_stat_groups(m->V)) * sizeof(ec::EntropyPartial);
+  if (m->w_lm && m->w_lm_packed) {
+    const size_t rows = size_t(max_block < ec::kLmStatRows ? max_block : ec::kLmStatRows);
+    const size_t lm = rows * size_t(ec::lmhead_max_stat_groups(m->V)) * sizeof(ec::EntropyPartial);
     if (lm > ent) ent = lm;
   }
   s.ent_ws = c.take<void>(ent);

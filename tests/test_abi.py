@@ -46,6 +46,19 @@ def test_workspace_queries(lib):
     assert lib.ec_attention_workspace_bytes(0, 1, 1, 1, 32) == 0
 
 
+def test_step_workspace_grows_with_the_block_bound(lib):
+    """A workspace sized for a block bound serves every shorter block, also
+    without a logits buffer, where a packed LM head's statistics need one
+    16-byte partial per row (up to 32) and group of column tiles."""
+    layers = (L.ec_layer * 1)(L.ec_layer(FAKE, FAKE, None, None, None, None, None))
+    m = L.ec_model(n_layers=1, d=256, Hq=2, Hkv=2, dh=128, d_ffn=0, V=40032, L_cap=256, dtype=1,
+                   rms_eps=1e-5, tok_emb=FAKE, pos_emb=FAKE, layers=layers, norm_final=None, w_lm=FAKE,
+                   logit_scale=None, w_lm_packed=FAKE)
+    sizes = [lib.ec_step_workspace_bytes(C.byref(m), b) for b in (1, 8, 16, 32, 33, 64, 256)]
+    assert all(x > 0 for x in sizes) and sizes == sorted(sizes), sizes
+    assert sizes[3] >= 32 * ((40032 + 63) // 64) * 16          # 32 rows x 626 groups
+
+
 FAKE = 1 << 20       # an aligned, never dereferenced address
 ODD = FAKE + 4       # misaligned
 

@@ -124,6 +124,28 @@ def test_packed_lm_head_stack_agrees():
                          prompt_len=96, gen_len=64, block_len=32, k=16))
 
 
+def test_no_logits_with_a_workspace_for_longer_blocks():
+    """Steps without a logits buffer on a sequence whose buffers and workspace
+    are sized for blocks of 64 give the same bits as on one sized for 32."""
+    cfg = C.scaled(C.LLADA_LAYER, name="ws64", model_d=256, model_n_q_heads=2, model_n_kv_heads=2,
+                   model_vocab=40032, prompt_len=96, gen_len=64, block_len=32, k=16)
+    w = G.model_weights(cfg)
+    toks, masked = G.initial_sequence(cfg)
+    dm = DeviceModel(cfg.model, cfg.dtype, cfg.L, w, pack_lm_head=True)
+    a, b = [DeviceSequence(dm, toks, masked, history_cap=cfg.gen_len, max_block=mb, keep_logits=False)
+            for mb in (32, 64)]
+    for i, (bs, bl, n) in enumerate(C.unmask_schedule(cfg)[:6]):
+        for s in (a, b):
+            s.step(TAU, cfg.k, bs, bl, n)
+        torch.cuda.synchronize()
+        for fld in ("row_entropy", "row_top1", "row_argmax", "e_max", "tokens", "is_masked", "chosen",
+                    "n_chosen", "full_flag"):
+            x, y = getattr(a, fld), getattr(b, fld)
+            m = min(x.numel(), y.numel())
+            assert torch.equal(x.flatten()[:m].view(torch.uint8) if x.dtype == torch.float32 else x.flatten()[:m],
+                               y.flatten()[:m].view(torch.uint8) if y.dtype == torch.float32 else y.flatten()[:m]), (i, fld)
+
+
 def test_non_finite_and_constant_rows_in_both_modes():
     """Candidate rows whose logits hold +-inf or NaN (a logit scale of +inf,
     -inf or NaN; 3e38 overflows some of a row) take the exact statistics path of the LM head's
